@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the deterministic training-linear GEMM on one MI355X.
+
+Default workload: the bf16 transformer MLP-up linear 768 -> 3072 at M = 4096
+(X[4096,768], W[768,3072] stored [in,out], bias[3072], dY[4096,3072]).  One
+step = forward + dX + dW through the C ABI on the MFMA tier.  Inputs are
+seeded synthetic data already resident in HBM when timing starts.
+
+Prints ONE JSON line with the whole-step throughput (TFLOP/s), a per-kernel
+roofline entry for the dominant kernel (average launch duration from HIP events
+recorded on the launch stream), and the CPU oracle's throughput on a bounded
+sample of the same workload.
+
+Other workloads (--workload): fp8 (e4m3 GEMM 8192x4096x4096), grouped (8
+experts, 16384x2048 -> 1408, forward + dinput + dweights), sweep (forward of
+W[4096,4096] at M in {1,3,17,128,1000,8192}).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK = 2516.6   # TFLOP/s, dense bf16/f16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+FP8_PEAK = 5033.2    # TFLOP/s, dense fp8 MFMA
+HBM_PEAK = 8000.0    # GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="linear", choices=["linear", "fp8", "grouped", "sweep"])
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def host_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit():
+        n = min(n, int(omp))
+    return max(n, 1)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Timer:
+    """HIP events recorded on the launch stream around every call of one op."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, []
+
+    def run(self, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        fn()
+        e1.record(self.stream)
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(len(self.pairs), 1)
+
+
+def timed_steps(torch, stream, ops, steps, warmup):
+    """ops: list of (name, callable).  Returns (ms_per_step, {name: mean ms})."""
+    for _ in range(warmup):
+        for _, fn in ops:
+            fn()
+    torch.cuda.synchronize()
+    timers = {name: Timer(torch, stream) for name, _ in ops}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for name, fn in ops:
+            timers[name].run(fn)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, {name: t.mean_ms() for name, t in timers.items()}
+
+
+def cpu_baseline_linear(d, target_s):
+    """The oracle, as it is, on the first R rows of the batch (forward, dX and
+    dW over those R rows); R grows until the sample takes about target_s."""
+    import oracle
+    thr = host_threads()
+    k, n, dt = d["k"], d["n"], d["dt"]
+
+    def run(r):
+        x, dy = d["x"][:r], d["dy"][:r]
+        t = time.perf_counter()
+        oracle.linear_forward(dt, x, d["w"], d["b"], r, k, n, threads=thr)
+        oracle.linear_dx(dt, dy, d["w"], r, k, n, threads=thr)
+        oracle.linear_dw(dt, x, dy, r, k, n, threads=thr)
+        return time.perf_counter() - t
+
+    r = 16
+    dt_s = run(r)
+    r = int(min(d["m"], max(16, r * target_s / max(dt_s, 1e-3))))
+    dt_s = run(r)
+    flops = 3 * 2.0 * r * k * n
+    return {"value": flops / dt_s / 1e12, "unit": "TFLOP/s", "cores": thr, "kind": "oracle",
+            "sample": f"forward+dX+dW on the first {r} of {d['m']} rows "
+                      f"(K={k}, N={n}), {dt_s:.1f} s, f64 accumulation, {cpu_model()}"}
+
+
+def bench_linear(args, torch, dig, synth):
+    dt = synth.BF16 if args.dtype == "bf16" else synth.F16
+    d = synth.config2(dt)
+    m, k, n = d["m"], d["k"], d["n"]
+    dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
+    x, w, b, dy = dev(d["x"]), dev(d["w"]), dev(d["b"]), dev(d["dy"])
+    y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.int16, device="cuda")
+    dw = torch.empty((k, n), dtype=torch.int16, device="cuda")
+    wsb = dig.bi_backward_dw_workspace_bytes(m, k, n, dt, 1)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+    ops = [
+        ("fwd", lambda: dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, s, 1))),
+        ("dX", lambda: dig.check(dig.bi_backward_dx(dx, dy, w, m, k, n, dt, s, 1))),
+        ("dW", lambda: dig.check(dig.bi_backward_dw(dw, x, dy, m, k, n, dt,
+                                                    ws if wsb else None, wsb, s, 1))),
+    ]
+    ms, per = timed_steps(torch, s, ops, args.steps, args.warmup)
+    flop = 2.0 * m * k * n
+    # algorithmic bytes per launch: each operand read once, the output written once
+    bytes_ = {"fwd": 2 * (m * k + k * n + n + m * n), "dX": 2 * (m * n + k * n + m * k),
+              "dW": 2 * (m * k + m * n + k * n)}
+    dominant = max(per, key=per.get)
+    achieved = flop / (per[dominant] * 1e-3) / 1e12
+    out = {
+        "metric": "TFLOP/s and % MFMA peak, bf16 fwd/dX/dW at M=4096, 768->3072; "
+                  "bit-exact determinism",
+        "value": round(3 * flop / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": f"{args.dtype} training linear 768->3072 (weight [in,out]) at "
+                               "M=4096: forward + dX + dW, MFMA tier",
+                   "M": m, "K": k, "N": n, "bias": True},
+        "roofline": {"bound": "mfma", "kernel": dominant,
+                     "achieved": round(achieved, 2), "peak": BF16_PEAK, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK, 4), "traffic": None,
+                     "algorithmic_bytes": bytes_[dominant]},
+        "ops": {name: {"us": round(v * 1e3, 2),
+                       "tflops": round(flop / (v * 1e-3) / 1e12, 2),
+                       "frac_peak": round(flop / (v * 1e-3) / 1e12 / BF16_PEAK, 4)}
+                for name, v in per.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_linear(d, args.cpu_seconds)
+    return out
+
+
+def bench_fp8(args, torch, dig, synth):
+    d = synth.config4()
+    m, k, n = d["m"], d["k"], d["n"]
+    a = torch.from_numpy(d["a8"]).cuda()
+    bt = torch.from_numpy(d["bt8"]).cuda()
+    da = torch.tensor([float(d["da"])], dtype=torch.float32, device="cuda")
+    db = torch.tensor([float(d["db"])], dtype=torch.float32, device="cuda")
+    y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    y16 = torch.empty((16, n), dtype=torch.int16, device="cuda")
+    s = torch.cuda.current_stream()
+    ops = [("fp8_m8192", lambda: dig.check(dig.bi_fp8_mm(y, a, bt, da, db, m, k, n, s, 1))),
+           ("fp8_m16", lambda: dig.check(dig.bi_fp8_mm(y16, a, bt, da, db, 16, k, n, s, 1)))]
+    ms, per = timed_steps(torch, s, ops, args.steps, args.warmup)
+    flop = 2.0 * m * k * n
+    ach = flop / (per["fp8_m8192"] * 1e-3) / 1e12
+    b16 = 16 * k + n * k + 16 * n * 2
+    return {
+        "metric": "fp8 e4m3 GEMM TFLOP/s", "value": round(ach, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "fp8 e4m3 A[8192,4096] x B^T[4096,4096], per-tensor scales, "
+                               "bf16 out; plus M=16", "M": m, "K": k, "N": n},
+        "roofline": {"bound": "mfma", "kernel": "fp8_m8192", "achieved": round(ach, 2),
+                     "peak": FP8_PEAK, "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK, 4),
+                     "traffic": None},
+        "m16": {"us": round(per["fp8_m16"] * 1e3, 2),
+                "GBps": round(b16 / (per["fp8_m16"] * 1e-3) / 1e9, 1),
+                "frac_hbm": round(b16 / (per["fp8_m16"] * 1e-3) / 1e9 / HBM_PEAK, 4)},
+    }
+
+
+def bench_grouped(args, torch, dig, synth):
+    d = synth.config5()
+    m, k, n, e = d["m"], d["k"], d["n"], d["e"]
+    dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
+    inp, w, dy = dev(d["input"]), dev(d["weights"]), dev(d["dy"])
+    ids = torch.from_numpy(d["row_experts"].view(np.int32).copy()).cuda()
+    off = torch.from_numpy(d["offsets"].view(np.int32).copy()).cuda()
+    y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    di = torch.empty((m, k), dtype=torch.int16, device="cuda")
+    dwt = torch.empty((e, n, k), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    bt = synth.BF16
+    ops = [("grouped_fwd", lambda: dig.check(dig.bi_grouped_nt(y, inp, w, ids, off, m, k, n, e,
+                                                               bt, s, 1))),
+           ("grouped_bwd", lambda: dig.check(dig.bi_grouped_nt_backward(
+               di, dwt, inp, w, dy, ids, off, m, k, n, e, bt, s, 1)))]
+    ms, per = timed_steps(torch, s, ops, args.steps, args.warmup)
+    valid = int(d["offsets"][e])
+    flop = 2.0 * valid * k * n
+    ach = flop / (per["grouped_fwd"] * 1e-3) / 1e12
+    return {
+        "metric": "grouped GEMM TFLOP/s (valid rows)", "value": round(3 * flop / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "row-routed grouped GEMM input[16384,2048] x weights[8,1408,2048]^T, "
+                               "5% padding rows: forward + dinput + f32 dweights",
+                   "M": m, "K": k, "N": n, "E": e, "valid_rows": valid},
+        "roofline": {"bound": "mfma", "kernel": "grouped_fwd", "achieved": round(ach, 2),
+                     "peak": BF16_PEAK, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK, 4),
+                     "traffic": None},
+        "ops": {k_: {"us": round(v * 1e3, 2)} for k_, v in per.items()},
+    }
+
+
+def bench_sweep(args, torch, dig, synth):
+    d = synth.config3()
+    m, k, n = d["m"], d["k"], d["n"]
+    dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
+    x, w = dev(d["x"]), dev(d["w"])
+    y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    s = torch.cuda.current_stream()
+    bt = synth.BF16
+    res = {}
+    for mp in (1, 3, 17, 128, 1000, 8192):
+        ops = [(f"m{mp}", lambda mp=mp: dig.check(dig.bi_forward(y, x, w, None, mp, k, n, bt, s,
+                                                                 1)))]
+        _, per = timed_steps(torch, s, ops, max(args.steps // 4, 10), 5)
+        us = per[f"m{mp}"] * 1e3
+        byt = 2 * (mp * k + k * n + mp * n)
+        res[mp] = {"us": round(us, 2), "tflops": round(2.0 * mp * k * n / (us * 1e-6) / 1e12, 2),
+                   "GBps": round(byt / (us * 1e-6) / 1e9, 1)}
+    big = res[8192]
+    return {"metric": "forward TFLOP/s, W[4096,4096] batch sweep", "value": big["tflops"],
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": big["us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "bf16 forward, W[4096,4096], M sweep", "K": k, "N": n},
+            "roofline": {"bound": "mfma", "kernel": "m8192", "achieved": big["tflops"],
+                         "peak": BF16_PEAK, "unit": "TFLOP/s",
+                         "frac": round(big["tflops"] / BF16_PEAK, 4), "traffic": None},
+            "sweep": res}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import deterministic_invariant_gemm_amd as dig
+    import synth
+    dig.load()
+    fn = {"linear": bench_linear, "fp8": bench_fp8, "grouped": bench_grouped,
+          "sweep": bench_sweep}[args.workload]
+    out = fn(args, torch, dig, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

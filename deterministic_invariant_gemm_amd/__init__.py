@@ -1,0 +1,136 @@
+"""Python binding of libbi.so, the deterministic batch-invariant GEMM library.
+
+Argument marshalling only: every function forwards to the C entry point of the
+same name declared in include/bi.h and returns its integer status.  Pointers
+may be given as integers (device addresses) or as objects with ``data_ptr()``
+(e.g. torch tensors); streams as integer ``hipStream_t`` handles or objects
+with a ``cuda_stream`` attribute (torch streams); ``None`` means NULL / the null
+stream.  No computation happens in Python and there is no fallback: if the
+library is not built, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbi.so")
+
+BI_F32, BI_BF16, BI_F16 = 0, 1, 2
+BI_OK = 0
+STATUS = {0: "BI_OK", -1: "BI_ERR_NULL", -2: "BI_ERR_DTYPE", -3: "BI_ERR_SHAPE",
+          -4: "BI_ERR_TOO_LARGE", -5: "BI_ERR_WORKSPACE", -6: "BI_ERR_HIP",
+          -7: "BI_ERR_UNSUPPORTED"}
+OP_FWD, OP_DX, OP_DW, OP_FP8, OP_GFWD, OP_GDIN, OP_GDW = range(7)
+
+_lib = None
+
+
+class BIError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}" if what else status_string(status))
+
+
+def load() -> ctypes.CDLL:
+    """Load libbi.so (built by ``build.build()``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run deterministic_invariant_gemm_amd."
+                           "build.build() (hipcc, gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.bi_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, i32]
+    L.bi_backward_dx.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32]
+    L.bi_backward_dw_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    L.bi_backward_dw_workspace_bytes.restype = sz
+    L.bi_backward_dw.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, sz, vp, i32]
+    L.bi_fp8_mm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i32]
+    L.bi_grouped_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, i32]
+    L.bi_grouped_nt_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                         vp, i32]
+    L.bi_status_string.argtypes = [i32]
+    L.bi_status_string.restype = ctypes.c_char_p
+    L.bi_plan.argtypes = [i32, i32, i32, i64, i64, ctypes.POINTER(i64)]
+    for f in ("bi_forward", "bi_backward_dx", "bi_backward_dw", "bi_fp8_mm", "bi_grouped_nt",
+              "bi_grouped_nt_backward", "bi_plan"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+def _p(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _s(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().bi_status_string(int(status)).decode()
+    except RuntimeError:
+        return STATUS.get(int(status), f"unknown status {status}")
+
+
+def check(status: int, what: str = "") -> None:
+    if status != BI_OK:
+        raise BIError(status, what)
+
+
+def bi_forward(y, x, w, bias, m, k, n, dtype, stream=None, tc=1) -> int:
+    return load().bi_forward(_p(y), _p(x), _p(w), _p(bias), m, k, n, dtype, _s(stream), tc)
+
+
+def bi_backward_dx(dx, dy, w, m, k, n, dtype, stream=None, tc=1) -> int:
+    return load().bi_backward_dx(_p(dx), _p(dy), _p(w), m, k, n, dtype, _s(stream), tc)
+
+
+def bi_backward_dw_workspace_bytes(m, k, n, dtype, tc=1) -> int:
+    return load().bi_backward_dw_workspace_bytes(m, k, n, dtype, tc)
+
+
+def bi_backward_dw(dw, x, dy, m, k, n, dtype, workspace, workspace_bytes, stream=None,
+                   tc=1) -> int:
+    return load().bi_backward_dw(_p(dw), _p(x), _p(dy), m, k, n, dtype, _p(workspace),
+                                 workspace_bytes, _s(stream), tc)
+
+
+def bi_fp8_mm(y, a, bt, a_dequant, b_dequant, m, k, n, stream=None, tc=1) -> int:
+    return load().bi_fp8_mm(_p(y), _p(a), _p(bt), _p(a_dequant), _p(b_dequant), m, k, n,
+                            _s(stream), tc)
+
+
+def bi_grouped_nt(y, inp, weights, row_experts, offsets, m, k, n, e, dtype, stream=None,
+                  tc=1) -> int:
+    return load().bi_grouped_nt(_p(y), _p(inp), _p(weights), _p(row_experts), _p(offsets),
+                                m, k, n, e, dtype, _s(stream), tc)
+
+
+def bi_grouped_nt_backward(dinput, dweights, inp, weights, grad_out, row_experts, offsets,
+                           m, k, n, e, dtype, stream=None, tc=1) -> int:
+    return load().bi_grouped_nt_backward(_p(dinput), _p(dweights), _p(inp), _p(weights),
+                                         _p(grad_out), _p(row_experts), _p(offsets), m, k, n,
+                                         e, dtype, _s(stream), tc)
+
+
+def bi_plan(op, dtype, tc, k, n):
+    """(tier/tile id, dW chunk rows) the dispatcher picks for these arguments."""
+    chunk = ctypes.c_int64(0)
+    r = load().bi_plan(op, dtype, tc, k, n, ctypes.byref(chunk))
+    return r, chunk.value
+
+
+def bi_status_string(status: int) -> str:
+    return status_string(status)

@@ -1,0 +1,346 @@
+// C ABI of the deterministic GEMM library: argument validation, the shape-only
+// tier / tile plan, and kernel launches.  Nothing here allocates, synchronises
+// or keeps state between calls.
+#include "../../include/bi.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+using namespace bi;
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr int64_t kNoSplit = (int64_t)1 << 62;  // "one chunk for any m"
+
+enum Op : int { OP_FWD = 0, OP_DX = 1, OP_DW = 2, OP_FP8 = 3, OP_GFWD = 4, OP_GDIN = 5, OP_GDW = 6 };
+
+bool dtype_ok(int dt) { return dt == BI_F32 || dt == BI_BF16 || dt == BI_F16; }
+
+int64_t elem_size(int dt) { return dt == BI_F32 ? 4 : 2; }
+
+// product of non-negative dims within kMaxElems, else -1
+int64_t checked_elems(int64_t a, int64_t b, int64_t c = 1) {
+    if (a < 0 || b < 0 || c < 0) return -1;
+    __int128 p = (__int128)a * b * c;
+    return p > kMaxElems ? -1 : (int64_t)p;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- the plan: tier, tile and chunk from (op, dtype, tc, k, n) only ----------
+
+struct Plan {
+    int tile;       // 0 = scalar tier, else MFMA tile id
+    int64_t chunk;  // dW: reduction rows per chunk
+};
+
+// non-M output dims of each op: the scalar tier takes over when one is < 64
+bool mfma_eligible(int op, int dt, int tc, int64_t k, int64_t n) {
+    if (!tc) return false;
+    if (op != OP_FP8 && dt == BI_F32) return false;
+    switch (op) {
+    case OP_FWD: case OP_FP8: case OP_GFWD: return n >= 64;
+    case OP_DX: case OP_GDIN: return k >= 64;
+    case OP_DW: case OP_GDW: return k >= 64 && n >= 64;
+    }
+    return false;
+}
+
+// output columns and reduction length, seen from the kernel
+int pick_tile(int op, int64_t k, int64_t n) {
+    int64_t cols = (op == OP_DX || op == OP_GDIN) ? k : n;
+    switch (op) {
+    case OP_FWD:
+        if (cols >= 2048 && cols % 256 == 0) return 1;  // 256x256
+        if (cols >= 2048 && cols % 192 == 0) return 2;  // 256x192
+        return cols >= 128 ? 4 : 6;
+    case OP_DX:
+        return cols >= 128 ? 4 : 6;
+    case OP_DW:
+        return (k >= 128 && n >= 128) ? 4 : 6;
+    case OP_FP8:
+        if (cols >= 2048 && cols % 256 == 0) return 1;
+        return cols >= 128 ? 4 : 6;
+    case OP_GFWD: case OP_GDIN: case OP_GDW:
+        return 4;
+    }
+    return 4;
+}
+
+Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
+    Plan pl{0, kNoSplit};
+    if (mfma_eligible(op, dt, tc, k, n)) pl.tile = pick_tile(op, k, n);
+    if (op == OP_DW) {
+        if (pl.tile) {
+            const TileShape *ts = mfma_tile(pl.tile);
+            const int64_t tiles = cdiv(k, ts->bm) * cdiv(n, ts->bn);
+            pl.chunk = tiles >= 128 ? kNoSplit : 1024;
+        } else {
+            // scalar tier: same rule for every dtype (bf16/f16 == upcast f32)
+            const int64_t tiles = cdiv(k, 64) * cdiv(n, 64);
+            pl.chunk = tiles >= 128 ? kNoSplit : 256;
+        }
+    }
+    return pl;
+}
+
+int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.chunk); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *bi_status_string(int status) {
+    switch (status) {
+    case BI_OK: return "BI_OK: success";
+    case BI_ERR_NULL: return "BI_ERR_NULL: a required pointer is NULL";
+    case BI_ERR_DTYPE: return "BI_ERR_DTYPE: unsupported dtype";
+    case BI_ERR_SHAPE: return "BI_ERR_SHAPE: invalid dimension";
+    case BI_ERR_TOO_LARGE: return "BI_ERR_TOO_LARGE: a tensor exceeds 2^40 elements";
+    case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE: dW workspace missing or too small";
+    case BI_ERR_HIP: return "BI_ERR_HIP: a HIP launch failed";
+    case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED: no tier for this dtype/tc";
+    }
+    return "unknown bi status";
+}
+
+int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows) {
+    if (op < OP_FWD || op > OP_GDW) return BI_ERR_UNSUPPORTED;
+    if (op != OP_FP8 && !dtype_ok(dtype)) return BI_ERR_DTYPE;
+    if (k < 0 || n < 0) return BI_ERR_SHAPE;
+    Plan pl = make_plan(op, op == OP_FP8 ? BI_BF16 : dtype, tc, k, n);
+    if (chunk_rows) *chunk_rows = pl.chunk;
+    return pl.tile;
+}
+
+int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t m, int64_t k,
+               int64_t n, int dtype, hipStream_t stream, int tc) {
+    if (!dtype_ok(dtype)) return BI_ERR_DTYPE;
+    if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, k) < 0 || checked_elems(k, n) < 0 || checked_elems(m, n) < 0)
+        return BI_ERR_TOO_LARGE;
+    if (m == 0 || n == 0) return BI_OK;
+    if (!y || (k > 0 && (!x || !w))) return BI_ERR_NULL;
+    const Plan pl = make_plan(OP_FWD, dtype, tc, k, n);
+    if (pl.tile == 0) {
+        ScalarGemmArgs a{};
+        a.a = x; a.a_is = k; a.a_rs = 1;
+        a.b = w; a.b_rs = n; a.b_js = 1;
+        a.bias = bias; a.c = y; a.ldc = n;
+        a.rows = m; a.cols = n; a.red = k; a.chunk = kNoSplit; a.nchunks = 1;
+        a.tiles_i = cdiv(m, 64); a.tiles_j = cdiv(n, 64);
+        return hip_status(launch_scalar_gemm(a, dtype, dtype, 0, stream));
+    }
+    const TileShape *ts = mfma_tile(pl.tile);
+    MfmaArgs a{};
+    a.a = x; a.lda = k; a.b = w; a.ldb = n; a.c = y; a.ldc = n; a.bias = bias;
+    a.rows = m; a.cols = n; a.red = k; a.chunk = kNoSplit; a.nchunks = 1;
+    a.tiles_i = cdiv(m, ts->bm); a.tiles_j = cdiv(n, ts->bn);
+    a.vec_a = aligned16(x) && k % 8 == 0;
+    a.vec_b = aligned16(w) && n % 8 == 0;
+    return hip_status(launch_mfma_gemm(a, pl.tile, dtype, /*layout A rc, B strided*/ 1, 0, stream));
+}
+
+int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k, int64_t n,
+                   int dtype, hipStream_t stream, int tc) {
+    if (!dtype_ok(dtype)) return BI_ERR_DTYPE;
+    if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, k) < 0 || checked_elems(k, n) < 0 || checked_elems(m, n) < 0)
+        return BI_ERR_TOO_LARGE;
+    if (m == 0 || k == 0) return BI_OK;
+    if (!dx || (n > 0 && (!dy || !w))) return BI_ERR_NULL;
+    const Plan pl = make_plan(OP_DX, dtype, tc, k, n);
+    if (pl.tile == 0) {
+        ScalarGemmArgs a{};
+        a.a = dy; a.a_is = n; a.a_rs = 1;
+        a.b = w; a.b_rs = 1; a.b_js = n;
+        a.c = dx; a.ldc = k;
+        a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
+        a.tiles_i = cdiv(m, 64); a.tiles_j = cdiv(k, 64);
+        return hip_status(launch_scalar_gemm(a, dtype, dtype, 0, stream));
+    }
+    const TileShape *ts = mfma_tile(pl.tile);
+    MfmaArgs a{};
+    a.a = dy; a.lda = n; a.b = w; a.ldb = n; a.c = dx; a.ldc = k;
+    a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
+    a.tiles_i = cdiv(m, ts->bm); a.tiles_j = cdiv(k, ts->bn);
+    a.vec_a = aligned16(dy) && n % 8 == 0;
+    a.vec_b = aligned16(w) && n % 8 == 0;
+    return hip_status(launch_mfma_gemm(a, pl.tile, dtype, /*both rc*/ 3, 0, stream));
+}
+
+size_t bi_backward_dw_workspace_bytes(int64_t m, int64_t k, int64_t n, int dtype, int tc) {
+    if (!dtype_ok(dtype) || m < 0 || k < 0 || n < 0) return 0;
+    if (checked_elems(m, k) < 0 || checked_elems(m, n) < 0 || checked_elems(k, n) < 0) return 0;
+    const Plan pl = make_plan(OP_DW, dtype, tc, k, n);
+    const int64_t chunks = dw_chunks(pl, m);
+    if (chunks <= 1) return 0;
+    return (size_t)chunks * (size_t)k * (size_t)n * sizeof(float);
+}
+
+int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k, int64_t n,
+                   int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                   int tc) {
+    if (!dtype_ok(dtype)) return BI_ERR_DTYPE;
+    if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, k) < 0 || checked_elems(k, n) < 0 || checked_elems(m, n) < 0)
+        return BI_ERR_TOO_LARGE;
+    if (k == 0 || n == 0) return BI_OK;
+    if (!dw || (m > 0 && (!x || !dy))) return BI_ERR_NULL;
+    const Plan pl = make_plan(OP_DW, dtype, tc, k, n);
+    const int64_t chunks = dw_chunks(pl, m);
+    const size_t need = chunks > 1 ? (size_t)chunks * (size_t)k * (size_t)n * sizeof(float) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return BI_ERR_WORKSPACE;
+    const int epi = chunks > 1 ? 1 : 0;
+    hipError_t e;
+    if (pl.tile == 0) {
+        ScalarGemmArgs a{};
+        a.a = x; a.a_is = 1; a.a_rs = k;
+        a.b = dy; a.b_rs = n; a.b_js = 1;
+        a.c = dw; a.ldc = n; a.ws = static_cast<float *>(workspace);
+        a.rows = k; a.cols = n; a.red = m; a.chunk = pl.chunk; a.nchunks = chunks;
+        a.tiles_i = cdiv(k, 64); a.tiles_j = cdiv(n, 64);
+        e = launch_scalar_gemm(a, dtype, epi ? BI_F32 : dtype, epi, stream);
+    } else {
+        const TileShape *ts = mfma_tile(pl.tile);
+        MfmaArgs a{};
+        a.a = x; a.lda = k; a.b = dy; a.ldb = n; a.c = dw; a.ldc = n;
+        a.ws = static_cast<float *>(workspace);
+        a.rows = k; a.cols = n; a.red = m; a.chunk = pl.chunk; a.nchunks = chunks;
+        a.tiles_i = cdiv(k, ts->bm); a.tiles_j = cdiv(n, ts->bn);
+        a.vec_a = aligned16(x) && k % 8 == 0;
+        a.vec_b = aligned16(dy) && n % 8 == 0;
+        e = launch_mfma_gemm(a, pl.tile, dtype, /*both strided*/ 0, epi, stream);
+    }
+    if (e != hipSuccess) return BI_ERR_HIP;
+    if (chunks > 1)
+        e = launch_chunk_sum(static_cast<const float *>(workspace), dw, k * n, chunks, dtype,
+                             stream);
+    return hip_status(e);
+}
+
+int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
+              const float *b_dequant, int64_t m, int64_t k, int64_t n, hipStream_t stream,
+              int tc) {
+    if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, k) < 0 || checked_elems(n, k) < 0 || checked_elems(m, n) < 0)
+        return BI_ERR_TOO_LARGE;
+    if (m == 0 || n == 0) return BI_OK;
+    if (!y || !a_dequant || !b_dequant || (k > 0 && (!a || !bt))) return BI_ERR_NULL;
+    const Plan pl = make_plan(OP_FP8, BI_BF16, tc, k, n);
+    if (pl.tile == 0) {
+        ScalarGemmArgs s{};
+        s.a = a; s.a_is = k; s.a_rs = 1;
+        s.b = bt; s.b_rs = 1; s.b_js = k;
+        s.scale_a = a_dequant; s.scale_b = b_dequant;
+        s.c = y; s.ldc = n;
+        s.rows = m; s.cols = n; s.red = k; s.chunk = kNoSplit; s.nchunks = 1;
+        s.tiles_i = cdiv(m, 64); s.tiles_j = cdiv(n, 64);
+        return hip_status(launch_scalar_gemm(s, 3 /*e4m3*/, BI_BF16, 2, stream));
+    }
+    const TileShape *ts = mfma_tile(pl.tile);
+    Fp8Args f{};
+    f.a = static_cast<const uint8_t *>(a);
+    f.bt = static_cast<const uint8_t *>(bt);
+    f.c = static_cast<uint16_t *>(y);
+    f.scale_a = a_dequant; f.scale_b = b_dequant;
+    f.m = m; f.n = n; f.k = k;
+    f.tiles_i = cdiv(m, ts->bm); f.tiles_j = cdiv(n, ts->bn);
+    f.vec = aligned16(a) && aligned16(bt) && k % 16 == 0;
+    return hip_status(launch_fp8_gemm(f, pl.tile, stream));
+}
+
+static int grouped_validate(int64_t m, int64_t k, int64_t n, int64_t e, int dtype) {
+    if (!dtype_ok(dtype)) return BI_ERR_DTYPE;
+    if (m < 0 || k <= 0 || n <= 0 || e <= 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, k) < 0 || checked_elems(m, n) < 0 || checked_elems(e, n, k) < 0)
+        return BI_ERR_TOO_LARGE;
+    if (m > 0xffffffffLL) return BI_ERR_TOO_LARGE;  // row indices are uint32 offsets
+    return BI_OK;
+}
+
+int bi_grouped_nt(void *y, const void *input, const void *weights, const uint32_t *row_experts,
+                  const uint32_t *offsets, int64_t m, int64_t k, int64_t n, int64_t e, int dtype,
+                  hipStream_t stream, int tc) {
+    int st = grouped_validate(m, k, n, e, dtype);
+    if (st != BI_OK) return st;
+    if (m == 0) return BI_OK;
+    if (!y || !input || !weights || !row_experts) return BI_ERR_NULL;
+    const Plan pl = make_plan(OP_GFWD, dtype, tc, k, n);
+    if (pl.tile == 0) {
+        GroupedScalarArgs g{};
+        g.input = input; g.weights = weights; g.row_experts = row_experts; g.offsets = offsets;
+        g.out = y; g.m = m; g.k = k; g.n = n; g.e = e;
+        return hip_status(launch_grouped_scalar(g, 0, dtype, stream));
+    }
+    if (!offsets) return BI_ERR_NULL;
+    const TileShape *ts = mfma_tile(pl.tile);
+    MfmaArgs a{};
+    a.a = input; a.lda = k; a.b = weights; a.ldb = k; a.c = y; a.ldc = n;
+    a.rows = m; a.cols = n; a.red = k; a.chunk = kNoSplit; a.nchunks = 1;
+    a.tiles_j = cdiv(n, ts->bn);
+    a.offsets = offsets; a.n_experts = e; a.b_expert_stride = n * k;
+    a.seg_tiles = cdiv(m, ts->bm) + e;
+    a.vec_a = aligned16(input) && k % 8 == 0;
+    a.vec_b = aligned16(weights) && k % 8 == 0;
+    return hip_status(launch_mfma_gemm(a, pl.tile, dtype, 3, 0, stream));
+}
+
+int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, const void *weights,
+                           const void *grad_out, const uint32_t *row_experts,
+                           const uint32_t *offsets, int64_t m, int64_t k, int64_t n, int64_t e,
+                           int dtype, hipStream_t stream, int tc) {
+    int st = grouped_validate(m, k, n, e, dtype);
+    if (st != BI_OK) return st;
+    if (!dweights || !offsets) return BI_ERR_NULL;
+    if (m > 0 && (!dinput || !input || !weights || !grad_out || !row_experts)) return BI_ERR_NULL;
+    // dinput (skipped for an empty batch)
+    if (m > 0) {
+        const Plan pl = make_plan(OP_GDIN, dtype, tc, k, n);
+        hipError_t er;
+        if (pl.tile == 0) {
+            GroupedScalarArgs g{};
+            g.grad_out = grad_out; g.weights = weights; g.row_experts = row_experts;
+            g.out = dinput; g.m = m; g.k = k; g.n = n; g.e = e;
+            er = launch_grouped_scalar(g, 1, dtype, stream);
+        } else {
+            const TileShape *ts = mfma_tile(pl.tile);
+            MfmaArgs a{};
+            a.a = grad_out; a.lda = n; a.b = weights; a.ldb = k; a.c = dinput; a.ldc = k;
+            a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
+            a.tiles_j = cdiv(k, ts->bn);
+            a.offsets = offsets; a.n_experts = e; a.b_expert_stride = n * k;
+            a.seg_tiles = cdiv(m, ts->bm) + e;
+            a.vec_a = aligned16(grad_out) && n % 8 == 0;
+            a.vec_b = aligned16(weights) && k % 8 == 0;
+            er = launch_mfma_gemm(a, pl.tile, dtype, 1, 0, stream);
+        }
+        if (er != hipSuccess) return BI_ERR_HIP;
+    }
+    // dweights (always written, so experts without rows get +0)
+    const Plan pw = make_plan(OP_GDW, dtype, tc, k, n);
+    if (pw.tile == 0 || m == 0) {
+        GroupedScalarArgs g{};
+        g.input = input; g.grad_out = grad_out; g.offsets = offsets; g.dweights = dweights;
+        g.m = m; g.k = k; g.n = n; g.e = e;
+        return hip_status(launch_grouped_scalar(g, 2, dtype, stream));
+    }
+    const TileShape *ts = mfma_tile(pw.tile);
+    MfmaArgs a{};
+    a.a = grad_out; a.lda = n; a.b = input; a.ldb = k; a.c = dweights; a.ldc = k;
+    a.rows = n; a.cols = k; a.red = m; a.chunk = kNoSplit; a.nchunks = 1;
+    a.tiles_i = cdiv(n, ts->bm); a.tiles_j = cdiv(k, ts->bn);
+    a.red_offsets = offsets; a.n_experts = e; a.c_expert_stride = n * k;
+    a.vec_a = aligned16(grad_out) && n % 8 == 0;
+    a.vec_b = aligned16(input) && k % 8 == 0;
+    return hip_status(launch_mfma_gemm(a, pw.tile, dtype, 0, 2, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Internal interface between the C ABI (bi_api.cpp) and the kernel files.
+// Every launch_* function enqueues on the given stream and returns the HIP
+// status of the launch; none of them allocates or synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+// Generic strided scalar GEMM  C(i,j) = sum_r A(i,r) B(r,j)  over the rows of
+// one reduction chunk [chunk*c, min((chunk+1)*c, red)).
+struct ScalarGemmArgs {
+    const void *a;
+    int64_t a_is, a_rs;  // A(i,r) = a[i*a_is + r*a_rs]
+    const void *b;
+    int64_t b_rs, b_js;  // B(r,j) = b[r*b_rs + j*b_js]
+    const void *bias;    // [cols] of the input dtype, or null
+    const float *scale_a, *scale_b;  // fp8 dequantisation scales (device)
+    void *c;
+    int64_t ldc;
+    float *ws;  // f32 chunk partials [nchunks][rows][cols] (EPI_PARTIAL)
+    int64_t rows, cols, red;
+    int64_t chunk, nchunks;
+    int64_t tiles_i, tiles_j;
+};
+
+struct GroupedScalarArgs {
+    const void *input, *weights, *grad_out;
+    const uint32_t *row_experts, *offsets;
+    void *out;        // y [m,n] or dinput [m,k]
+    float *dweights;  // [e,n,k]
+    int64_t m, k, n, e;
+};
+
+// MFMA tier (bf16 / f16): C(i,j) = sum_r A(i,r) B(j,r).
+//   A "reduction-contiguous":  A(i,r) = a[i*lda + r];  else A(i,r) = a[r*lda + i]
+//   B "reduction-contiguous":  B(j,r) = b[j*ldb + r];  else B(j,r) = b[r*ldb + j]
+// Grouped mode (offsets != null): the row range of C is cut into expert
+// segments [offsets[x], offsets[x+1]); tiles are anchored at segment starts,
+// B is advanced by x*b_expert_stride, rows in [offsets[e], rows) are written as
+// +0.  Expert-reduction mode (red_offsets != null): tile z = expert x reduces
+// over r in [red_offsets[x], red_offsets[x+1]), A/B rows are global, C is
+// advanced by x*c_expert_stride.
+struct MfmaArgs {
+    const void *a;
+    int64_t lda;
+    const void *b;
+    int64_t ldb;
+    void *c;
+    int64_t ldc;
+    const void *bias;  // [cols] of the operand dtype or null
+    float *ws;         // f32 partials [nchunks][rows][cols]
+    int64_t rows, cols, red;
+    int64_t chunk, nchunks;
+    int64_t tiles_i, tiles_j;
+    // grouped forward / dinput
+    const uint32_t *offsets;
+    int64_t n_experts;
+    int64_t b_expert_stride;
+    int64_t seg_tiles;  // tiles_i bound: ceil(rows/BM) + n_experts + 1
+    // grouped dweights
+    const uint32_t *red_offsets;
+    int64_t c_expert_stride;
+    int vec_a, vec_b;  // 16-byte vector loads allowed for A / B
+};
+
+struct Fp8Args {
+    const uint8_t *a;   // [m,k]
+    const uint8_t *bt;  // [n,k]
+    uint16_t *c;        // [m,n] bf16
+    const float *scale_a, *scale_b;
+    int64_t m, n, k;
+    int64_t tiles_i, tiles_j;
+    int vec;
+};
+
+hipError_t launch_scalar_gemm(const ScalarGemmArgs &p, int dt_in, int dt_out, int epi,
+                              hipStream_t s);
+hipError_t launch_chunk_sum(const float *ws, void *out, int64_t count, int64_t nchunks,
+                            int dt_out, hipStream_t s);
+hipError_t launch_grouped_scalar(const GroupedScalarArgs &p, int op, int dt, hipStream_t s);
+
+// Tile shapes of the MFMA tier.  All use v_mfma_f32_32x32x16_{bf16,f16} with
+// the same ascending 16-deep reduction steps, so they give identical bits.
+struct TileShape {
+    int id, bm, bn;
+};
+const TileShape *mfma_tile(int id);  // null for an unknown id
+
+// layout: bit 0 = A reduction-contiguous, bit 1 = B reduction-contiguous.
+// epi: 0 round to dtype (+bias), 1 f32 partial into ws, 2 f32 into c (dweights).
+hipError_t launch_mfma_gemm(const MfmaArgs &p, int tile_id, int dt, int layout, int epi,
+                            hipStream_t s);
+
+hipError_t launch_fp8_gemm(const Fp8Args &p, int tile_id, hipStream_t s);
+
+}  // namespace bi

@@ -1,0 +1,244 @@
+// Scalar FMA tier (sgemm-bi PyPI page, "Determinism contracts": the f32 /
+// typed scalar tier, bit-identical across runs, bf16/f16 equal to "upcast ->
+// f32 kernel -> RNE downcast", full shape coverage).
+//
+// Every output element is ONE f32 chain
+//     acc = +0;  for r ascending over the reduction range: acc = fmaf(a_r, b_r, acc)
+// followed by the epilogue (+bias in f32, or the two fp8 scale multiplies, or
+// the f32 partial store) and a single rounding to the output type.  Inputs are
+// widened exactly to f32 when staged, so the bf16/f16 instantiations execute
+// the very same f32 instruction sequence as the f32 one on the upcast values.
+// This file is compiled with -ffp-contract=off: the only fused operations are
+// the explicit fmaf calls.
+//
+// Layout: a generic strided formulation C(i,j) = sum_r A(i,r) B(r,j) with
+// A(i,r) = a[i*a_is + r*a_rs] and B(r,j) = b[r*b_rs + j*b_js] covers forward,
+// dX, dW and fp8.  A workgroup of 256 threads computes a 64x64 tile, each thread
+// a 4x4 micro-tile with stride 16, staging 16-deep reduction slices through LDS.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace bi {
+
+namespace {
+
+constexpr int ST = 64;  // tile edge
+constexpr int RK = 16;  // reduction slice staged per step
+
+enum ScalarEpi : int { EPI_ROUND = 0, EPI_PARTIAL = 1, EPI_FP8 = 2 };
+
+template <int DT_IN, int DT_OUT, int EPI>
+__global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
+    __shared__ float As[RK][ST + 1];
+    __shared__ float Bs[RK][ST + 1];
+
+    const int t = threadIdx.x;
+    const int tx = t & 15, ty = t >> 4;
+    const int64_t tiles = p.tiles_i * p.tiles_j;
+    const int64_t bid = blockIdx.x;
+    const int64_t chunk = bid / tiles;
+    const int64_t tile = bid % tiles;
+    const int64_t i0 = (tile / p.tiles_j) * ST;
+    const int64_t j0 = (tile % p.tiles_j) * ST;
+    const int64_t r_begin = chunk * p.chunk;
+    const int64_t r_end = r_begin + p.chunk < p.red ? r_begin + p.chunk : p.red;
+
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+
+    const bool a_r_contig = p.a_rs == 1;
+    const bool b_j_contig = p.b_js == 1;
+
+    for (int64_t rk = r_begin; rk < r_end; rk += RK) {
+        const int valid = (int)(r_end - rk < RK ? r_end - rk : RK);
+        // stage A(i0.., rk..) and B(rk.., j0..) as exact f32
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int idx = t + 256 * q;
+            int row, rr;
+            if (a_r_contig) { row = idx >> 4; rr = idx & 15; }
+            else            { row = idx & 63; rr = idx >> 6; }
+            const int64_t gi = i0 + row, gr = rk + rr;
+            float v = 0.0f;
+            if (gi < p.rows && rr < valid) v = load_elem<DT_IN>(p.a, gi * p.a_is + gr * p.a_rs);
+            As[rr][row] = v;
+            int col;
+            if (b_j_contig) { col = idx & 63; rr = idx >> 6; }
+            else            { col = idx >> 4; rr = idx & 15; }
+            const int64_t gj = j0 + col, gr2 = rk + rr;
+            float w = 0.0f;
+            if (gj < p.cols && rr < valid) w = load_elem<DT_IN>(p.b, gr2 * p.b_rs + gj * p.b_js);
+            Bs[rr][col] = w;
+        }
+        __syncthreads();
+        for (int rr = 0; rr < valid; ++rr) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) av[a] = As[rr][ty + 16 * a];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bv[b] = Bs[rr][tx + 16 * b];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(av[a], bv[b], acc[a][b]);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int64_t gi = i0 + ty + 16 * a;
+        if (gi >= p.rows) continue;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t gj = j0 + tx + 16 * b;
+            if (gj >= p.cols) continue;
+            float v = acc[a][b];
+            if constexpr (EPI == EPI_PARTIAL) {
+                p.ws[(chunk * p.rows + gi) * p.cols + gj] = v;
+            } else {
+                if constexpr (EPI == EPI_FP8) {
+                    v = v * p.scale_a[0];
+                    v = v * p.scale_b[0];
+                } else {
+                    if (p.bias) v = v + load_elem<DT_IN>(p.bias, gj);
+                }
+                store_elem<DT_OUT>(p.c, gi * p.ldc + gj, v);
+            }
+        }
+    }
+}
+
+// Pass 2 of the chunked dW: out = RNE( ((P0 + P1) + P2) + ... ) per element,
+// chunks in ascending order.  Shared by both tiers.
+template <int DT_OUT>
+__global__ __launch_bounds__(256) void chunk_sum_kernel(const float *__restrict__ ws,
+                                                        void *out, int64_t count,
+                                                        int64_t nchunks) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        float s = ws[i];
+        for (int64_t c = 1; c < nchunks; ++c) s = s + ws[c * count + i];
+        store_elem<DT_OUT>(out, i, s);
+    }
+}
+
+// Grouped scalar tier (rublas tensor_grouped/mod.rs: one thread per output
+// element, FP32 accumulation, one output rounding).
+template <int DT>
+__global__ __launch_bounds__(256) void grouped_fwd_scalar_kernel(GroupedScalarArgs p) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= p.m * p.n) return;
+    const int64_t row = idx / p.n, col = idx % p.n;
+    const uint32_t ex = p.row_experts[row];
+    if ((int64_t)ex < p.e) {
+        float acc = 0.0f;
+        const int64_t wb = ((int64_t)ex * p.n + col) * p.k;
+        for (int64_t r = 0; r < p.k; ++r)
+            acc = __builtin_fmaf(load_elem<DT>(p.input, row * p.k + r),
+                                 load_elem<DT>(p.weights, wb + r), acc);
+        store_elem<DT>(p.out, idx, acc);
+    } else {
+        if constexpr (DT == DT_F32) static_cast<uint32_t *>(p.out)[idx] = 0u;
+        else static_cast<uint16_t *>(p.out)[idx] = 0u;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void grouped_dinput_scalar_kernel(GroupedScalarArgs p) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= p.m * p.k) return;
+    const int64_t row = idx / p.k, col = idx % p.k;
+    const uint32_t ex = p.row_experts[row];
+    if ((int64_t)ex < p.e) {
+        float acc = 0.0f;
+        const int64_t wb = (int64_t)ex * p.n * p.k + col;
+        for (int64_t r = 0; r < p.n; ++r)
+            acc = __builtin_fmaf(load_elem<DT>(p.grad_out, row * p.n + r),
+                                 load_elem<DT>(p.weights, wb + r * p.k), acc);
+        store_elem<DT>(p.out, idx, acc);
+    } else {
+        if constexpr (DT == DT_F32) static_cast<uint32_t *>(p.out)[idx] = 0u;
+        else static_cast<uint16_t *>(p.out)[idx] = 0u;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void grouped_dweights_scalar_kernel(GroupedScalarArgs p) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= p.e * p.n * p.k) return;
+    const int64_t ex = idx / (p.n * p.k);
+    const int64_t col_n = (idx / p.k) % p.n, col_k = idx % p.k;
+    // offsets are a caller invariant; clamping keeps a violated invariant from
+    // reading outside the operands (the result is then simply wrong)
+    int64_t r1 = p.offsets[ex + 1], r0 = p.offsets[ex];
+    if (r1 > p.m) r1 = p.m;
+    if (r0 > r1) r0 = r1;
+    float acc = 0.0f;
+    for (int64_t r = r0; r < r1; ++r)
+        acc = __builtin_fmaf(load_elem<DT>(p.grad_out, r * p.n + col_n),
+                             load_elem<DT>(p.input, r * p.k + col_k), acc);
+    p.dweights[idx] = acc;
+}
+
+}  // namespace
+
+#define BI_LAUNCH(kern, grid, block, stream, ...)                                   \
+    do {                                                                             \
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(block), 0, stream, __VA_ARGS__);   \
+    } while (0)
+
+hipError_t launch_scalar_gemm(const ScalarGemmArgs &p, int dt_in, int dt_out, int epi,
+                              hipStream_t s) {
+    const int64_t grid = p.tiles_i * p.tiles_j * p.nchunks;
+    if (grid <= 0) return hipSuccess;
+#define CASE(DI, DO, E)                                                                   \
+    if (dt_in == DI && dt_out == DO && epi == E) {                                        \
+        BI_LAUNCH((scalar_gemm_kernel<DI, DO, E>), grid, 256, s, p);                      \
+        return hipGetLastError();                                                         \
+    }
+    CASE(DT_F32, DT_F32, EPI_ROUND)
+    CASE(DT_BF16, DT_BF16, EPI_ROUND)
+    CASE(DT_F16, DT_F16, EPI_ROUND)
+    CASE(DT_F32, DT_F32, EPI_PARTIAL)
+    CASE(DT_BF16, DT_F32, EPI_PARTIAL)
+    CASE(DT_F16, DT_F32, EPI_PARTIAL)
+    CASE(DT_E4M3, DT_BF16, EPI_FP8)
+#undef CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_sum(const float *ws, void *out, int64_t count, int64_t nchunks,
+                            int dt_out, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    int64_t grid = (count + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    if (dt_out == DT_F32) BI_LAUNCH(chunk_sum_kernel<DT_F32>, grid, 256, s, ws, out, count, nchunks);
+    else if (dt_out == DT_BF16) BI_LAUNCH(chunk_sum_kernel<DT_BF16>, grid, 256, s, ws, out, count, nchunks);
+    else if (dt_out == DT_F16) BI_LAUNCH(chunk_sum_kernel<DT_F16>, grid, 256, s, ws, out, count, nchunks);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_scalar(const GroupedScalarArgs &p, int op, int dt, hipStream_t s) {
+    int64_t count = op == 0 ? p.m * p.n : (op == 1 ? p.m * p.k : p.e * p.n * p.k);
+    if (count <= 0) return hipSuccess;
+    const int64_t grid = (count + 255) / 256;
+#define GCASE(D)                                                                           \
+    if (dt == D) {                                                                         \
+        if (op == 0) BI_LAUNCH(grouped_fwd_scalar_kernel<D>, grid, 256, s, p);             \
+        else if (op == 1) BI_LAUNCH(grouped_dinput_scalar_kernel<D>, grid, 256, s, p);     \
+        else BI_LAUNCH(grouped_dweights_scalar_kernel<D>, grid, 256, s, p);                \
+        return hipGetLastError();                                                          \
+    }
+    GCASE(DT_F32)
+    GCASE(DT_BF16)
+    GCASE(DT_F16)
+#undef GCASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace bi

@@ -1,0 +1,180 @@
+/*
+ * bi.h -- C ABI of the deterministic, batch-invariant training GEMM library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (each defined by the pages cited beside it):
+ *   bi_forward              Y  = RNE_T(X W + b)
+ *   bi_backward_dx          dX = RNE_T(dY W^T)
+ *   bi_backward_dw          dW = RNE_T(X^T dY)           (fixed-order two-pass)
+ *   bi_fp8_mm               Y  = RNE_bf16((A B^T) dA dB) (fp8 e4m3fn inputs)
+ *   bi_grouped_nt           Y[m] = in[m] Wt[e(m)]^T, zero rows for padding ids
+ *   bi_grouped_nt_backward  dIn and f32 dWt of the grouped GEMM
+ *
+ * Common conventions
+ *   Layout     Every matrix is dense row-major with no padding between rows.
+ *              The linear weight W is stored [in, out] = [K, N] (sgemm-bi
+ *              PyPI page, "Use": weight stored [in, out]).  Pointers of 16-bit
+ *              types must be 2-byte aligned, f32 pointers 4-byte aligned;
+ *              16-byte alignment of every row lets the kernels use vector loads
+ *              (other alignments take a slower load path with the same bits).
+ *   Memory     Every tensor pointer is a device pointer on the current HIP
+ *              device, owned by the caller.  The library allocates nothing,
+ *              keeps no per-call state, and never writes an input.  Outputs
+ *              must not overlap inputs or each other.
+ *   Execution  Work is enqueued on `stream` (0 = the null stream) and runs
+ *              asynchronously; BI_OK means "validated and enqueued".
+ *   Errors     All arguments are validated before anything is enqueued; on a
+ *              validation error nothing is enqueued and no output is touched.
+ *              A launch failure returns BI_ERR_HIP and is never retried on
+ *              another tier (rublas tensor_grouped/mod.rs, strategy
+ *              documentation: launch errors are propagated, never treated as a
+ *              fallback).  bi_status_string() names every code.
+ *   Sizes      m, k, n, e are int64; each tensor may hold at most 2^40
+ *              elements (BI_ERR_TOO_LARGE beyond).  m == 0 is a valid empty
+ *              batch: nothing is enqueued (except bi_backward_dw and the
+ *              grouped backward, which then write zero gradients).
+ *   dtype      BI_F32, BI_BF16 or BI_F16 for operands and outputs of the
+ *              linear and grouped ops; accumulation is always f32 and the
+ *              output is rounded once, to nearest-even (sgemm-bi PyPI page,
+ *              "Determinism contracts").
+ *   tc         Tensor-core (MFMA) tier request.  tc = 0 always selects the
+ *              scalar FMA tier.  tc = 1 selects the MFMA tier for bf16/f16
+ *              (and fp8) unless a non-M output dimension is below 64, in which
+ *              case the scalar tier runs (sgemm-bi PyPI page, "Determinism
+ *              contracts": shape-only fallback below 64).  f32 operands always
+ *              use the scalar tier.  The choice, and the tile shape, depend
+ *              only on (op, dtype, tc, the non-M output dims, the reduction
+ *              length) -- never on m -- so the forward is batch-invariant:
+ *              a row's output bits do not depend on how many other rows are in
+ *              the batch.
+ *
+ * Determinism contracts
+ *   Every entry point is bit-identical from run to run for the same inputs.
+ *   Scalar tier: each output is one fmaf chain over the reduction index in
+ *   ascending order from +0, then (+bias in f32), then one RNE; bf16/f16
+ *   results equal RNE of the f32 tier run on the upcast inputs.
+ *   MFMA tier: one MFMA instruction kind per dtype and a fixed ascending
+ *   sequence of 16-deep (bf16/f16) or 64-deep (fp8) reduction steps per output
+ *   element in every tile shape, so all tile shapes give identical bits.
+ *   No atomics anywhere.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BI_F32 = 0,  /* IEEE binary32 */
+    BI_BF16 = 1, /* bfloat16 */
+    BI_F16 = 2   /* IEEE binary16 */
+} bi_dtype;
+
+typedef enum {
+    BI_OK = 0,
+    BI_ERR_NULL = -1,        /* a required pointer is NULL */
+    BI_ERR_DTYPE = -2,       /* dtype code not supported by this entry point */
+    BI_ERR_SHAPE = -3,       /* negative or zero-where-forbidden dimension */
+    BI_ERR_TOO_LARGE = -4,   /* a tensor exceeds 2^40 elements */
+    BI_ERR_WORKSPACE = -5,   /* dW workspace missing or too small */
+    BI_ERR_HIP = -6,         /* a HIP launch failed (hipGetLastError) */
+    BI_ERR_UNSUPPORTED = -7  /* tc/dtype combination has no tier */
+} bi_status;
+
+/* Forward of the training linear (sgemm-bi PyPI page, "Use" and
+ * "Determinism contracts"; ViperLLM ffma.py, _FFMAAddmm.forward):
+ *   y[m,n] = RNE_dtype( sum_k x[m,k] * w[k,n] + bias[n] )
+ * x: [m,k], w: [k,n] ([in,out]), bias: [n] or NULL, y: [m,n]; all of `dtype`.
+ * The bias is added in f32 to the f32 accumulator before the single rounding.
+ * k == 0 gives y = RNE(bias) (or +0).  Batch-invariant in m. */
+int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t m, int64_t k,
+               int64_t n, int dtype, hipStream_t stream, int tc);
+
+/* Input gradient (ffma.py, _FFMAAddmm.backward: gx = gy W^T):
+ *   dx[m,k] = RNE_dtype( sum_n dy[m,n] * w[k,n] )
+ * dy: [m,n], w: [k,n], dx: [m,k].  Tier and tile depend on (k, n) only. */
+int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k, int64_t n,
+                   int dtype, hipStream_t stream, int tc);
+
+/* Workspace bytes bi_backward_dw needs for these sizes (0 when the reduction
+ * over m fits in one chunk).  Returns 0 for invalid arguments as well. */
+size_t bi_backward_dw_workspace_bytes(int64_t m, int64_t k, int64_t n, int dtype, int tc);
+
+/* Weight gradient (ffma.py, _FFMAAddmm.backward: gW = x^T gy, returned in the
+ * weight dtype; sgemm-bi PyPI page, "Use": f32-accumulated dW):
+ *   dw[k,n] = RNE_dtype( sum_m x[m,k] * dy[m,n] )
+ * x: [m,k], dy: [m,n], dw: [k,n].  No atomics.  The m rows are cut into chunks
+ * of C rows, C fixed by (dtype, tc, k, n) and never by m; pass 1 writes one f32
+ * partial per chunk into the workspace, pass 2 sums the partials in ascending
+ * chunk order and rounds once.  With a single chunk pass 1 rounds and stores
+ * directly (same bits).  workspace: device memory of at least
+ * bi_backward_dw_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * m == 0 writes dw = +0. */
+int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k, int64_t n,
+                   int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                   int tc);
+
+/* Per-tensor-scaled fp8 GEMM (AstrAI fp8_mm.cu: fp8_mm takes e4m3fn a[M,K]
+ * and b[N,K] and returns bf16 [M,N]; fp8_gemm_into applies the per-tensor f32
+ * scales inside the GEMM, D = A_SCALE * B_SCALE * A * B):
+ *   y[m,n] = RNE_bf16( ((sum_k a[m,k] * bt[n,k]) * a_dequant) * b_dequant )
+ * a: [m,k] OCP e4m3fn codes, bt: [n,k] e4m3fn codes (both k-contiguous),
+ * a_dequant / b_dequant: device pointers to one f32 each, y: [m,n] bf16.
+ * Products are exact; the sum is f32; the two scale multiplies are f32, left
+ * to right; one RNE to bf16.  Batch-invariant in m. */
+int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
+              const float *b_dequant, int64_t m, int64_t k, int64_t n, hipStream_t stream,
+              int tc);
+
+/* Row-routed grouped GEMM (rublas tensor_grouped/mod.rs, grouped_matmul_nt:
+ * [M,K] @ [E,N,K]^T selecting one expert per row; ids outside [0,E) are padding
+ * and produce zero rows; f32 accumulation, one output rounding):
+ *   y[m,n] = row_experts[m] < e ? RNE_dtype( sum_k input[m,k] * weights[row_experts[m],n,k] )
+ *                               : +0
+ * input: [m,k], weights: [e,n,k], y: [m,n], all of `dtype`;
+ * row_experts: [m] uint32; offsets: [e+1] uint32 or NULL.
+ * offsets (required when tc selects the MFMA tier): offsets[0] = 0 and the rows
+ * of expert j are [offsets[j], offsets[j+1]); rows [offsets[e], m) are padding.
+ * That is, rows are sorted by expert with padding last, and offsets describes
+ * the same grouping as row_experts -- a caller invariant that is not checked
+ * on the device (rublas: GPU values are not copied to the CPU to validate
+ * grouping).  The scalar tier reads row_experts only, in any row order.
+ * k, n, e must be > 0 (BI_ERR_SHAPE). */
+int bi_grouped_nt(void *y, const void *input, const void *weights, const uint32_t *row_experts,
+                  const uint32_t *offsets, int64_t m, int64_t k, int64_t n, int64_t e, int dtype,
+                  hipStream_t stream, int tc);
+
+/* Backward of the grouped GEMM (rublas tensor_grouped/mod.rs,
+ * grouped_matmul_nt_backward_segmented and GroupedBackward: dinput in the
+ * input dtype, dweights always f32):
+ *   dinput[m,k]     = row_experts[m] < e ? RNE_dtype( sum_n grad_out[m,n] * weights[e(m),n,k] ) : +0
+ *   dweights[j,n,k] = sum over rows m of expert j, ascending, of grad_out[m,n] * input[m,k]  (f32)
+ * dinput: [m,k] of dtype, dweights: [e,n,k] f32, grad_out: [m,n] of dtype.
+ * offsets: [e+1] uint32, required (same invariants as bi_grouped_nt); experts
+ * with no rows get dweights = +0.  k, n, e must be > 0. */
+int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, const void *weights,
+                           const void *grad_out, const uint32_t *row_experts,
+                           const uint32_t *offsets, int64_t m, int64_t k, int64_t n, int64_t e,
+                           int dtype, hipStream_t stream, int tc);
+
+/* Static, NUL-terminated name of a status code (never NULL). */
+const char *bi_status_string(int status);
+
+/* Tier and tile the dispatcher picks, without launching anything:
+ * op: 0 forward, 1 dX, 2 dW, 3 fp8, 4 grouped forward, 5 grouped dinput,
+ * 6 grouped dweights.  Returns 0 for the scalar tier, a positive tile id for
+ * the MFMA tier, or a negative bi_status.  Depends on (op, dtype, tc, k, n)
+ * only.  For dW, *chunk_rows (if not NULL) receives the chunk length C. */
+int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

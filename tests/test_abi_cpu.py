@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/bi.h declares, and rejects invalid arguments before any HIP call.
+No kernel is launched here (every call below returns during validation or is
+an empty-batch no-op), so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_invariant_gemm_amd as dig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "bi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dig.LIB_PATH):
+        from deterministic_invariant_gemm_amd import build
+        build.build()
+    return dig.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in list(range(-7, 1)):
+        s = dig.status_string(code)
+        assert s.startswith(dig.STATUS[code])
+    assert "unknown" in dig.status_string(-99)
+
+
+F = 12345 * 4096  # a non-null fake device address; never dereferenced
+
+
+def test_validation_errors(lib):
+    assert dig.bi_forward(F, F, F, None, 4, 4, 4, 7) == -2
+    assert dig.bi_forward(F, F, F, None, -1, 4, 4, dig.BI_BF16) == -3
+    assert dig.bi_forward(None, F, F, None, 4, 4, 4, dig.BI_BF16) == -1
+    assert dig.bi_forward(F, None, F, None, 4, 4, 4, dig.BI_BF16) == -1
+    assert dig.bi_forward(F, F, F, None, 1 << 30, 1 << 20, 4, dig.BI_BF16) == -4
+    assert dig.bi_backward_dx(F, None, F, 4, 4, 4, dig.BI_F16) == -1
+    assert dig.bi_backward_dx(F, F, F, 4, -4, 4, dig.BI_F16) == -3
+    assert dig.bi_fp8_mm(F, F, F, None, F, 4, 4, 4) == -1
+    assert dig.bi_fp8_mm(F, F, F, F, F, 4, -1, 4) == -3
+    # grouped: k, n, e must be positive; offsets needed on the MFMA tier
+    assert dig.bi_grouped_nt(F, F, F, F, F, 4, 0, 4, 2, dig.BI_BF16) == -3
+    assert dig.bi_grouped_nt(F, F, F, F, F, 4, 4, 4, 0, dig.BI_BF16) == -3
+    assert dig.bi_grouped_nt(F, F, F, F, None, 4, 128, 128, 2, dig.BI_BF16, tc=1) == -1
+    assert dig.bi_grouped_nt(F, F, F, None, F, 4, 128, 128, 2, dig.BI_BF16) == -1
+    assert dig.bi_grouped_nt_backward(F, F, F, F, F, F, None, 4, 8, 8, 2, dig.BI_BF16) == -1
+    assert dig.bi_grouped_nt_backward(F, None, F, F, F, F, F, 4, 8, 8, 2, dig.BI_BF16) == -1
+
+
+def test_dw_workspace_rules(lib):
+    # small output (few tiles): the reduction over m is chunked, workspace needed
+    m, k, n = 4096, 768, 48
+    need = dig.bi_backward_dw_workspace_bytes(m, k, n, dig.BI_BF16, 1)
+    tile, chunk = dig.bi_plan(dig.OP_DW, dig.BI_BF16, 1, k, n)
+    assert tile == 0 and chunk > 0
+    assert need == -(-m // chunk) * k * n * 4
+    assert dig.bi_backward_dw(F, F, F, m, k, n, dig.BI_BF16, None, 0) == -5
+    assert dig.bi_backward_dw(F, F, F, m, k, n, dig.BI_BF16, F, need - 1) == -5
+    # one chunk: no workspace
+    assert dig.bi_backward_dw_workspace_bytes(64, 128, 256, dig.BI_F32, 0) == 0
+    # invalid arguments report 0 bytes
+    assert dig.bi_backward_dw_workspace_bytes(-1, 4, 4, dig.BI_BF16, 1) == 0
+
+
+def test_empty_batch_is_a_noop(lib):
+    # m == 0: nothing to compute, nothing enqueued, success even with NULL data
+    assert dig.bi_forward(None, None, None, None, 0, 16, 16, dig.BI_BF16) == 0
+    assert dig.bi_backward_dx(None, None, None, 0, 16, 16, dig.BI_BF16) == 0
+    assert dig.bi_fp8_mm(None, None, None, None, None, 0, 16, 16) == 0
+    assert dig.bi_grouped_nt(None, None, None, None, None, 0, 16, 16, 2, dig.BI_BF16) == 0
+
+
+def test_plan_is_shape_only_and_follows_fallback_rule(lib):
+    # below 64 in a non-M output dim -> scalar tier; f32 -> scalar; tc=0 -> scalar
+    assert dig.bi_plan(dig.OP_FWD, dig.BI_BF16, 1, 768, 48)[0] == 0
+    assert dig.bi_plan(dig.OP_FWD, dig.BI_BF16, 1, 768, 3072)[0] > 0
+    assert dig.bi_plan(dig.OP_FWD, dig.BI_F32, 1, 768, 3072)[0] == 0
+    assert dig.bi_plan(dig.OP_FWD, dig.BI_BF16, 0, 768, 3072)[0] == 0
+    assert dig.bi_plan(dig.OP_DX, dig.BI_BF16, 1, 768, 48)[0] > 0   # dX output dim is K
+    assert dig.bi_plan(dig.OP_DX, dig.BI_BF16, 1, 48, 768)[0] == 0
+    assert dig.bi_plan(dig.OP_DW, dig.BI_BF16, 1, 768, 48)[0] == 0
+    assert dig.bi_plan(dig.OP_FP8, 0, 1, 4096, 4096)[0] > 0
+    # the scalar-tier dW chunk does not depend on dtype (bf16 == upcast f32)
+    for k, n in [(768, 48), (64, 64), (4096, 4096)]:
+        assert dig.bi_plan(dig.OP_DW, dig.BI_BF16, 0, k, n) == dig.bi_plan(dig.OP_DW, dig.BI_F32, 0, k, n)

@@ -1,0 +1,81 @@
+"""GPU parity of the per-tensor-scaled fp8 e4m3 GEMM against the CPU oracle,
+with the determinism contracts (run-to-run hashes, batch invariance)."""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_invariant_gemm_amd as dig
+import oracle
+import synth
+from parity import check, dev, digest, empty, f32_scalar, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+class Fp8:
+    def __init__(self, d):
+        self.d = d
+        self.m, self.k, self.n = d["m"], d["k"], d["n"]
+        self.a, self.bt = dev(d["a8"]), dev(d["bt8"])
+        self.da, self.db = f32_scalar(float(d["da"])), f32_scalar(float(d["db"]))
+
+    def run(self, tc, m=None):
+        m = self.m if m is None else m
+        y = empty((m, self.n), np.uint16)
+        dig.check(dig.bi_fp8_mm(y, self.a, self.bt, self.da, self.db, m, self.k, self.n,
+                                torch.cuda.current_stream(), tc), "bi_fp8_mm")
+        return y
+
+
+def test_e4m3_format_is_ocp():
+    """Code 0x7E must act as 448 (OCP e4m3fn), not 224 (the FNUZ flavour):
+    A = [[448]*64], B^T = [[1]*64] gives 64*448 = 28672 exactly."""
+    k = 64
+    for tc in (0, 1):
+        d = {"a8": np.full((64, k), 0x7E, np.uint8), "bt8": np.full((64, k), 0x38, np.uint8),
+             "da": np.float32(1.0), "db": np.float32(1.0), "m": 64, "k": k, "n": 64}
+        y = host(Fp8(d).run(tc), np.uint16)
+        assert np.all(y == synth.to_bits(np.array([28672.0], np.float32), synth.BF16)[0]), tc
+
+
+@pytest.mark.parametrize("tc", [0, 1])
+@pytest.mark.parametrize("shape", [(300, 256, 260), (129, 200, 96), (1, 64, 64),
+                                   (70, 1000, 130), (5, 7, 3)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_parity_small(tc, shape):
+    m, k, n = shape
+    d = synth.fp8(m, k, n, seed=200 + m + k)
+    print(f"fp8 parity tc={tc} shape={shape}", flush=True)
+    r = oracle.fp8_mm(d["a8"], d["bt8"], d["da"], d["db"], m, k, n)
+    check(host(Fp8(d).run(tc), np.uint16), r, synth.BF16, f"fp8 {shape}")
+
+
+@pytest.mark.parametrize("tc", [0, 1])
+@pytest.mark.parametrize("shape", [(300, 256, 260), (70, 1000, 130), (257, 4096, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_exact_integer_bits(tc, shape):
+    """Integer e4m3 codes in [-8, 8] with power-of-two scales: exact in any
+    summation order, so the GPU must equal the oracle bit for bit."""
+    m, k, n = shape
+    d = synth.fp8_integer(m, k, n, seed=9)
+    r = oracle.fp8_mm(d["a8"], d["bt8"], d["da"], d["db"], m, k, n)
+    assert np.array_equal(host(Fp8(d).run(tc), np.uint16), r.out)
+
+
+def test_config4_fp8():
+    """A[8192,4096], B^T[4096,4096] quantised from N(0,1) bf16 with scale
+    448/amax: sampled parity at M = 8192, full parity at M = 16 (the first 16
+    rows), 10-run hashes and batch invariance between the two."""
+    d = synth.config4()
+    F = Fp8(d)
+    m, k, n = F.m, F.k, F.n
+    y = host(F.run(1), np.uint16)
+    rows = sample_rows(m, 16, 6)
+    r = oracle.fp8_mm(d["a8"], d["bt8"], d["da"], d["db"], m, k, n, rows=rows)
+    print("config4 M=8192:", check(y[rows], r, synth.BF16, "config4 M=8192"))
+    y16 = host(F.run(1, m=16), np.uint16)
+    r16 = oracle.fp8_mm(d["a8"], d["bt8"], d["da"], d["db"], m, k, n, rows=np.arange(16))
+    print("config4 M=16:", check(y16, r16, synth.BF16, "config4 M=16"))
+    assert np.array_equal(y16, y[:16])
+    assert len({digest(F.run(1)) for _ in range(10)}) == 1
+    assert len({digest(F.run(1, m=16)) for _ in range(10)}) == 1

@@ -1,0 +1,121 @@
+"""GPU parity of the row-routed grouped GEMM (forward, dinput, f32 dweights)
+against the CPU oracle, which routes rows by row_experts alone; padding rows
+must be exact +0 bytes and experts without rows must get zero dweights."""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_invariant_gemm_amd as dig
+import oracle
+import synth
+from parity import check, dev, digest, empty, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+ST = {synth.F32: np.uint32, synth.BF16: np.uint16, synth.F16: np.uint16}
+
+
+class Grouped:
+    def __init__(self, d):
+        self.d = d
+        self.m, self.k, self.n, self.e, self.dt = d["m"], d["k"], d["n"], d["e"], d["dt"]
+        self.st = ST[self.dt]
+        self.inp, self.w, self.dy = dev(d["input"]), dev(d["weights"]), dev(d["dy"])
+        self.ids, self.off = dev(d["row_experts"]), dev(d["offsets"])
+
+    def forward(self, tc):
+        y = empty((self.m, self.n), self.st)
+        dig.check(dig.bi_grouped_nt(y, self.inp, self.w, self.ids, self.off, self.m, self.k,
+                                    self.n, self.e, self.dt, torch.cuda.current_stream(), tc),
+                  "bi_grouped_nt")
+        return y
+
+    def backward(self, tc):
+        di = empty((self.m, self.k), self.st)
+        dw = empty((self.e, self.n, self.k), np.uint32)
+        dig.check(dig.bi_grouped_nt_backward(di, dw, self.inp, self.w, self.dy, self.ids,
+                                             self.off, self.m, self.k, self.n, self.e, self.dt,
+                                             torch.cuda.current_stream(), tc),
+                  "bi_grouped_nt_backward")
+        return di, dw
+
+
+def parity(d, tc, what, rows=None, wrows=None):
+    G = Grouped(d)
+    m, k, n, e, dt = G.m, G.k, G.n, G.e, G.dt
+    ids = d["row_experts"]
+    y = host(G.forward(tc), G.st)
+    di, dw = G.backward(tc)
+    di, dw = host(di, G.st), host(dw, np.uint32).reshape(e * n, k)
+    rsel = np.arange(m) if rows is None else rows
+    wsel = np.arange(e * n) if wrows is None else wrows
+    ry = oracle.grouped_fwd(dt, d["input"], d["weights"], ids, m, k, n, e, rows=rsel)
+    check(y[rsel], ry, dt, f"{what} fwd")
+    rd = oracle.grouped_dinput(dt, d["dy"], d["weights"], ids, m, k, n, e, rows=rsel)
+    check(di[rsel], rd, dt, f"{what} dinput")
+    rw = oracle.grouped_dweights(dt, d["input"], d["dy"], ids, m, k, n, e, rows=wsel)
+    check(dw[wsel], rw, synth.F32, f"{what} dweights")
+    pad = ids >= e
+    assert np.all(y[pad] == 0) and np.all(di[pad] == 0), "padding rows must be +0 bytes"
+    return y, di, dw
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.F16, synth.F32])
+@pytest.mark.parametrize("tc", [0, 1])
+@pytest.mark.parametrize("case", [(300, 136, 200, 5, 17, (2,)), (129, 64, 64, 3, 0, ()),
+                                  (520, 72, 260, 8, 40, (0, 7)), (7, 8, 5, 2, 2, ())],
+                         ids=lambda c: "m{}k{}n{}e{}".format(*c[:4]))
+def test_grouped_parity_small(dt, tc, case):
+    m, k, n, e, pad, empty_experts = case
+    d = synth.grouped(m, k, n, e, dt, seed=300 + m, pad_rows=pad, empty=empty_experts,
+                      sigma_w=0.05)
+    print(f"grouped parity dt={dt} tc={tc} case={case}", flush=True)
+    y, di, dw = parity(d, tc, f"grouped {case}")
+    for x in empty_experts:
+        assert np.all(dw.reshape(e, n, k)[x] == 0)
+
+
+@pytest.mark.parametrize("tc", [0, 1])
+def test_grouped_exact_integer_bits(tc):
+    dt = synth.BF16
+    m, k, n, e = 600, 200, 136, 6
+    ids, offsets = synth.route(m, e, seed=12, pad_rows=31, empty=(3,))
+    d = {"input": synth.integer_bits((m, k), -3, 3, 12, 0, dt),
+         "weights": synth.integer_bits((e, n, k), -3, 3, 12, 1, dt),
+         "dy": synth.integer_bits((m, n), -3, 3, 12, 3, dt),
+         "row_experts": ids, "offsets": offsets, "m": m, "k": k, "n": n, "e": e, "dt": dt}
+    G = Grouped(d)
+    y = host(G.forward(tc), np.uint16)
+    di, dw = G.backward(tc)
+    assert np.array_equal(y, oracle.grouped_fwd(dt, d["input"], d["weights"], ids, m, k, n, e).out)
+    assert np.array_equal(host(di, np.uint16),
+                          oracle.grouped_dinput(dt, d["dy"], d["weights"], ids, m, k, n, e).out)
+    assert np.array_equal(host(dw, np.uint32).reshape(e * n, k),
+                          oracle.grouped_dweights(dt, d["input"], d["dy"], ids, m, k, n, e).out)
+
+
+def test_config5_grouped():
+    """input[16384,2048], weights[8,1408,2048], 819 padding rows: sampled parity
+    of forward, dinput and dweights, padding rows +0 bytes, 10-run hashes;
+    then the same with expert 5 emptied (its dweights must be zero)."""
+    d = synth.config5()
+    G = Grouped(d)
+    rows = sample_rows(G.m, 40, 7)
+    rows = np.union1d(rows, np.nonzero(d["row_experts"] >= G.e)[0][:8])
+    wrows = sample_rows(G.e * G.n, 16, 8)
+    parity(d, 1, "config5", rows=rows, wrows=wrows)
+    assert len({digest(G.forward(1)) for _ in range(10)}) == 1
+    hs = set()
+    for _ in range(10):
+        di, dw = G.backward(1)
+        hs.add((digest(di), digest(dw)))
+    assert len(hs) == 1
+    d2 = synth.config5(empty=(5,))
+    G2 = Grouped(d2)
+    _, dw2 = G2.backward(1)
+    dw2 = host(dw2, np.uint32).reshape(G2.e, G2.n, G2.k)
+    assert np.all(dw2[5] == 0)
+    wr = np.array([5 * G2.n, 5 * G2.n + 7, 2 * G2.n + 3], dtype=np.int64)
+    rw = oracle.grouped_dweights(d2["dt"], d2["input"], d2["dy"], d2["row_experts"], G2.m,
+                                 G2.k, G2.n, G2.e, rows=wr)
+    check(dw2.reshape(G2.e * G2.n, G2.k)[wr], rw, synth.F32, "config5 empty-expert dweights")

@@ -1,0 +1,236 @@
+"""GPU parity of the linear trio (forward, dX, dW) against the CPU oracle,
+plus the determinism contracts: run-to-run byte equality, batch invariance of
+the forward, identical bits across tile shapes, and the scalar tier's
+bf16/f16 == RNE(f32 tier on upcast inputs) statement."""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_invariant_gemm_amd as dig
+import oracle
+import synth
+from parity import check, dev, digest, empty, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+ST = {synth.F32: np.uint32, synth.BF16: np.uint16, synth.F16: np.uint16}
+
+
+class Linear:
+    """Device copies of one linear workload and calls through the C ABI."""
+
+    def __init__(self, d):
+        self.d = d
+        self.m, self.k, self.n, self.dt = d["m"], d["k"], d["n"], d["dt"]
+        self.st = ST[self.dt]
+        self.x, self.w, self.dy = dev(d["x"]), dev(d["w"]), dev(d["dy"])
+        self.b = dev(d["b"]) if d["b"] is not None else None
+
+    def forward(self, tc, m=None):
+        m = self.m if m is None else m
+        y = empty((m, self.n), self.st)
+        dig.check(dig.bi_forward(y, self.x, self.w, self.b, m, self.k, self.n, self.dt,
+                                 torch.cuda.current_stream(), tc), "bi_forward")
+        return y
+
+    def dx(self, tc, m=None):
+        m = self.m if m is None else m
+        out = empty((m, self.k), self.st)
+        dig.check(dig.bi_backward_dx(out, self.dy, self.w, m, self.k, self.n, self.dt,
+                                     torch.cuda.current_stream(), tc), "bi_backward_dx")
+        return out
+
+    def dw(self, tc):
+        out = empty((self.k, self.n), self.st)
+        nbytes = dig.bi_backward_dw_workspace_bytes(self.m, self.k, self.n, self.dt, tc)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        ws.fill_(255)
+        dig.check(dig.bi_backward_dw(out, self.x, self.dy, self.m, self.k, self.n, self.dt,
+                                     ws if nbytes else None, nbytes,
+                                     torch.cuda.current_stream(), tc), "bi_backward_dw")
+        return out
+
+
+def full_parity(d, tc, what):
+    L = Linear(d)
+    m, k, n, dt = L.m, L.k, L.n, L.dt
+    ry = oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n)
+    check(host(L.forward(tc), L.st), ry, dt, f"{what} fwd")
+    rx = oracle.linear_dx(dt, d["dy"], d["w"], m, k, n)
+    check(host(L.dx(tc), L.st), rx, dt, f"{what} dX")
+    rw = oracle.linear_dw(dt, d["x"], d["dy"], m, k, n)
+    check(host(L.dw(tc), L.st), rw, dt, f"{what} dW")
+
+
+# shapes spanning several tiles of every tier, with ragged tails in every dim
+SHAPES = [(300, 200, 260), (129, 72, 96), (1, 64, 64), (257, 1000, 130), (70, 136, 72),
+          (64, 33, 65), (5, 7, 3)]
+
+
+@pytest.mark.parametrize("dt", [synth.F32, synth.BF16, synth.F16])
+@pytest.mark.parametrize("tc", [0, 1])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_linear_parity_small(dt, tc, shape):
+    m, k, n = shape
+    d = synth.linear(m, k, n, dt, seed=100 + m + k + n, sigma_w=0.05)
+    print(f"linear parity dt={dt} tc={tc} shape={shape}", flush=True)
+    full_parity(d, tc, f"dt{dt} tc{tc} {shape}")
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.F16, synth.F32])
+@pytest.mark.parametrize("tc", [0, 1])
+@pytest.mark.parametrize("shape", [(300, 200, 260), (257, 1000, 130), (4100, 96, 72),
+                                   (33, 4096, 64)], ids=lambda s: "x".join(map(str, s)))
+def test_linear_exact_integer_bits(dt, tc, shape):
+    """Small-integer operands: every partial sum is an exactly representable
+    integer, so f32 accumulation is exact in any order and every tier, tile,
+    chunking and layout must reproduce the oracle bit for bit."""
+    m, k, n = shape
+    d = synth.linear_integer(m, k, n, dt, seed=7 + m, lo=-3, hi=3)
+    L = Linear(d)
+    print(f"exact integer dt={dt} tc={tc} shape={shape}", flush=True)
+    ry = oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n)
+    assert np.array_equal(host(L.forward(tc), L.st), ry.out)
+    rx = oracle.linear_dx(dt, d["dy"], d["w"], m, k, n)
+    assert np.array_equal(host(L.dx(tc), L.st), rx.out)
+    rw = oracle.linear_dw(dt, d["x"], d["dy"], m, k, n)
+    assert np.array_equal(host(L.dw(tc), L.st), rw.out)
+
+
+def test_config1_f32():
+    """f32 X[64,128] W[128,256] + b, dY[64,256]: parity, 10-run hashes and batch
+    invariance at M' in {1, 7, 64}."""
+    d = synth.config1()
+    full_parity(d, 1, "config1")
+    L = Linear(d)
+    for op in (lambda: L.forward(1), lambda: L.dx(1), lambda: L.dw(1)):
+        assert len({digest(op()) for _ in range(10)}) == 1
+    y = host(L.forward(1), np.uint32)
+    for mp in (1, 7, 64):
+        assert np.array_equal(host(L.forward(1, m=mp), np.uint32), y[:mp])
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
+def test_config2_parity_sampled(dt):
+    """X[4096,768] W[768,3072] + b, dY[4096,3072] on the MFMA tier: sampled
+    output rows against the oracle (rows for forward and dX, K-rows for dW)."""
+    d = synth.config2(dt)
+    L = Linear(d)
+    m, k, n = L.m, L.k, L.n
+    rows = sample_rows(m, 48, 1)
+    stats = []
+    ry = oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n, rows=rows)
+    stats.append(check(host(L.forward(1), L.st)[rows], ry, dt, "config2 fwd"))
+    rx = oracle.linear_dx(dt, d["dy"], d["w"], m, k, n, rows=rows)
+    stats.append(check(host(L.dx(1), L.st)[rows], rx, dt, "config2 dX"))
+    krows = sample_rows(k, 24, 2)
+    rw = oracle.linear_dw(dt, d["x"], d["dy"], m, k, n, rows=krows)
+    stats.append(check(host(L.dw(1), L.st)[krows], rw, dt, "config2 dW"))
+    print("config2 (max ulp, #A-clause, max rel):", stats)
+
+
+def test_config2_determinism_and_batch_invariance():
+    d = synth.config2(synth.BF16)
+    L = Linear(d)
+    for name, op in (("fwd", lambda: L.forward(1)), ("dX", lambda: L.dx(1)),
+                     ("dW", lambda: L.dw(1))):
+        assert len({digest(op()) for _ in range(10)}) == 1, name
+    y = host(L.forward(1), np.uint16)
+    dx = host(L.dx(1), np.uint16)
+    for mp in (1, 7, 64, 4096):
+        assert np.array_equal(host(L.forward(1, m=mp), np.uint16), y[:mp]), mp
+        assert np.array_equal(host(L.dx(1, m=mp), np.uint16), dx[:mp]), mp
+
+
+def test_config2_narrow_n48():
+    """N = 48 < 64: forward and dW fall back to the scalar tier, dX (output dim
+    K = 768) stays on MFMA; sampled parity and run-to-run hashes."""
+    d = synth.config2(synth.BF16, n=48, seed=22)
+    L = Linear(d)
+    m, k, n, dt = L.m, L.k, L.n, L.dt
+    assert dig.bi_plan(dig.OP_FWD, dt, 1, k, n)[0] == 0
+    assert dig.bi_plan(dig.OP_DW, dt, 1, k, n)[0] == 0
+    assert dig.bi_plan(dig.OP_DX, dt, 1, k, n)[0] > 0
+    rows = sample_rows(m, 64, 3)
+    ry = oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n, rows=rows)
+    check(host(L.forward(1), L.st)[rows], ry, dt, "n48 fwd")
+    rx = oracle.linear_dx(dt, d["dy"], d["w"], m, k, n, rows=rows)
+    check(host(L.dx(1), L.st)[rows], rx, dt, "n48 dX")
+    rw = oracle.linear_dw(dt, d["x"], d["dy"], m, k, n)
+    check(host(L.dw(1), L.st), rw, dt, "n48 dW")
+    for op in (lambda: L.forward(1), lambda: L.dx(1), lambda: L.dw(1)):
+        assert len({digest(op()) for _ in range(10)}) == 1
+    y = host(L.forward(1), np.uint16)
+    for mp in (1, 7, 64):
+        assert np.array_equal(host(L.forward(1, m=mp), np.uint16), y[:mp])
+
+
+def test_scalar_tier_bf16_is_rne_of_f32_on_upcast():
+    """Scalar-tier contract: the bf16 (and f16) result equals the f32 tier run on
+    the exactly upcast inputs, then rounded once to nearest-even."""
+    for dt in (synth.BF16, synth.F16):
+        d = synth.linear(130, 300, 70, dt, seed=31, sigma_w=0.05)
+        up = dict(d)
+        for t in ("x", "w", "b", "dy"):
+            up[t] = synth.to_bits(synth.to_f32(d[t], dt), synth.F32)
+        up["dt"] = synth.F32
+        Lb, Lf = Linear(d), Linear(up)
+        for name in ("forward", "dx", "dw"):
+            low = host(getattr(Lb, name)(0), np.uint16)
+            f32 = host(getattr(Lf, name)(0), np.uint32).view(np.float32)
+            assert np.array_equal(low, synth.to_bits(f32, dt)), (dt, name)
+
+
+def test_tile_families_give_identical_bits():
+    """The same output columns computed under different tile shapes (the plan
+    picks the tile from N) are bit-identical."""
+    dt = synth.BF16
+    m, k = 600, 512
+    d = synth.linear(m, k, 4096, dt, seed=41, sigma_w=0.02)
+    full = Linear(d)
+    y_full = host(full.forward(1), np.uint16)
+    tiles = {dig.bi_plan(dig.OP_FWD, dt, 1, k, 4096)[0]}
+    for n in (3072, 384, 96):
+        sub = dict(d)
+        sub["w"] = np.ascontiguousarray(d["w"][:, :n])
+        sub["b"] = np.ascontiguousarray(d["b"][:n])
+        sub["dy"] = np.ascontiguousarray(d["dy"][:, :n])
+        sub["n"] = n
+        tiles.add(dig.bi_plan(dig.OP_FWD, dt, 1, k, n)[0])
+        y = host(Linear(sub).forward(1), np.uint16)
+        assert np.array_equal(y, y_full[:, :n]), n
+    assert len(tiles) >= 3, tiles
+
+
+def test_config3_batch_invariance_sweep():
+    """W[4096,4096], X[8192,4096]: every shared row is bit-identical across
+    M in {1, 3, 17, 128, 1000, 8192}; dW at M = 8192 hashed 10 times; sampled
+    oracle parity of the forward at M = 8192 and of dW."""
+    d = synth.config3()
+    L = Linear(d)
+    y = host(L.forward(1), np.uint16)
+    for mp in (1, 3, 17, 128, 1000, 8192):
+        assert np.array_equal(host(L.forward(1, m=mp), np.uint16), y[:mp]), mp
+    rows = sample_rows(L.m, 12, 4)
+    ry = oracle.linear_forward(L.dt, d["x"], d["w"], None, L.m, L.k, L.n, rows=rows)
+    check(y[rows], ry, L.dt, "config3 fwd")
+    hashes = {digest(L.dw(1)) for _ in range(10)}
+    assert len(hashes) == 1
+    krows = sample_rows(L.k, 4, 5)
+    rw = oracle.linear_dw(L.dt, d["x"], d["dy"], L.m, L.k, L.n, rows=krows)
+    check(host(L.dw(1), np.uint16)[krows], rw, L.dt, "config3 dW")
+
+
+def test_k_zero_gives_rounded_bias_and_m_zero_dw_is_zero():
+    dt = synth.BF16
+    b = dev(synth.normal_bits((96,), 1.0, 5, 0, dt))
+    y = empty((3, 96), np.uint16)
+    x = torch.empty(1, dtype=torch.int16, device="cuda")
+    w = torch.empty(1, dtype=torch.int16, device="cuda")
+    for tc in (0, 1):
+        dig.check(dig.bi_forward(y, x, w, b, 3, 0, 96, dt, torch.cuda.current_stream(), tc))
+        assert np.array_equal(host(y, np.uint16), np.tile(host(b, np.uint16), (3, 1)))
+        dw = empty((70, 96), np.uint16)
+        dig.check(dig.bi_backward_dw(dw, x, x, 0, 70, 96, dt, None, 0,
+                                     torch.cuda.current_stream(), tc))
+        assert np.all(host(dw, np.uint16) == 0)
