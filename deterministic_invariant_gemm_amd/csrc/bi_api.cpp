@@ -19,8 +19,6 @@ enum Op : int { OP_FWD = 0, OP_DX = 1, OP_DW = 2, OP_FP8 = 3, OP_GFWD = 4, OP_GD
 
 bool dtype_ok(int dt) { return dt == BI_F32 || dt == BI_BF16 || dt == BI_F16; }
 
-int64_t elem_size(int dt) { return dt == BI_F32 ? 4 : 2; }
-
 // product of non-negative dims within kMaxElems, else -1
 int64_t checked_elems(int64_t a, int64_t b, int64_t c = 1) {
     if (a < 0 || b < 0 || c < 0) return -1;
@@ -29,6 +27,7 @@ int64_t checked_elems(int64_t a, int64_t b, int64_t c = 1) {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned8(const void *p) { return ((uintptr_t)p & 7u) == 0; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -51,31 +50,38 @@ bool mfma_eligible(int op, int dt, int tc, int64_t k, int64_t n) {
     return false;
 }
 
-// output columns and reduction length, seen from the kernel
+// Tile per op from the non-M output dims only (the kernel's column count is N
+// for forward / fp8 / grouped forward, K for dX / grouped dinput; dW tiles its
+// [K, N] output).  Every tile issues the same MFMA sequence per element, so
+// this choice affects speed only.
 int pick_tile(int op, int64_t k, int64_t n) {
-    int64_t cols = (op == OP_DX || op == OP_GDIN) ? k : n;
+    const int64_t cols = (op == OP_DX || op == OP_GDIN) ? k : n;
     switch (op) {
     case OP_FWD:
-        if (cols >= 2048 && cols % 256 == 0) return 1;  // 256x256
-        if (cols >= 2048 && cols % 192 == 0) return 2;  // 256x192
+    case OP_FP8:
+        if (cols >= 2048 && cols % 192 == 0 && cols / 192 <= 16) return 2;  // 256x192
+        if (cols >= 2048) return 1;                                           // 256x256
         return cols >= 128 ? 4 : 6;
     case OP_DX:
         return cols >= 128 ? 4 : 6;
     case OP_DW:
         return (k >= 128 && n >= 128) ? 4 : 6;
-    case OP_FP8:
-        if (cols >= 2048 && cols % 256 == 0) return 1;
-        return cols >= 128 ? 4 : 6;
     case OP_GFWD: case OP_GDIN: case OP_GDW:
         return 4;
     }
     return 4;
 }
 
+// tc >= 16 is a tuning / test hook: tc = 16 + id forces MFMA tile `id` (when the
+// op is on the MFMA tier).  Tiles do not change results.
+constexpr int kForceBase = 16;
+
 Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
     Plan pl{0, kNoSplit};
     if (mfma_eligible(op, dt, tc, k, n)) pl.tile = pick_tile(op, k, n);
     if (op == OP_DW) {
+        // the chunk length follows from the default tile of (k, n), so a
+        // forced tile below never changes the reduction order
         if (pl.tile) {
             const TileShape *ts = mfma_tile(pl.tile);
             const int64_t tiles = cdiv(k, ts->bm) * cdiv(n, ts->bn);
@@ -86,6 +92,7 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
             pl.chunk = tiles >= 128 ? kNoSplit : 256;
         }
     }
+    if (pl.tile && tc >= kForceBase && mfma_tile(tc - kForceBase)) pl.tile = tc - kForceBase;
     return pl;
 }
 
@@ -145,6 +152,7 @@ int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t 
     a.tiles_i = cdiv(m, ts->bm); a.tiles_j = cdiv(n, ts->bn);
     a.vec_a = aligned16(x) && k % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
+    a.vec_c = aligned8(y) && n % 4 == 0;
     return hip_status(launch_mfma_gemm(a, pl.tile, dtype, /*layout A rc, B strided*/ 1, 0, stream));
 }
 
@@ -173,6 +181,7 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
     a.tiles_i = cdiv(m, ts->bm); a.tiles_j = cdiv(k, ts->bn);
     a.vec_a = aligned16(dy) && n % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
+    a.vec_c = aligned8(dx) && k % 4 == 0;
     return hip_status(launch_mfma_gemm(a, pl.tile, dtype, /*both rc*/ 3, 0, stream));
 }
 
@@ -217,6 +226,7 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
         a.tiles_i = cdiv(k, ts->bm); a.tiles_j = cdiv(n, ts->bn);
         a.vec_a = aligned16(x) && k % 8 == 0;
         a.vec_b = aligned16(dy) && n % 8 == 0;
+        a.vec_c = epi ? (aligned16(workspace) && n % 4 == 0) : (aligned8(dw) && n % 4 == 0);
         e = launch_mfma_gemm(a, pl.tile, dtype, /*both strided*/ 0, epi, stream);
     }
     if (e != hipSuccess) return BI_ERR_HIP;
@@ -254,6 +264,7 @@ int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
     f.m = m; f.n = n; f.k = k;
     f.tiles_i = cdiv(m, ts->bm); f.tiles_j = cdiv(n, ts->bn);
     f.vec = aligned16(a) && aligned16(bt) && k % 16 == 0;
+    f.vec_c = aligned8(y) && n % 4 == 0;
     return hip_status(launch_fp8_gemm(f, pl.tile, stream));
 }
 
@@ -290,6 +301,7 @@ int bi_grouped_nt(void *y, const void *input, const void *weights, const uint32_
     a.seg_tiles = cdiv(m, ts->bm) + e;
     a.vec_a = aligned16(input) && k % 8 == 0;
     a.vec_b = aligned16(weights) && k % 8 == 0;
+    a.vec_c = aligned8(y) && n % 4 == 0;
     return hip_status(launch_mfma_gemm(a, pl.tile, dtype, 3, 0, stream));
 }
 
@@ -320,6 +332,7 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
             a.seg_tiles = cdiv(m, ts->bm) + e;
             a.vec_a = aligned16(grad_out) && n % 8 == 0;
             a.vec_b = aligned16(weights) && k % 8 == 0;
+            a.vec_c = aligned8(dinput) && k % 4 == 0;
             er = launch_mfma_gemm(a, pl.tile, dtype, 1, 0, stream);
         }
         if (er != hipSuccess) return BI_ERR_HIP;
@@ -340,6 +353,7 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
     a.red_offsets = offsets; a.n_experts = e; a.c_expert_stride = n * k;
     a.vec_a = aligned16(grad_out) && n % 8 == 0;
     a.vec_b = aligned16(input) && k % 8 == 0;
+    a.vec_c = aligned16(dweights) && k % 4 == 0;
     return hip_status(launch_mfma_gemm(a, pw.tile, dtype, 0, 2, stream));
 }
 

@@ -12,6 +12,8 @@
 // never change the bits.  Both operands are k-contiguous, so staging is a
 // straight 16-byte copy into a k-grouped, XOR-swizzled LDS layout (16 fp8
 // values per slot); an operand fragment of one lane is two adjacent slots.
+// Pipeline: two LDS buffers, one slice in registers ahead, one barrier per
+// slice; branch-free vector loads for interior tiles, masked loads at edges.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -27,34 +29,48 @@ __device__ __forceinline__ int swz(int row, int kg) {
     return (row & ~7) | ((row ^ (row >> 3) ^ kg) & 7);
 }
 
-// 16 consecutive fp8 codes from p[0], zero beyond `count`.
-__device__ __forceinline__ u32x4 load16(const uint8_t *p, int count, bool vec) {
-    if (count >= 16 && vec) return *reinterpret_cast<const u32x4 *>(p);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        if (i < count) w[i >> 2] |= (uint32_t)p[i] << (8 * (i & 3));
-    return u32x4{w[0], w[1], w[2], w[3]};
-}
-
 template <int R>
 struct Stage8 {
     static constexpr int PER_THREAD = R * KG / NT;
     static_assert((R * KG) % NT == 0, "tile rows must fill the workgroup");
     u32x4 reg[PER_THREAD];
 
-    __device__ __forceinline__ void load(const uint8_t *p, int64_t ld, int64_t row0,
-                                         int64_t row_end, int64_t rk, int64_t r_end, bool vec,
-                                         int t) {
+    // whole tile and slice in range, 16-byte aligned rows: vector loads
+    __device__ __forceinline__ void load_fast(const uint8_t *p, int64_t ld, int64_t row0,
+                                              int64_t rk, int t) {
 #pragma unroll
         for (int q = 0; q < PER_THREAD; ++q) {
             const int c = t + NT * q;
             const int row = c / KG, kg = c % KG;
-            const int64_t gi = row0 + row, gr = rk + 16 * kg;
-            int cnt = gi < row_end ? (int)(r_end - gr < 16 ? r_end - gr : 16) : 0;
-            if (cnt < 0) cnt = 0;
-            reg[q] = cnt > 0 ? load16(p + gi * ld + gr, cnt, vec) : u32x4{0u, 0u, 0u, 0u};
+            reg[q] = *reinterpret_cast<const u32x4 *>(p + (row0 + row) * ld + rk + 16 * kg);
         }
+    }
+    // masked: clamped addresses, zero outside [row0,row_end) x [rk,r_end)
+    __device__ __forceinline__ void load_masked(const uint8_t *p, int64_t ld, int64_t row0,
+                                                int64_t row_end, int64_t rk, int64_t r_end,
+                                                int t) {
+#pragma unroll
+        for (int q = 0; q < PER_THREAD; ++q) {
+            const int c = t + NT * q;
+            const int row = c / KG, kg = c % KG;
+            const int64_t gi = row0 + row;
+            const int64_t gic = gi < row_end ? gi : row_end - 1;
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                const int64_t gr = rk + 16 * kg + x;
+                const int64_t grc = gr < r_end ? gr : r_end - 1;
+                const uint32_t v = p[gic * ld + grc];
+                w[x >> 2] |= ((gi < row_end && gr < r_end) ? v : 0u) << (8 * (x & 3));
+            }
+            reg[q] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+    }
+    __device__ __forceinline__ void load(const uint8_t *p, int64_t ld, int64_t row0,
+                                         int64_t row_end, int64_t rk, int64_t r_end,
+                                         bool interior, int t) {
+        if (interior && rk + BK <= r_end) load_fast(p, ld, row0, rk, t);
+        else load_masked(p, ld, row0, row_end, rk, r_end, t);
     }
     __device__ __forceinline__ void store(u32x4 *lds, int t) const {
 #pragma unroll
@@ -72,14 +88,13 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
     constexpr int FM = WTM / 32, FN = WTN / 32;
     static_assert(WGM * WGN == 4 && FM * 32 == WTM && FN * 32 == WTN, "wave tiling");
 
-    __shared__ u32x4 lds_a[KG * BM];
-    __shared__ u32x4 lds_b[KG * BN];
+    __shared__ u32x4 lds_a[2][KG * BM];
+    __shared__ u32x4 lds_b[2][KG * BN];
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    const int64_t tiles = p.tiles_i * p.tiles_j;
     const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
     constexpr int64_t GROUP = 4;
     const int64_t per_group = GROUP * p.tiles_j;
@@ -88,7 +103,6 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
     const int64_t in_g = tile % per_group;
     const int64_t row0 = (first + in_g % gsz) * BM;
     const int64_t col0 = (in_g / gsz) * BN;
-    (void)tiles;
 
     Stage8<BM> sa;
     Stage8<BN> sb;
@@ -98,20 +112,34 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const bool vec = p.vec != 0;
-    if (p.k > 0) {
-        sa.load(p.a, p.k, row0, p.m, 0, p.k, vec, t);
-        sb.load(p.bt, p.k, col0, p.n, 0, p.k, vec, t);
-    }
+    const bool int_a = p.vec != 0 && row0 + BM <= p.m;
+    const bool int_b = p.vec != 0 && col0 + BN <= p.n;
     const int lrow = lane & 31, lhalf = lane >> 5;
-    for (int64_t rk = 0; rk < p.k; rk += BK) {
-        sa.store(lds_a, t);
-        sb.store(lds_b, t);
-        __syncthreads();
-        if (rk + BK < p.k) {
-            sa.load(p.a, p.k, row0, p.m, rk + BK, p.k, vec, t);
-            sb.load(p.bt, p.k, col0, p.n, rk + BK, p.k, vec, t);
+    const int64_t nst = (p.k + BK - 1) / BK;
+
+    if (nst > 0) {
+        sa.load(p.a, p.k, row0, p.m, 0, p.k, int_a, t);
+        sb.load(p.bt, p.k, col0, p.n, 0, p.k, int_b, t);
+        sa.store(lds_a[0], t);
+        sb.store(lds_b[0], t);
+        if (nst > 1) {
+            sa.load(p.a, p.k, row0, p.m, BK, p.k, int_a, t);
+            sb.load(p.bt, p.k, col0, p.n, BK, p.k, int_b, t);
         }
+        __syncthreads();
+    }
+    for (int64_t s = 0; s < nst; ++s) {
+        const int cur = (int)(s & 1);
+        if (s + 1 < nst) {
+            sa.store(lds_a[cur ^ 1], t);
+            sb.store(lds_b[cur ^ 1], t);
+            if (s + 2 < nst) {
+                sa.load(p.a, p.k, row0, p.m, (s + 2) * BK, p.k, int_a, t);
+                sb.load(p.bt, p.k, col0, p.n, (s + 2) * BK, p.k, int_b, t);
+            }
+        }
+        const u32x4 *la = lds_a[cur];
+        const u32x4 *lb = lds_b[cur];
 #pragma unroll
         for (int kk = 0; kk < BK / 64; ++kk) {
             // this lane's 32 reduction values of the step: groups kg0, kg0 + 1
@@ -120,16 +148,16 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int row = wm * WTM + 32 * i + lrow;
-                const u32x4 lo = lds_a[kg0 * BM + swz(row, kg0)];
-                const u32x4 hi = lds_a[(kg0 + 1) * BM + swz(row, kg0 + 1)];
+                const u32x4 lo = la[kg0 * BM + swz(row, kg0)];
+                const u32x4 hi = la[(kg0 + 1) * BM + swz(row, kg0 + 1)];
                 fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
                 const int row = wn * WTN + 32 * j + lrow;
-                const u32x4 lo = lds_b[kg0 * BN + swz(row, kg0)];
-                const u32x4 hi = lds_b[(kg0 + 1) * BN + swz(row, kg0 + 1)];
+                const u32x4 lo = lb[kg0 * BN + swz(row, kg0)];
+                const u32x4 hi = lb[(kg0 + 1) * BN + swz(row, kg0 + 1)];
                 fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             }
@@ -137,27 +165,42 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    // format codes 0/0: both operands OCP fp8 e4m3; no block scales
+                    // B fragment first: the lane then holds 4 consecutive output
+                    // columns of one row.  Format codes 0/0: both operands OCP
+                    // fp8 e4m3; no block scales.
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fa[i], fb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+                        fb[j], fa[i], acc[i][j], 0, 0, 0, 0, 0, 0);
         }
         __syncthreads();
     }
 
     const float sa_v = p.scale_a[0], sb_v = p.scale_b[0];
+    const bool vec_c = p.vec_c != 0;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int64_t gj = col0 + wn * WTN + 32 * j + lrow;
-        if (gj >= p.n) continue;
+    for (int i = 0; i < FM; ++i) {
+        const int64_t gi = row0 + wm * WTM + 32 * i + lrow;
+        if (gi >= p.m) continue;
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t gi = row0 + wm * WTM + 32 * i + 8 * (v >> 2) + 4 * lhalf + (v & 3);
-                if (gi >= p.m) continue;
-                float val = acc[i][j][v] * sa_v;
-                val = val * sb_v;
-                p.c[gi * p.n + gj] = (uint16_t)f32_to_bf16_bits(val);
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int64_t gj = col0 + wn * WTN + 32 * j + 8 * g4 + 4 * lhalf;
+                if (gj >= p.n) continue;
+                uint32_t h[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    float v = acc[i][j][4 * g4 + x] * sa_v;
+                    v = v * sb_v;
+                    h[x] = f32_to_bf16_bits(v);
+                }
+                uint16_t *pc = p.c + gi * p.n + gj;
+                if (vec_c && gj + 4 <= p.n) {
+                    *reinterpret_cast<u32x2 *>(pc) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                } else {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        if (gj + x < p.n) pc[x] = (uint16_t)h[x];
+                }
             }
         }
     }

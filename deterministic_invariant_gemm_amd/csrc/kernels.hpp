@@ -63,6 +63,7 @@ struct MfmaArgs {
     const uint32_t *red_offsets;
     int64_t c_expert_stride;
     int vec_a, vec_b;  // 16-byte vector loads allowed for A / B
+    int vec_c;         // 8-byte (16-bit outputs) / 16-byte (f32) vector stores allowed
 };
 
 struct Fp8Args {
@@ -72,7 +73,8 @@ struct Fp8Args {
     const float *scale_a, *scale_b;
     int64_t m, n, k;
     int64_t tiles_i, tiles_j;
-    int vec;
+    int vec;    // 16-byte vector loads allowed
+    int vec_c;  // 8-byte vector stores allowed
 };
 
 hipError_t launch_scalar_gemm(const ScalarGemmArgs &p, int dt_in, int dt_out, int epi,

@@ -1,0 +1,580 @@
+// MFMA tier for bf16 / f16 operands on gfx950 (sgemm-bi PyPI page,
+// "Determinism contracts": tensor-core tier with f32 accumulation, bit-identical
+// across runs, forward strictly batch-invariant across all M, several tile
+// families giving the same bits).
+//
+// One kernel template serves the linear forward, dX, dW (and pass 1 of the
+// chunked dW), and the grouped forward / dinput / dweights (rublas
+// tensor_grouped/mod.rs).  It computes C(i,j) = sum_r A(i,r) B(j,r) with:
+//   * v_mfma_f32_32x32x16_{bf16,f16} as the only arithmetic on the reduction:
+//     each output element's accumulator starts at +0 and receives one MFMA per
+//     16-deep reduction step, steps in ascending order from the start of the
+//     reduction range.  Neither the tile shape nor the element's position in
+//     its tile changes that sequence, so all tile shapes give the same bits and
+//     a row's bits never depend on the number of rows (M).
+//   * 64-deep reduction slices staged global -> registers -> LDS with two LDS
+//     buffers: while slice s is multiplied out of one buffer, slice s+1 (loaded
+//     one slice earlier) is written to the other and slice s+2 is fetched from
+//     global memory.  One workgroup barrier per slice.
+//   * Interior tiles with full slices take a branch-free path of 16-byte vector
+//     loads; edge tiles and the last partial slice take a branch-free masked
+//     path (clamped addresses, zero-selected values), so no load waits on
+//     another.
+//   * LDS layout "k-grouped": for every group of 8 consecutive reduction
+//     indices, each tile row owns one 16-byte slot holding those 8 values, so
+//     an MFMA operand (8 consecutive reduction values of one row per lane) is a
+//     single ds_read_b128.  Slots are XOR-swizzled within groups of 8 rows so
+//     that the reads, the direct writes and the transposed writes spread over
+//     the banks.
+//   * Operands whose reduction index is contiguous in memory are copied as
+//     16-byte vectors; operands whose reduction index is strided (W in the
+//     forward, X and dY in dW, ...) are loaded as 8x8 element blocks and
+//     transposed in registers before the LDS write.
+//   * The MFMA is issued with the B fragment as its first operand, so each lane
+//     ends up holding 4 consecutive output columns of one row: the epilogue
+//     stores 8 bytes (bf16/f16) or 16 bytes (f32) per instruction.
+//   * Workgroup ids are remapped so that the 32 CUs of one XCD work on one
+//     compact block of output tiles and share operand rows in that XCD's L2.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace bi {
+
+namespace mfma {
+
+constexpr int BK = 64;      // reduction slice per LDS stage
+constexpr int KG = BK / 8;  // 8-element groups per slice
+constexpr int NT = 256;     // threads per workgroup (4 waves)
+
+enum Mode : int { MODE_PLAIN = 0, MODE_SEGMENTS = 1, MODE_EXPERT_RED = 2 };
+enum Epi : int { EPI_ROUND = 0, EPI_PARTIAL = 1, EPI_F32 = 2 };
+
+__device__ __forceinline__ int swz(int row, int kg) {
+    return (row & ~7) | ((row ^ (row >> 3) ^ kg) & 7);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_step(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (DT == DT_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 pack8(const uint32_t e[8]) {
+    return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                 e[6] | (e[7] << 16)};
+}
+
+// Transpose an 8x8 block of 16-bit elements: in[r] holds row r (8 elements),
+// out[c] receives column c (8 elements, row 0 in the low half of word 0).
+__device__ __forceinline__ void transpose8x8(const u32x4 *in, u32x4 *out) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t lo = in[2 * d][c >> 1], hi = in[2 * d + 1][c >> 1];
+            out[c][d] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                                : ((lo & 0xffffu) | (hi << 16));
+        }
+    }
+}
+
+// Staging of one operand tile of R rows x BK reduction values.
+//   RC = true : element (row, r) at p[row*ld + r]  (reduction-contiguous)
+//   RC = false: element (row, r) at p[r*ld + row]  (row-contiguous)
+template <int R, bool RC>
+struct Stage {
+    static constexpr int DIRECT = R * KG / NT;              // RC: 16-byte chunks per thread
+    static constexpr int UNITS = KG * (R / 8);              // !RC: 8x8 blocks per tile
+    static constexpr int UNITS_PER_THREAD = (UNITS + NT - 1) / NT;
+    static constexpr int NREG = RC ? DIRECT : UNITS_PER_THREAD * 8;
+    static_assert(!RC || (R * KG) % NT == 0, "tile rows must fill the workgroup");
+
+    u32x4 reg[NREG];
+
+    // All rows of the tile in range, the whole slice in range, 16-byte aligned
+    // rows: unconditional vector loads.
+    __device__ __forceinline__ void load_fast(const uint16_t *p, int64_t ld, int64_t row0,
+                                              int64_t rk, int t) {
+        if constexpr (RC) {
+#pragma unroll
+            for (int q = 0; q < DIRECT; ++q) {
+                const int c = t + NT * q;
+                const int row = c / KG, kg = c % KG;
+                reg[q] = *reinterpret_cast<const u32x4 *>(p + (row0 + row) * ld + rk + 8 * kg);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < UNITS_PER_THREAD; ++q) {
+                int u = t + NT * q;
+                if (UNITS % NT != 0 && u >= UNITS) u = UNITS - 1;  // duplicate, never stored
+                const int kg = u / (R / 8), ib = u % (R / 8);
+                const uint16_t *src = p + (rk + 8 * kg) * ld + row0 + 8 * ib;
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr)
+                    reg[q * 8 + rr] = *reinterpret_cast<const u32x4 *>(src + rr * ld);
+            }
+        }
+    }
+
+    // Masked variant: rows [row0, row_end), reduction [rk, r_end); elements
+    // outside are zero.  Addresses are clamped into range, so every load is
+    // valid and none depends on a branch.
+    __device__ __forceinline__ void load_masked(const uint16_t *p, int64_t ld, int64_t row0,
+                                                int64_t row_end, int64_t rk, int64_t r_end,
+                                                int t) {
+        if constexpr (RC) {
+#pragma unroll
+            for (int q = 0; q < DIRECT; ++q) {
+                const int c = t + NT * q;
+                const int row = c / KG, kg = c % KG;
+                const int64_t gi = row0 + row;
+                const int64_t gic = gi < row_end ? gi : row_end - 1;
+                uint32_t e[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const int64_t gr = rk + 8 * kg + x;
+                    const int64_t grc = gr < r_end ? gr : r_end - 1;
+                    const uint32_t v = p[gic * ld + grc];
+                    e[x] = (gi < row_end && gr < r_end) ? v : 0u;
+                }
+                reg[q] = pack8(e);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < UNITS_PER_THREAD; ++q) {
+                int u = t + NT * q;
+                if (UNITS % NT != 0 && u >= UNITS) u = UNITS - 1;
+                const int kg = u / (R / 8), ib = u % (R / 8);
+#pragma unroll
+                for (int rr = 0; rr < 8; ++rr) {
+                    const int64_t gr = rk + 8 * kg + rr;
+                    const int64_t grc = gr < r_end ? gr : r_end - 1;
+                    uint32_t e[8];
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        const int64_t gi = row0 + 8 * ib + x;
+                        const int64_t gic = gi < row_end ? gi : row_end - 1;
+                        const uint32_t v = p[grc * ld + gic];
+                        e[x] = (gi < row_end && gr < r_end) ? v : 0u;
+                    }
+                    reg[q * 8 + rr] = pack8(e);
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void load(const uint16_t *p, int64_t ld, int64_t row0,
+                                         int64_t row_end, int64_t rk, int64_t r_end,
+                                         bool interior, int t) {
+        if (interior && rk + BK <= r_end) load_fast(p, ld, row0, rk, t);
+        else load_masked(p, ld, row0, row_end, rk, r_end, t);
+    }
+
+    __device__ __forceinline__ void store(u32x4 *lds, int t) const {
+        if constexpr (RC) {
+#pragma unroll
+            for (int q = 0; q < DIRECT; ++q) {
+                const int c = t + NT * q;
+                const int row = c / KG, kg = c % KG;
+                lds[kg * R + swz(row, kg)] = reg[q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < UNITS_PER_THREAD; ++q) {
+                const int u = t + NT * q;
+                if (UNITS % NT != 0 && u >= UNITS) continue;
+                const int kg = u / (R / 8), ib = u % (R / 8);
+                u32x4 tr[8];
+                transpose8x8(&reg[q * 8], tr);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) lds[kg * R + swz(8 * ib + c, kg)] = tr[c];
+            }
+        }
+    }
+};
+
+// Fast loads for interior tiles and full slices: a uniform (scalar) base
+// pointer per slice plus one 32-bit byte offset per thread and load, fixed for
+// the whole reduction, so address arithmetic stays out of the main loop.
+template <int R, bool RC>
+struct FastAddr {
+    static constexpr int NOFF = RC ? Stage<R, RC>::DIRECT : Stage<R, RC>::UNITS_PER_THREAD;
+    uint32_t off[NOFF];
+
+    __device__ __forceinline__ void init(int64_t ld, int t) {
+#pragma unroll
+        for (int q = 0; q < NOFF; ++q) {
+            if constexpr (RC) {
+                const int c = t + NT * q;
+                off[q] = (uint32_t)(((c / KG) * ld + 8 * (c % KG)) * 2);
+            } else {
+                int u = t + NT * q;
+                if (Stage<R, RC>::UNITS % NT != 0 && u >= Stage<R, RC>::UNITS)
+                    u = Stage<R, RC>::UNITS - 1;
+                const int kg = u / (R / 8), ib = u % (R / 8);
+                off[q] = (uint32_t)(((int64_t)8 * kg * ld + 8 * ib) * 2);
+            }
+        }
+    }
+    // slice base: element (row0, rk) for RC, element (rk, row0) otherwise
+    __device__ __forceinline__ void load(Stage<R, RC> &st, const uint16_t *p, int64_t ld,
+                                         int64_t row0, int64_t rk) const {
+        if constexpr (RC) {
+            const char *base = reinterpret_cast<const char *>(p + row0 * ld + rk);
+#pragma unroll
+            for (int q = 0; q < NOFF; ++q)
+                st.reg[q] = *reinterpret_cast<const u32x4 *>(base + off[q]);
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const char *base = reinterpret_cast<const char *>(p + (rk + rr) * ld + row0);
+#pragma unroll
+                for (int q = 0; q < NOFF; ++q)
+                    st.reg[q * 8 + rr] = *reinterpret_cast<const u32x4 *>(base + off[q]);
+            }
+        }
+    }
+};
+
+// 32-bit offsets cover the whole tile of one slice
+template <int R, bool RC>
+__device__ __forceinline__ bool offsets_fit(int64_t ld) {
+    const int64_t span = RC ? ((int64_t)(R - 1) * ld + BK) * 2 : ((int64_t)(BK - 1) * ld + R) * 2;
+    return span < ((int64_t)1 << 31);
+}
+
+template <int DT, int BM, int BN, int WTM, int WTN, int FM, int FN>
+struct Compute {
+    // multiply one LDS slice into the accumulators: four 16-deep steps in
+    // ascending order; the fragments of step kk+1 are read while step kk's
+    // MFMAs run
+    __device__ __forceinline__ static void run(const u32x4 *la, const u32x4 *lb,
+                                               f32x16 (&acc)[FM][FN], int wm, int wn, int lrow,
+                                               int lkg) {
+        u32x4 fa[2][FM], fb[2][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[0][i] = la[lkg * BM + swz(wm * WTM + 32 * i + lrow, lkg)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[0][j] = lb[lkg * BN + swz(wn * WTN + 32 * j + lrow, lkg)];
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < BK / 16) {
+                const int kg = 2 * (kk + 1) + lkg;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    fa[cur ^ 1][i] = la[kg * BM + swz(wm * WTM + 32 * i + lrow, kg)];
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    fb[cur ^ 1][j] = lb[kg * BN + swz(wn * WTN + 32 * j + lrow, kg)];
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = mfma_step<DT>(fb[cur][j], fa[cur][i], acc[i][j]);
+        }
+    }
+};
+
+template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE>
+__global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
+    static_assert(WGM * WGN == 4, "four waves");
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
+    using Comp = Compute<DT, BM, BN, WTM, WTN, FM, FN>;
+
+    // stage buffers: A slices [2][KG*BM], then B slices [2][KG*BN] (16-byte
+    // slots); reused by the epilogue
+    __shared__ u32x4 lds_raw[2 * KG * (BM + BN)];
+    __shared__ float lds_bias[BN];
+    auto lds_a = [&](int b) { return lds_raw + b * (KG * BM); };
+    auto lds_b = [&](int b) { return lds_raw + 2 * KG * BM + b * (KG * BN); };
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+
+    // ---- which tile, which rows, which reduction range --------------------
+    int64_t row0, row_end, col0, r_begin, r_end, chunk = 0;
+    const uint16_t *pa = static_cast<const uint16_t *>(p.a);
+    const uint16_t *pb = static_cast<const uint16_t *>(p.b);
+    int64_t c_off = 0;
+    if constexpr (MODE == MODE_PLAIN) {
+        const int64_t tiles = p.tiles_i * p.tiles_j;
+        const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+        chunk = bid / tiles;
+        const int64_t tile = bid % tiles;
+        // groups of 4 row-tiles, column-major inside a group
+        constexpr int64_t GROUP = 4;
+        const int64_t per_group = GROUP * p.tiles_j;
+        const int64_t g = tile / per_group, first = g * GROUP;
+        const int64_t gsz = p.tiles_i - first < GROUP ? p.tiles_i - first : GROUP;
+        const int64_t in_g = tile % per_group;
+        row0 = (first + in_g % gsz) * BM;
+        col0 = (in_g / gsz) * BN;
+        row_end = p.rows;
+        r_begin = chunk * p.chunk;
+        r_end = r_begin + p.chunk < p.red ? r_begin + p.chunk : p.red;
+    } else if constexpr (MODE == MODE_SEGMENTS) {
+        const int64_t ti = blockIdx.x / p.tiles_j;
+        col0 = (blockIdx.x % p.tiles_j) * BN;
+        int64_t tt = ti;
+        int64_t x = 0;
+        row0 = -1;
+        row_end = 0;
+        for (; x <= p.n_experts; ++x) {
+            int64_t s = p.offsets[x < p.n_experts ? x : p.n_experts];
+            int64_t e = x < p.n_experts ? (int64_t)p.offsets[x + 1] : p.rows;
+            if (e > p.rows) e = p.rows;
+            if (s > e) s = e;
+            const int64_t cnt = (e - s + BM - 1) / BM;
+            if (tt < cnt) {
+                row0 = s + tt * BM;
+                row_end = e;
+                break;
+            }
+            tt -= cnt;
+        }
+        if (row0 < 0) return;  // beyond the last segment tile (whole workgroup)
+        if (x == p.n_experts) {
+            // padding rows: exact +0 (rublas: ids outside [0,E) give zero rows)
+            const int64_t r1 = row0 + BM < row_end ? row0 + BM : row_end;
+            uint16_t *pc = static_cast<uint16_t *>(p.c);
+            for (int64_t idx = t; idx < (r1 - row0) * BN; idx += NT) {
+                const int64_t i = row0 + idx / BN, j = col0 + idx % BN;
+                if (j < p.cols) pc[i * p.ldc + j] = 0;
+            }
+            return;
+        }
+        pb += x * p.b_expert_stride;
+        r_begin = 0;
+        r_end = p.red;
+    } else {  // MODE_EXPERT_RED
+        const int64_t per_x = p.tiles_i * p.tiles_j;
+        const int64_t x = blockIdx.x / per_x;
+        const int64_t tile = blockIdx.x % per_x;
+        row0 = (tile / p.tiles_j) * BM;
+        col0 = (tile % p.tiles_j) * BN;
+        row_end = p.rows;
+        r_end = p.red_offsets[x + 1];
+        r_begin = p.red_offsets[x];
+        if (r_end > p.red) r_end = p.red;
+        if (r_begin > r_end) r_begin = r_end;
+        c_off = x * p.c_expert_stride;
+    }
+
+    // bias of this tile's columns, widened once (read after the main loop's
+    // barriers)
+    if constexpr (EPI == EPI_ROUND) {
+        if (p.bias && t < BN) {
+            const int64_t j = col0 + t < p.cols ? col0 + t : p.cols - 1;
+            const uint16_t b = static_cast<const uint16_t *>(p.bias)[j];
+            lds_bias[t] = DT == DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+        }
+    }
+
+    Stage<BM, A_RC> sa;
+    Stage<BN, B_RC> sb;
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    // interior: every row of the operand tile exists and rows are 16-byte
+    // aligned (the same value on every thread of the workgroup)
+    const bool int_a = p.vec_a != 0 && row0 + BM <= row_end;
+    const bool int_b = p.vec_b != 0 && col0 + BN <= p.cols;
+    const int lrow = lane & 31, lkg = lane >> 5;
+    const int64_t nst = (r_end - r_begin + BK - 1) / BK;
+    const int64_t nfull = (r_end - r_begin) / BK;
+
+    int64_t s = 0;
+    if (int_a && int_b && offsets_fit<BM, A_RC>(p.lda) && offsets_fit<BN, B_RC>(p.ldb)) {
+        // ---- lean main loop over full slices ----------------------------------
+        FastAddr<BM, A_RC> fa_addr;
+        FastAddr<BN, B_RC> fb_addr;
+        fa_addr.init(p.lda, t);
+        fb_addr.init(p.ldb, t);
+        if (nfull >= 2) {
+            fa_addr.load(sa, pa, p.lda, row0, r_begin);
+            fb_addr.load(sb, pb, p.ldb, col0, r_begin);
+            sa.store(lds_a(0), t);
+            sb.store(lds_b(0), t);
+            fa_addr.load(sa, pa, p.lda, row0, r_begin + BK);
+            fb_addr.load(sb, pb, p.ldb, col0, r_begin + BK);
+            __syncthreads();
+            // slices s+1 in registers, s in LDS buffer s&1; loads run 2 ahead
+            for (; s + 2 < nfull; ++s) {
+                const int cur = (int)(s & 1);
+                sa.store(lds_a(cur ^ 1), t);
+                sb.store(lds_b(cur ^ 1), t);
+                const int64_t rk = r_begin + (s + 2) * BK;
+                fa_addr.load(sa, pa, p.lda, row0, rk);
+                fb_addr.load(sb, pb, p.ldb, col0, rk);
+                Comp::run(lds_a(cur), lds_b(cur), acc, wm, wn, lrow, lkg);
+                __syncthreads();
+            }
+            // here s + 2 == nfull: slice s in LDS, slice s+1 in registers
+        } else {
+            s = -1;  // nothing staged yet
+        }
+    } else {
+        s = -1;
+    }
+
+    // ---- generic loop (edge tiles, partial slices, pipeline drain) -----------
+    // invariant at loop entry: slice s is in LDS buffer s&1 (s >= 0) and slice
+    // s+1 is in registers (if it exists); s = -1 means nothing is staged.
+    if (s < 0 && nst > 0) {
+        sa.load(pa, p.lda, row0, row_end, r_begin, r_end, int_a, t);
+        sb.load(pb, p.ldb, col0, p.cols, r_begin, r_end, int_b, t);
+        sa.store(lds_a(0), t);
+        sb.store(lds_b(0), t);
+        if (nst > 1) {
+            sa.load(pa, p.lda, row0, row_end, r_begin + BK, r_end, int_a, t);
+            sb.load(pb, p.ldb, col0, p.cols, r_begin + BK, r_end, int_b, t);
+        }
+        __syncthreads();
+        s = 0;
+    }
+    for (; s >= 0 && s < nst; ++s) {
+        const int cur = (int)(s & 1);
+        if (s + 1 < nst) {
+            sa.store(lds_a(cur ^ 1), t);
+            sb.store(lds_b(cur ^ 1), t);
+            if (s + 2 < nst) {
+                const int64_t rk = r_begin + (s + 2) * BK;
+                sa.load(pa, p.lda, row0, row_end, rk, r_end, int_a, t);
+                sb.load(pb, p.ldb, col0, p.cols, rk, r_end, int_b, t);
+            }
+        }
+        Comp::run(lds_a(cur), lds_b(cur), acc, wm, wn, lrow, lkg);
+        __syncthreads();
+    }
+
+    // ---- epilogue ---------------------------------------------------------
+    // For block (i, j) a lane holds row (lane & 31) and, for accumulator
+    // elements 4g..4g+3, the 4 consecutive columns 8g + 4*(lane/32) + 0..3.
+    // Each wave converts one 32-row slab of its tile at a time into a private
+    // LDS area (row-major), then writes it out as whole contiguous row segments,
+    // 16 bytes per lane.  The stage buffers are free: the main loop ended with a
+    // barrier.
+    using OutT = typename std::conditional<EPI == EPI_ROUND, uint16_t, float>::type;
+    constexpr int OSZ = (int)sizeof(OutT);
+    constexpr int ROWB = WTN * OSZ;           // bytes of one slab row
+    constexpr int ROWP = ROWB + 16;           // padded LDS row pitch (spreads banks)
+    constexpr int CPR = ROWB / 16;            // 16-byte chunks per slab row
+    static_assert(ROWB % 16 == 0, "slab rows are whole 16-byte chunks");
+    static_assert(4 * 32 * ROWP <= 2 * KG * (BM + BN) * 16, "slabs fit in the stage buffers");
+    char *slab = reinterpret_cast<char *>(lds_raw) + wave * 32 * ROWP;
+    const float *bias_l = lds_bias;
+    const bool vec_c = p.vec_c != 0;
+    __syncthreads();  // bias visible; every wave done with the stage buffers
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int cl = 32 * j + 8 * g + 4 * lkg;  // column inside the wave tile
+                float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                              acc[i][j][4 * g + 3]};
+                char *dst = slab + lrow * ROWP + cl * OSZ;
+                if constexpr (EPI == EPI_ROUND) {
+                    if (p.bias) {
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) v[x] = v[x] + bias_l[wn * WTN + cl + x];
+                    }
+                    uint32_t h[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        h[x] = DT == DT_BF16 ? f32_to_bf16_bits(v[x]) : f32_to_f16_bits(v[x]);
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                } else {
+                    *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+                }
+            }
+        }
+        __syncthreads();
+        // write the slab: rows gi0 + 0..31, columns gj0 + 0..WTN-1
+        const int64_t gi0 = row0 + wm * WTM + 32 * i;
+        const int64_t gj0 = col0 + wn * WTN;
+        OutT *base = EPI == EPI_PARTIAL
+                         ? reinterpret_cast<OutT *>(p.ws + chunk * p.rows * p.cols)
+                         : reinterpret_cast<OutT *>(static_cast<char *>(p.c) + c_off * OSZ);
+        const int64_t ld = EPI == EPI_PARTIAL ? p.cols : p.ldc;
+#pragma unroll
+        for (int q = 0; q < (32 * CPR + 63) / 64; ++q) {
+            const int idx = lane + 64 * q;
+            if (idx < 32 * CPR) {
+                const int r = idx / CPR, c = idx % CPR;
+                const int64_t gi = gi0 + r;
+                const int64_t gj = gj0 + c * (16 / OSZ);
+                const u32x4 val = *reinterpret_cast<const u32x4 *>(slab + r * ROWP + c * 16);
+                if (gi < row_end) {
+                    OutT *dst = base + gi * ld + gj;
+                    if (vec_c && gj + 16 / OSZ <= p.cols) {
+                        *reinterpret_cast<u32x4 *>(dst) = val;
+                    } else {
+                        const OutT *e = reinterpret_cast<const OutT *>(&val);
+#pragma unroll
+                        for (int x = 0; x < 16 / OSZ; ++x)
+                            if (gj + x < p.cols) dst[x] = e[x];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace mfma
+
+}  // namespace bi
+
+namespace bi {
+namespace mfma {
+
+// Tile shapes (id -> BM x BN, wave layout).  All issue the same MFMA sequence
+// per output element; they differ only in how work is spread over the chip.
+template <int ID> struct TileOf;
+template <> struct TileOf<1> { static constexpr int BM = 256, BN = 256, WGM = 2, WGN = 2; };
+template <> struct TileOf<2> { static constexpr int BM = 256, BN = 192, WGM = 2, WGN = 2; };
+template <> struct TileOf<3> { static constexpr int BM = 256, BN = 128, WGM = 2, WGN = 2; };
+template <> struct TileOf<4> { static constexpr int BM = 128, BN = 128, WGM = 2, WGN = 2; };
+template <> struct TileOf<5> { static constexpr int BM = 128, BN = 96, WGM = 4, WGN = 1; };
+template <> struct TileOf<6> { static constexpr int BM = 64, BN = 64, WGM = 2, WGN = 2; };
+template <> struct TileOf<7> { static constexpr int BM = 128, BN = 256, WGM = 2, WGN = 2; };
+template <> struct TileOf<9> { static constexpr int BM = 128, BN = 192, WGM = 2, WGN = 2; };
+template <> struct TileOf<10> { static constexpr int BM = 256, BN = 96, WGM = 4, WGN = 1; };
+
+template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>
+hipError_t launch_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
+    using T = TileOf<ID>;
+    hipLaunchKernelGGL((mfma_gemm_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE>),
+                       dim3(grid), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+// dispatch over a compile-time list of tile ids
+template <int DT, bool ARC, bool BRC, int EPI, int MODE, int... IDS>
+hipError_t launch_among(const MfmaArgs &p, int tile_id, int64_t grid, hipStream_t s) {
+    hipError_t r = hipErrorInvalidValue;
+    ((tile_id == IDS ? (void)(r = launch_tile<DT, ARC, BRC, EPI, MODE, IDS>(p, grid, s)) : (void)0),
+     ...);
+    return r;
+}
+
+}  // namespace mfma
+}  // namespace bi
