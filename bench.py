@@ -38,12 +38,40 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="linear", choices=["linear", "fp8", "grouped", "sweep"])
+    ap.add_argument("--workload", default="linear",
+                    choices=["linear", "fp8", "grouped", "sweep", "copy"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; a committed counter record is valid only for it."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "deterministic_invariant_gemm_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(record: str, op: str):
+    """HBM bytes per launch of `op` from the committed rocprofv3 counter record
+    (FETCH_SIZE and WRITE_SIZE, calibrated against a copy of known size), or
+    None if the record is missing or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", record)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash() or op not in rec.get("kernels", {}):
+        return None
+    return int(rec["kernels"][op]["traffic_bytes"])
 
 
 def host_threads() -> int:
@@ -116,11 +144,16 @@ def cpu_baseline_linear(d, target_s):
     r = 16
     dt_s = run(r)
     r = int(min(d["m"], max(16, r * target_s / max(dt_s, 1e-3))))
-    dt_s = run(r)
-    flops = 3 * 2.0 * r * k * n
+    # the whole batch is cheaper than the target: repeat it
+    reps = 1 if r < d["m"] else max(1, int(target_s / max(dt_s * r / 16, 1e-3)))
+    t = time.perf_counter()
+    for _ in range(reps):
+        run(r)
+    dt_s = time.perf_counter() - t
+    flops = reps * 3 * 2.0 * r * k * n
     return {"value": flops / dt_s / 1e12, "unit": "TFLOP/s", "cores": thr, "kind": "oracle",
-            "sample": f"forward+dX+dW on the first {r} of {d['m']} rows "
-                      f"(K={k}, N={n}), {dt_s:.1f} s, f64 accumulation, {cpu_model()}"}
+            "sample": f"forward+dX+dW on the first {r} of {d['m']} rows (K={k}, N={n}), "
+                      f"{reps} pass(es), {dt_s:.1f} s, f64 accumulation, {cpu_model()}"}
 
 
 def bench_linear(args, torch, dig, synth):
@@ -162,7 +195,8 @@ def bench_linear(args, torch, dig, synth):
                    "M": m, "K": k, "N": n, "bias": True},
         "roofline": {"bound": "mfma", "kernel": dominant,
                      "achieved": round(achieved, 2), "peak": BF16_PEAK, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_PEAK, 4), "traffic": None,
+                     "frac": round(achieved / BF16_PEAK, 4),
+                     "traffic": recorded_traffic("linear_768x3072_m4096_traffic.json", dominant),
                      "algorithmic_bytes": bytes_[dominant]},
         "ops": {name: {"us": round(v * 1e3, 2),
                        "tflops": round(flop / (v * 1e-3) / 1e12, 2),
@@ -270,6 +304,27 @@ def bench_sweep(args, torch, dig, synth):
             "sweep": res}
 
 
+def bench_copy(args, torch, dig, synth):
+    """Plain device-to-device copy of a 512 MiB buffer: the known-size kernel
+    used to calibrate the FETCH_SIZE / WRITE_SIZE counters, and a measured HBM
+    bandwidth reference."""
+    n = 256 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    s = torch.cuda.current_stream()
+    ms, per = timed_steps(torch, s, [("copy", lambda: dst.copy_(src))], args.steps, args.warmup)
+    nbytes = 2 * 2 * n
+    gbps = nbytes / (per["copy"] * 1e-3) / 1e9
+    return {"metric": "device copy GB/s (read + write)", "value": round(gbps, 1), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+            "data": "synthetic", "config": {"workload": "copy of 512 MiB (read 512 MiB, write 512 MiB)",
+                                            "bytes_read": 2 * n, "bytes_written": 2 * n},
+            "roofline": {"bound": "hbm", "kernel": "copy", "achieved": round(gbps, 1),
+                         "peak": HBM_PEAK, "unit": "GB/s", "frac": round(gbps / HBM_PEAK, 4),
+                         "traffic": None}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -284,7 +339,7 @@ def main():
     import synth
     dig.load()
     fn = {"linear": bench_linear, "fp8": bench_fp8, "grouped": bench_grouped,
-          "sweep": bench_sweep}[args.workload]
+          "sweep": bench_sweep, "copy": bench_copy}[args.workload]
     out = fn(args, torch, dig, synth)
     print(json.dumps(out), flush=True)
 

@@ -63,6 +63,7 @@ int pick_tile(int op, int64_t k, int64_t n) {
         if (cols >= 2048) return 1;                                           // 256x256
         return cols >= 128 ? 4 : 6;
     case OP_DX:
+        if (cols % 96 == 0 && cols <= 1536) return 5;  // 128x96
         return cols >= 128 ? 4 : 6;
     case OP_DW:
         return (k >= 128 && n >= 128) ? 4 : 6;
