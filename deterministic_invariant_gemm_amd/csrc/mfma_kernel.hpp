@@ -253,17 +253,22 @@ __device__ __forceinline__ bool offsets_fit(int64_t ld) {
 
 template <int DT, int BM, int BN, int WTM, int WTN, int FM, int FN>
 struct Compute {
-    // multiply one LDS slice into the accumulators: four 16-deep steps in
-    // ascending order; the fragments of step kk+1 are read while step kk's
-    // MFMAs run
-    __device__ __forceinline__ static void run(const u32x4 *la, const u32x4 *lb,
-                                               f32x16 (&acc)[FM][FN], int wm, int wn, int lrow,
-                                               int lkg) {
-        u32x4 fa[2][FM], fb[2][FN];
+    u32x4 fa[2][FM], fb[2][FN];
+
+    // fragments of the first 16-deep step of a slice
+    __device__ __forceinline__ void first(const u32x4 *la, const u32x4 *lb, int wm, int wn,
+                                          int lrow, int lkg) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[0][i] = la[lkg * BM + swz(wm * WTM + 32 * i + lrow, lkg)];
 #pragma unroll
         for (int j = 0; j < FN; ++j) fb[0][j] = lb[lkg * BN + swz(wn * WTN + 32 * j + lrow, lkg)];
+    }
+
+    // multiply one LDS slice into the accumulators (first() already issued):
+    // four 16-deep steps in ascending order; the fragments of step kk+1 are
+    // read while step kk's MFMAs run
+    __device__ __forceinline__ void rest(const u32x4 *la, const u32x4 *lb, f32x16 (&acc)[FM][FN],
+                                         int wm, int wn, int lrow, int lkg) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const int cur = kk & 1;
@@ -283,6 +288,12 @@ struct Compute {
                     acc[i][j] = mfma_step<DT>(fb[cur][j], fa[cur][i], acc[i][j]);
         }
     }
+
+    __device__ __forceinline__ void run(const u32x4 *la, const u32x4 *lb, f32x16 (&acc)[FM][FN],
+                                        int wm, int wn, int lrow, int lkg) {
+        first(la, lb, wm, wn, lrow, lkg);
+        rest(la, lb, acc, wm, wn, lrow, lkg);
+    }
 };
 
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE>
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
     // stage buffers: A slices [2][KG*BM], then B slices [2][KG*BN] (16-byte
     // slots); reused by the epilogue
     __shared__ u32x4 lds_raw[2 * KG * (BM + BN)];
-    __shared__ float lds_bias[BN];
+    __shared__ __align__(16) float lds_bias[BN];
     auto lds_a = [&](int b) { return lds_raw + b * (KG * BM); };
     auto lds_b = [&](int b) { return lds_raw + 2 * KG * BM + b * (KG * BN); };
 
@@ -385,6 +396,7 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
 
     Stage<BM, A_RC> sa;
     Stage<BN, B_RC> sb;
+    Comp comp;
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -417,12 +429,17 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
             // slices s+1 in registers, s in LDS buffer s&1; loads run 2 ahead
             for (; s + 2 < nfull; ++s) {
                 const int cur = (int)(s & 1);
+                // order pinned for the scheduler: first fragments of slice s,
+                // LDS writes of slice s+1, global loads of slice s+2, then the
+                // MFMAs of slice s (the loads stay in flight for a whole slice)
+                comp.first(lds_a(cur), lds_b(cur), wm, wn, lrow, lkg);
                 sa.store(lds_a(cur ^ 1), t);
                 sb.store(lds_b(cur ^ 1), t);
                 const int64_t rk = r_begin + (s + 2) * BK;
                 fa_addr.load(sa, pa, p.lda, row0, rk);
                 fb_addr.load(sb, pb, p.ldb, col0, rk);
-                Comp::run(lds_a(cur), lds_b(cur), acc, wm, wn, lrow, lkg);
+                __builtin_amdgcn_sched_barrier(0);
+                comp.rest(lds_a(cur), lds_b(cur), acc, wm, wn, lrow, lkg);
                 __syncthreads();
             }
             // here s + 2 == nfull: slice s in LDS, slice s+1 in registers
@@ -459,7 +476,7 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
                 sb.load(pb, p.ldb, col0, p.cols, rk, r_end, int_b, t);
             }
         }
-        Comp::run(lds_a(cur), lds_b(cur), acc, wm, wn, lrow, lkg);
+        comp.run(lds_a(cur), lds_b(cur), acc, wm, wn, lrow, lkg);
         __syncthreads();
     }
 
@@ -481,6 +498,16 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
     const float *bias_l = lds_bias;
     const bool vec_c = p.vec_c != 0;
     __syncthreads();  // bias visible; every wave done with the stage buffers
+    // this lane's bias columns, read from LDS once for all row slabs
+    f32x4 bias_r[FN][4];
+    if constexpr (EPI == EPI_ROUND) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                bias_r[j][g] = *reinterpret_cast<const f32x4 *>(
+                    bias_l + wn * WTN + 32 * j + 8 * g + 4 * lkg);
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -494,7 +521,7 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
                 if constexpr (EPI == EPI_ROUND) {
                     if (p.bias) {
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) v[x] = v[x] + bias_l[wn * WTN + cl + x];
+                        for (int x = 0; x < 4; ++x) v[x] = v[x] + bias_r[j][g][x];
                     }
                     uint32_t h[4];
 #pragma unroll
@@ -506,7 +533,10 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
                 }
             }
         }
-        __syncthreads();
+        // The slab is private to this wave and a wave's LDS operations execute
+        // in program order, so the reads below see the writes above and the
+        // next slab's writes cannot overtake these reads: no workgroup barrier
+        // (which would also wait for every outstanding global store).
         // write the slab: rows gi0 + 0..31, columns gj0 + 0..WTN-1
         const int64_t gi0 = row0 + wm * WTM + 32 * i;
         const int64_t gj0 = col0 + wn * WTN;
@@ -535,7 +565,6 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
                 }
             }
         }
-        __syncthreads();
     }
 }
 
