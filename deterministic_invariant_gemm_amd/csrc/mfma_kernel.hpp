@@ -296,6 +296,201 @@ struct Compute {
     }
 };
 
+// Position of one workgroup's tile: output rows [row0, row_end), columns from
+// col0, reduction range [r_begin, r_end), dW chunk index, offset of the output
+// (grouped dweights) and of B (grouped expert).  `skip` = nothing to multiply
+// (beyond the last segment tile, or a padding tile that was zero-filled here).
+struct TileInfo {
+    int64_t row0, row_end, col0, r_begin, r_end, chunk, c_off, b_off;
+    bool skip;
+};
+
+template <int MODE, int BM, int BN>
+__device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
+    TileInfo ti{};
+    ti.skip = false;
+    if constexpr (MODE == MODE_PLAIN) {
+        const int64_t tiles = p.tiles_i * p.tiles_j;
+        const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+        ti.chunk = bid / tiles;
+        const int64_t tile = bid % tiles;
+        // groups of 4 row-tiles, column-major inside a group
+        constexpr int64_t GROUP = 4;
+        const int64_t per_group = GROUP * p.tiles_j;
+        const int64_t g = tile / per_group, first = g * GROUP;
+        const int64_t gsz = p.tiles_i - first < GROUP ? p.tiles_i - first : GROUP;
+        const int64_t in_g = tile % per_group;
+        ti.row0 = (first + in_g % gsz) * BM;
+        ti.col0 = (in_g / gsz) * BN;
+        ti.row_end = p.rows;
+        ti.r_begin = ti.chunk * p.chunk;
+        ti.r_end = ti.r_begin + p.chunk < p.red ? ti.r_begin + p.chunk : p.red;
+    } else if constexpr (MODE == MODE_SEGMENTS) {
+        const int64_t tt0 = blockIdx.x / p.tiles_j;
+        ti.col0 = (blockIdx.x % p.tiles_j) * BN;
+        int64_t tt = tt0;
+        int64_t x = 0;
+        ti.row0 = -1;
+        ti.row_end = 0;
+        for (; x <= p.n_experts; ++x) {
+            int64_t s = p.offsets[x < p.n_experts ? x : p.n_experts];
+            int64_t e = x < p.n_experts ? (int64_t)p.offsets[x + 1] : p.rows;
+            if (e > p.rows) e = p.rows;
+            if (s > e) s = e;
+            const int64_t cnt = (e - s + BM - 1) / BM;
+            if (tt < cnt) {
+                ti.row0 = s + tt * BM;
+                ti.row_end = e;
+                break;
+            }
+            tt -= cnt;
+        }
+        if (ti.row0 < 0) {  // beyond the last segment tile (whole workgroup)
+            ti.skip = true;
+            return ti;
+        }
+        if (x == p.n_experts) {
+            // padding rows: exact +0 (rublas: ids outside [0,E) give zero rows)
+            const int64_t r1 = ti.row0 + BM < ti.row_end ? ti.row0 + BM : ti.row_end;
+            uint16_t *pc = static_cast<uint16_t *>(p.c);
+            for (int64_t idx = t; idx < (r1 - ti.row0) * BN; idx += NT) {
+                const int64_t i = ti.row0 + idx / BN, j = ti.col0 + idx % BN;
+                if (j < p.cols) pc[i * p.ldc + j] = 0;
+            }
+            ti.skip = true;
+            return ti;
+        }
+        ti.b_off = x * p.b_expert_stride;
+        ti.r_begin = 0;
+        ti.r_end = p.red;
+    } else {  // MODE_EXPERT_RED
+        const int64_t per_x = p.tiles_i * p.tiles_j;
+        const int64_t x = blockIdx.x / per_x;
+        const int64_t tile = blockIdx.x % per_x;
+        ti.row0 = (tile / p.tiles_j) * BM;
+        ti.col0 = (tile % p.tiles_j) * BN;
+        ti.row_end = p.rows;
+        ti.r_end = p.red_offsets[x + 1];
+        ti.r_begin = p.red_offsets[x];
+        if (ti.r_end > p.red) ti.r_end = p.red;
+        if (ti.r_begin > ti.r_end) ti.r_begin = ti.r_end;
+        ti.c_off = x * p.c_expert_stride;
+    }
+    return ti;
+}
+
+// Stage the bias of this tile's columns into LDS as f32 (read after a barrier).
+template <int DT, int EPI, int BN>
+__device__ __forceinline__ void stage_bias(const MfmaArgs &p, int64_t col0, float *lds_bias,
+                                           int t) {
+    if constexpr (EPI == EPI_ROUND) {
+        if (p.bias && t < BN) {
+            const int64_t j = col0 + t < p.cols ? col0 + t : p.cols - 1;
+            const uint16_t b = static_cast<const uint16_t *>(p.bias)[j];
+            lds_bias[t] = DT == DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+        }
+    }
+}
+
+// LDS bytes the epilogue needs (four waves, one 32-row slab each)
+template <int EPI, int WTN>
+constexpr int slab_bytes() {
+    return 4 * 32 * (WTN * (EPI == EPI_ROUND ? 2 : 4) + 16);
+}
+
+// Epilogue.  For block (i, j) a lane holds row (lane & 31) and, for
+// accumulator elements 4g..4g+3, the 4 consecutive columns 8g + 4*(lane/32) +
+// 0..3.  Each wave converts one 32-row slab of its tile at a time into a
+// private LDS area (row-major), then writes it out as whole contiguous row
+// segments, 16 bytes per lane.  Starts with a workgroup barrier, after which
+// the stage buffers (`lds`) are free.
+template <int DT, int EPI, int WTM, int WTN, int FM, int FN>
+__device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti,
+                                           f32x16 (&acc)[FM][FN], char *lds,
+                                           const float *bias_l, int wave, int wm, int wn,
+                                           int lane) {
+    const int lrow = lane & 31, lkg = lane >> 5;
+    const int64_t row0 = ti.row0, row_end = ti.row_end, col0 = ti.col0;
+    const int64_t chunk = ti.chunk, c_off = ti.c_off;
+    using OutT = typename std::conditional<EPI == EPI_ROUND, uint16_t, float>::type;
+    constexpr int OSZ = (int)sizeof(OutT);
+    constexpr int ROWB = WTN * OSZ;           // bytes of one slab row
+    constexpr int ROWP = ROWB + 16;           // padded LDS row pitch (spreads banks)
+    constexpr int CPR = ROWB / 16;            // 16-byte chunks per slab row
+    static_assert(ROWB % 16 == 0, "slab rows are whole 16-byte chunks");
+    char *slab = lds + wave * 32 * ROWP;
+    const bool vec_c = p.vec_c != 0;
+    __syncthreads();  // bias visible; every wave done with the stage buffers
+    // this lane's bias columns, read from LDS once for all row slabs
+    f32x4 bias_r[FN][4];
+    if constexpr (EPI == EPI_ROUND) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                bias_r[j][g] = *reinterpret_cast<const f32x4 *>(
+                    bias_l + wn * WTN + 32 * j + 8 * g + 4 * lkg);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int cl = 32 * j + 8 * g + 4 * lkg;  // column inside the wave tile
+                float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                              acc[i][j][4 * g + 3]};
+                char *dst = slab + lrow * ROWP + cl * OSZ;
+                if constexpr (EPI == EPI_ROUND) {
+                    if (p.bias) {
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) v[x] = v[x] + bias_r[j][g][x];
+                    }
+                    uint32_t h[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        h[x] = DT == DT_BF16 ? f32_to_bf16_bits(v[x]) : f32_to_f16_bits(v[x]);
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                } else {
+                    *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+                }
+            }
+        }
+        // The slab is private to this wave and a wave's LDS operations execute
+        // in program order, so the reads below see the writes above and the
+        // next slab's writes cannot overtake these reads: no workgroup barrier
+        // (which would also wait for every outstanding global store).
+        // write the slab: rows gi0 + 0..31, columns gj0 + 0..WTN-1
+        const int64_t gi0 = row0 + wm * WTM + 32 * i;
+        const int64_t gj0 = col0 + wn * WTN;
+        OutT *base = EPI == EPI_PARTIAL
+                         ? reinterpret_cast<OutT *>(p.ws + chunk * p.rows * p.cols)
+                         : reinterpret_cast<OutT *>(static_cast<char *>(p.c) + c_off * OSZ);
+        const int64_t ld = EPI == EPI_PARTIAL ? p.cols : p.ldc;
+#pragma unroll
+        for (int q = 0; q < (32 * CPR + 63) / 64; ++q) {
+            const int idx = lane + 64 * q;
+            if (idx < 32 * CPR) {
+                const int r = idx / CPR, c = idx % CPR;
+                const int64_t gi = gi0 + r;
+                const int64_t gj = gj0 + c * (16 / OSZ);
+                const u32x4 val = *reinterpret_cast<const u32x4 *>(slab + r * ROWP + c * 16);
+                if (gi < row_end) {
+                    OutT *dst = base + gi * ld + gj;
+                    if (vec_c && gj + 16 / OSZ <= p.cols) {
+                        *reinterpret_cast<u32x4 *>(dst) = val;
+                    } else {
+                        const OutT *e = reinterpret_cast<const OutT *>(&val);
+#pragma unroll
+                        for (int x = 0; x < 16 / OSZ; ++x)
+                            if (gj + x < p.cols) dst[x] = e[x];
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE>
 __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
     static_assert(WGM * WGN == 4, "four waves");
@@ -315,84 +510,14 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    // ---- which tile, which rows, which reduction range --------------------
-    int64_t row0, row_end, col0, r_begin, r_end, chunk = 0;
+    const TileInfo ti = decode_tile<MODE, BM, BN>(p, t);
+    if (ti.skip) return;
+    const int64_t row0 = ti.row0, row_end = ti.row_end, col0 = ti.col0;
+    const int64_t r_begin = ti.r_begin, r_end = ti.r_end;
     const uint16_t *pa = static_cast<const uint16_t *>(p.a);
-    const uint16_t *pb = static_cast<const uint16_t *>(p.b);
-    int64_t c_off = 0;
-    if constexpr (MODE == MODE_PLAIN) {
-        const int64_t tiles = p.tiles_i * p.tiles_j;
-        const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-        chunk = bid / tiles;
-        const int64_t tile = bid % tiles;
-        // groups of 4 row-tiles, column-major inside a group
-        constexpr int64_t GROUP = 4;
-        const int64_t per_group = GROUP * p.tiles_j;
-        const int64_t g = tile / per_group, first = g * GROUP;
-        const int64_t gsz = p.tiles_i - first < GROUP ? p.tiles_i - first : GROUP;
-        const int64_t in_g = tile % per_group;
-        row0 = (first + in_g % gsz) * BM;
-        col0 = (in_g / gsz) * BN;
-        row_end = p.rows;
-        r_begin = chunk * p.chunk;
-        r_end = r_begin + p.chunk < p.red ? r_begin + p.chunk : p.red;
-    } else if constexpr (MODE == MODE_SEGMENTS) {
-        const int64_t ti = blockIdx.x / p.tiles_j;
-        col0 = (blockIdx.x % p.tiles_j) * BN;
-        int64_t tt = ti;
-        int64_t x = 0;
-        row0 = -1;
-        row_end = 0;
-        for (; x <= p.n_experts; ++x) {
-            int64_t s = p.offsets[x < p.n_experts ? x : p.n_experts];
-            int64_t e = x < p.n_experts ? (int64_t)p.offsets[x + 1] : p.rows;
-            if (e > p.rows) e = p.rows;
-            if (s > e) s = e;
-            const int64_t cnt = (e - s + BM - 1) / BM;
-            if (tt < cnt) {
-                row0 = s + tt * BM;
-                row_end = e;
-                break;
-            }
-            tt -= cnt;
-        }
-        if (row0 < 0) return;  // beyond the last segment tile (whole workgroup)
-        if (x == p.n_experts) {
-            // padding rows: exact +0 (rublas: ids outside [0,E) give zero rows)
-            const int64_t r1 = row0 + BM < row_end ? row0 + BM : row_end;
-            uint16_t *pc = static_cast<uint16_t *>(p.c);
-            for (int64_t idx = t; idx < (r1 - row0) * BN; idx += NT) {
-                const int64_t i = row0 + idx / BN, j = col0 + idx % BN;
-                if (j < p.cols) pc[i * p.ldc + j] = 0;
-            }
-            return;
-        }
-        pb += x * p.b_expert_stride;
-        r_begin = 0;
-        r_end = p.red;
-    } else {  // MODE_EXPERT_RED
-        const int64_t per_x = p.tiles_i * p.tiles_j;
-        const int64_t x = blockIdx.x / per_x;
-        const int64_t tile = blockIdx.x % per_x;
-        row0 = (tile / p.tiles_j) * BM;
-        col0 = (tile % p.tiles_j) * BN;
-        row_end = p.rows;
-        r_end = p.red_offsets[x + 1];
-        r_begin = p.red_offsets[x];
-        if (r_end > p.red) r_end = p.red;
-        if (r_begin > r_end) r_begin = r_end;
-        c_off = x * p.c_expert_stride;
-    }
+    const uint16_t *pb = static_cast<const uint16_t *>(p.b) + ti.b_off;
 
-    // bias of this tile's columns, widened once (read after the main loop's
-    // barriers)
-    if constexpr (EPI == EPI_ROUND) {
-        if (p.bias && t < BN) {
-            const int64_t j = col0 + t < p.cols ? col0 + t : p.cols - 1;
-            const uint16_t b = static_cast<const uint16_t *>(p.bias)[j];
-            lds_bias[t] = DT == DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
-        }
-    }
+    stage_bias<DT, EPI, BN>(p, col0, lds_bias, t);
 
     Stage<BM, A_RC> sa;
     Stage<BN, B_RC> sb;
@@ -480,92 +605,9 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
         __syncthreads();
     }
 
-    // ---- epilogue ---------------------------------------------------------
-    // For block (i, j) a lane holds row (lane & 31) and, for accumulator
-    // elements 4g..4g+3, the 4 consecutive columns 8g + 4*(lane/32) + 0..3.
-    // Each wave converts one 32-row slab of its tile at a time into a private
-    // LDS area (row-major), then writes it out as whole contiguous row segments,
-    // 16 bytes per lane.  The stage buffers are free: the main loop ended with a
-    // barrier.
-    using OutT = typename std::conditional<EPI == EPI_ROUND, uint16_t, float>::type;
-    constexpr int OSZ = (int)sizeof(OutT);
-    constexpr int ROWB = WTN * OSZ;           // bytes of one slab row
-    constexpr int ROWP = ROWB + 16;           // padded LDS row pitch (spreads banks)
-    constexpr int CPR = ROWB / 16;            // 16-byte chunks per slab row
-    static_assert(ROWB % 16 == 0, "slab rows are whole 16-byte chunks");
-    static_assert(4 * 32 * ROWP <= 2 * KG * (BM + BN) * 16, "slabs fit in the stage buffers");
-    char *slab = reinterpret_cast<char *>(lds_raw) + wave * 32 * ROWP;
-    const float *bias_l = lds_bias;
-    const bool vec_c = p.vec_c != 0;
-    __syncthreads();  // bias visible; every wave done with the stage buffers
-    // this lane's bias columns, read from LDS once for all row slabs
-    f32x4 bias_r[FN][4];
-    if constexpr (EPI == EPI_ROUND) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                bias_r[j][g] = *reinterpret_cast<const f32x4 *>(
-                    bias_l + wn * WTN + 32 * j + 8 * g + 4 * lkg);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int cl = 32 * j + 8 * g + 4 * lkg;  // column inside the wave tile
-                float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                              acc[i][j][4 * g + 3]};
-                char *dst = slab + lrow * ROWP + cl * OSZ;
-                if constexpr (EPI == EPI_ROUND) {
-                    if (p.bias) {
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) v[x] = v[x] + bias_r[j][g][x];
-                    }
-                    uint32_t h[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        h[x] = DT == DT_BF16 ? f32_to_bf16_bits(v[x]) : f32_to_f16_bits(v[x]);
-                    *reinterpret_cast<u32x2 *>(dst) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-                } else {
-                    *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-                }
-            }
-        }
-        // The slab is private to this wave and a wave's LDS operations execute
-        // in program order, so the reads below see the writes above and the
-        // next slab's writes cannot overtake these reads: no workgroup barrier
-        // (which would also wait for every outstanding global store).
-        // write the slab: rows gi0 + 0..31, columns gj0 + 0..WTN-1
-        const int64_t gi0 = row0 + wm * WTM + 32 * i;
-        const int64_t gj0 = col0 + wn * WTN;
-        OutT *base = EPI == EPI_PARTIAL
-                         ? reinterpret_cast<OutT *>(p.ws + chunk * p.rows * p.cols)
-                         : reinterpret_cast<OutT *>(static_cast<char *>(p.c) + c_off * OSZ);
-        const int64_t ld = EPI == EPI_PARTIAL ? p.cols : p.ldc;
-#pragma unroll
-        for (int q = 0; q < (32 * CPR + 63) / 64; ++q) {
-            const int idx = lane + 64 * q;
-            if (idx < 32 * CPR) {
-                const int r = idx / CPR, c = idx % CPR;
-                const int64_t gi = gi0 + r;
-                const int64_t gj = gj0 + c * (16 / OSZ);
-                const u32x4 val = *reinterpret_cast<const u32x4 *>(slab + r * ROWP + c * 16);
-                if (gi < row_end) {
-                    OutT *dst = base + gi * ld + gj;
-                    if (vec_c && gj + 16 / OSZ <= p.cols) {
-                        *reinterpret_cast<u32x4 *>(dst) = val;
-                    } else {
-                        const OutT *e = reinterpret_cast<const OutT *>(&val);
-#pragma unroll
-                        for (int x = 0; x < 16 / OSZ; ++x)
-                            if (gj + x < p.cols) dst[x] = e[x];
-                    }
-                }
-            }
-        }
-    }
+    static_assert(slab_bytes<EPI, WTN>() <= 2 * KG * (BM + BN) * 16, "slabs fit in the stage buffers");
+    write_tile<DT, EPI, WTM, WTN, FM, FN>(p, ti, acc, reinterpret_cast<char *>(lds_raw), lds_bias,
+                                          wave, wm, wn, lane);
 }
 
 }  // namespace mfma

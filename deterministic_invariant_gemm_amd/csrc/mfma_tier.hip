@@ -20,7 +20,14 @@ const TileShape *mfma_tile(int id) {
         {1, 256, 256}, {2, 256, 192}, {3, 256, 128}, {4, 128, 128}, {5, 128, 96},
         {6, 64, 64},   {7, 128, 256}, {9, 128, 192}, {10, 256, 96},
     };
+    // ids 20 + i: the A-direct kernel on base tile i (same shape)
+    static const TileShape ad[] = {
+        {21, 256, 256}, {22, 256, 192}, {23, 256, 128}, {24, 128, 128}, {25, 128, 96},
+        {27, 128, 256}, {29, 128, 192}, {30, 256, 96},
+    };
     for (const TileShape &s : shapes)
+        if (s.id == id) return &s;
+    for (const TileShape &s : ad)
         if (s.id == id) return &s;
     return nullptr;
 }

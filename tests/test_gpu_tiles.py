@@ -1,0 +1,98 @@
+"""Every tile shape of the MFMA tier -- in both kernel families (A staged
+through LDS, and A read directly into registers) -- must give the same bits for
+the same problem: the per-element MFMA sequence does not depend on the tile.
+Tiles are forced with the tuning hook tc = 16 + tile id; ids that an op does
+not instantiate are rejected with BI_ERR_HIP before any launch and skipped."""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_invariant_gemm_amd as dig
+import oracle
+import synth
+from parity import check, dev, empty, host
+
+pytestmark = pytest.mark.gpu
+
+TILE_IDS = list(range(1, 11)) + list(range(21, 31))
+
+
+def run_all(fn):
+    """{tile id: output bytes} for every tile the op accepts."""
+    out = {}
+    for tid in TILE_IDS:
+        try:
+            r = fn(16 + tid)
+        except dig.BIError as e:
+            assert e.status == -6
+            continue
+        out[tid] = r
+    return out
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
+@pytest.mark.parametrize("shape", [(300, 200, 260), (520, 136, 392)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_linear_tiles_identical(dt, shape):
+    m, k, n = shape
+    d = synth.linear(m, k, n, dt, seed=61 + m, sigma_w=0.05)
+    x, w, b, dy = dev(d["x"]), dev(d["w"]), dev(d["b"]), dev(d["dy"])
+    s = torch.cuda.current_stream()
+
+    def fwd(tc):
+        y = empty((m, n), np.uint16)
+        dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, s, tc))
+        return host(y, np.uint16)
+
+    def dxf(tc):
+        o = empty((m, k), np.uint16)
+        dig.check(dig.bi_backward_dx(o, dy, w, m, k, n, dt, s, tc))
+        return host(o, np.uint16)
+
+    def dwf(tc):
+        o = empty((k, n), np.uint16)
+        nb = dig.bi_backward_dw_workspace_bytes(m, k, n, dt, tc)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        dig.check(dig.bi_backward_dw(o, x, dy, m, k, n, dt, ws if nb else None, nb, s, tc))
+        return host(o, np.uint16)
+
+    refs = {"fwd": oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n),
+            "dX": oracle.linear_dx(dt, d["dy"], d["w"], m, k, n),
+            "dW": oracle.linear_dw(dt, d["x"], d["dy"], m, k, n)}
+    for name, fn in (("fwd", fwd), ("dX", dxf), ("dW", dwf)):
+        base = fn(1)
+        check(base, refs[name], dt, f"{name} default tile")
+        outs = run_all(fn)
+        assert len(outs) >= 4, (name, sorted(outs))
+        for tid, o in outs.items():
+            assert np.array_equal(o, base), (name, tid)
+        print(name, "tiles", sorted(outs))
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
+def test_grouped_tiles_identical(dt):
+    d = synth.grouped(700, 136, 200, 5, dt, seed=71, pad_rows=37, empty=(3,), sigma_w=0.05)
+    m, k, n, e = d["m"], d["k"], d["n"], d["e"]
+    inp, wts, g = dev(d["input"]), dev(d["weights"]), dev(d["dy"])
+    ids, off = dev(d["row_experts"]), dev(d["offsets"])
+    s = torch.cuda.current_stream()
+
+    def fwd(tc):
+        y = empty((m, n), np.uint16)
+        dig.check(dig.bi_grouped_nt(y, inp, wts, ids, off, m, k, n, e, dt, s, tc))
+        return host(y, np.uint16)
+
+    def bwd(tc):
+        di = empty((m, k), np.uint16)
+        dw = empty((e, n, k), np.uint32)
+        dig.check(dig.bi_grouped_nt_backward(di, dw, inp, wts, g, ids, off, m, k, n, e, dt, s, tc))
+        return np.concatenate([host(di, np.uint16).view(np.uint8).ravel(),
+                               host(dw, np.uint32).view(np.uint8).ravel()])
+
+    for name, fn in (("grouped fwd", fwd), ("grouped bwd", bwd)):
+        base = fn(1)
+        outs = run_all(fn)
+        assert len(outs) >= 2, (name, sorted(outs))
+        for tid, o in outs.items():
+            assert np.array_equal(o, base), (name, tid)
+        print(name, "tiles", sorted(outs))
