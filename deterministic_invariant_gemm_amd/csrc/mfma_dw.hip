@@ -5,10 +5,10 @@ namespace bi {
 
 hipError_t launch_mfma_dw(const MfmaArgs &p, int tile_id, int dt, int epi, int64_t grid, hipStream_t s) {
     using namespace mfma;
-    if (dt == DT_BF16 && epi == EPI_ROUND) return launch_among<DT_BF16, false, false, EPI_ROUND, MODE_PLAIN, 1, 3, 4, 5, 6, 7, 10>(p, tile_id, grid, s);
-    if (dt == DT_F16 && epi == EPI_ROUND) return launch_among<DT_F16, false, false, EPI_ROUND, MODE_PLAIN, 1, 3, 4, 5, 6, 7, 10>(p, tile_id, grid, s);
-    if (dt == DT_BF16 && epi == EPI_PARTIAL) return launch_among<DT_BF16, false, false, EPI_PARTIAL, MODE_PLAIN, 1, 3, 4, 5, 6, 7, 10>(p, tile_id, grid, s);
-    if (dt == DT_F16 && epi == EPI_PARTIAL) return launch_among<DT_F16, false, false, EPI_PARTIAL, MODE_PLAIN, 1, 3, 4, 5, 6, 7, 10>(p, tile_id, grid, s);
+    if (dt == DT_BF16 && epi == EPI_ROUND) return launch_among<DT_BF16, false, false, EPI_ROUND, MODE_PLAIN, 1, 3, 4, 5, 6, 7, 10, 13, 14, 15>(p, tile_id, grid, s);
+    if (dt == DT_F16 && epi == EPI_ROUND) return launch_among<DT_F16, false, false, EPI_ROUND, MODE_PLAIN, 1, 3, 4, 5, 6, 7, 10, 13, 14, 15>(p, tile_id, grid, s);
+    if (dt == DT_BF16 && epi == EPI_PARTIAL) return launch_among<DT_BF16, false, false, EPI_PARTIAL, MODE_PLAIN, 1, 3, 4, 5, 6, 7, 10, 13, 14, 15>(p, tile_id, grid, s);
+    if (dt == DT_F16 && epi == EPI_PARTIAL) return launch_among<DT_F16, false, false, EPI_PARTIAL, MODE_PLAIN, 1, 3, 4, 5, 6, 7, 10, 13, 14, 15>(p, tile_id, grid, s);
     return hipErrorInvalidValue;
 }
 

@@ -11,8 +11,8 @@ hipError_t launch_mfma_dx(const MfmaArgs &p, int tile_id, int dt, int epi, int64
         if (dt == DT_F16) return launch_ad_among<DT_F16, true, EPI_ROUND, MODE_PLAIN, 2, 3, 4, 5, 7, 9, 10>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
-    if (dt == DT_BF16) return launch_among<DT_BF16, true, true, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 5, 6, 7, 9, 10>(p, tile_id, grid, s);
-    if (dt == DT_F16) return launch_among<DT_F16, true, true, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 5, 6, 7, 9, 10>(p, tile_id, grid, s);
+    if (dt == DT_BF16) return launch_among<DT_BF16, true, true, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11, 13, 15>(p, tile_id, grid, s);
+    if (dt == DT_F16) return launch_among<DT_F16, true, true, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11, 13, 15>(p, tile_id, grid, s);
     return hipErrorInvalidValue;
 }
 

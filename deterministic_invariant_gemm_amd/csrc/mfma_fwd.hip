@@ -11,8 +11,8 @@ hipError_t launch_mfma_fwd(const MfmaArgs &p, int tile_id, int dt, int epi, int6
         if (dt == DT_F16) return launch_ad_among<DT_F16, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 7, 9>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
-    if (dt == DT_BF16) return launch_among<DT_BF16, true, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 6, 7, 9>(p, tile_id, grid, s);
-    if (dt == DT_F16) return launch_among<DT_F16, true, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 6, 7, 9>(p, tile_id, grid, s);
+    if (dt == DT_BF16) return launch_among<DT_BF16, true, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 6, 7, 9, 11, 12, 13, 14>(p, tile_id, grid, s);
+    if (dt == DT_F16) return launch_among<DT_F16, true, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 6, 7, 9, 11, 12, 13, 14>(p, tile_id, grid, s);
     return hipErrorInvalidValue;
 }
 

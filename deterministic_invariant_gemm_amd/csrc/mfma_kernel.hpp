@@ -89,13 +89,13 @@ __device__ __forceinline__ void transpose8x8(const u32x4 *in, u32x4 *out) {
 // Staging of one operand tile of R rows x BK reduction values.
 //   RC = true : element (row, r) at p[row*ld + r]  (reduction-contiguous)
 //   RC = false: element (row, r) at p[r*ld + row]  (row-contiguous)
-template <int R, bool RC>
+template <int R, bool RC, int NTH = NT>
 struct Stage {
-    static constexpr int DIRECT = R * KG / NT;              // RC: 16-byte chunks per thread
+    static constexpr int DIRECT = R * KG / NTH;              // RC: 16-byte chunks per thread
     static constexpr int UNITS = KG * (R / 8);              // !RC: 8x8 blocks per tile
-    static constexpr int UNITS_PER_THREAD = (UNITS + NT - 1) / NT;
+    static constexpr int UNITS_PER_THREAD = (UNITS + NTH - 1) / NTH;
     static constexpr int NREG = RC ? DIRECT : UNITS_PER_THREAD * 8;
-    static_assert(!RC || (R * KG) % NT == 0, "tile rows must fill the workgroup");
+    static_assert(!RC || (R * KG) % NTH == 0, "tile rows must fill the workgroup");
 
     u32x4 reg[NREG];
 
@@ -106,15 +106,15 @@ struct Stage {
         if constexpr (RC) {
 #pragma unroll
             for (int q = 0; q < DIRECT; ++q) {
-                const int c = t + NT * q;
+                const int c = t + NTH * q;
                 const int row = c / KG, kg = c % KG;
                 reg[q] = *reinterpret_cast<const u32x4 *>(p + (row0 + row) * ld + rk + 8 * kg);
             }
         } else {
 #pragma unroll
             for (int q = 0; q < UNITS_PER_THREAD; ++q) {
-                int u = t + NT * q;
-                if (UNITS % NT != 0 && u >= UNITS) u = UNITS - 1;  // duplicate, never stored
+                int u = t + NTH * q;
+                if (UNITS % NTH != 0 && u >= UNITS) u = UNITS - 1;  // duplicate, never stored
                 const int kg = u / (R / 8), ib = u % (R / 8);
                 const uint16_t *src = p + (rk + 8 * kg) * ld + row0 + 8 * ib;
 #pragma unroll
@@ -133,7 +133,7 @@ struct Stage {
         if constexpr (RC) {
 #pragma unroll
             for (int q = 0; q < DIRECT; ++q) {
-                const int c = t + NT * q;
+                const int c = t + NTH * q;
                 const int row = c / KG, kg = c % KG;
                 const int64_t gi = row0 + row;
                 const int64_t gic = gi < row_end ? gi : row_end - 1;
@@ -150,8 +150,8 @@ struct Stage {
         } else {
 #pragma unroll
             for (int q = 0; q < UNITS_PER_THREAD; ++q) {
-                int u = t + NT * q;
-                if (UNITS % NT != 0 && u >= UNITS) u = UNITS - 1;
+                int u = t + NTH * q;
+                if (UNITS % NTH != 0 && u >= UNITS) u = UNITS - 1;
                 const int kg = u / (R / 8), ib = u % (R / 8);
 #pragma unroll
                 for (int rr = 0; rr < 8; ++rr) {
@@ -182,15 +182,15 @@ struct Stage {
         if constexpr (RC) {
 #pragma unroll
             for (int q = 0; q < DIRECT; ++q) {
-                const int c = t + NT * q;
+                const int c = t + NTH * q;
                 const int row = c / KG, kg = c % KG;
                 lds[kg * R + swz(row, kg)] = reg[q];
             }
         } else {
 #pragma unroll
             for (int q = 0; q < UNITS_PER_THREAD; ++q) {
-                const int u = t + NT * q;
-                if (UNITS % NT != 0 && u >= UNITS) continue;
+                const int u = t + NTH * q;
+                if (UNITS % NTH != 0 && u >= UNITS) continue;
                 const int kg = u / (R / 8), ib = u % (R / 8);
                 u32x4 tr[8];
                 transpose8x8(&reg[q * 8], tr);
@@ -204,28 +204,28 @@ struct Stage {
 // Fast loads for interior tiles and full slices: a uniform (scalar) base
 // pointer per slice plus one 32-bit byte offset per thread and load, fixed for
 // the whole reduction, so address arithmetic stays out of the main loop.
-template <int R, bool RC>
+template <int R, bool RC, int NTH = NT>
 struct FastAddr {
-    static constexpr int NOFF = RC ? Stage<R, RC>::DIRECT : Stage<R, RC>::UNITS_PER_THREAD;
+    static constexpr int NOFF = RC ? Stage<R, RC, NTH>::DIRECT : Stage<R, RC, NTH>::UNITS_PER_THREAD;
     uint32_t off[NOFF];
 
     __device__ __forceinline__ void init(int64_t ld, int t) {
 #pragma unroll
         for (int q = 0; q < NOFF; ++q) {
             if constexpr (RC) {
-                const int c = t + NT * q;
+                const int c = t + NTH * q;
                 off[q] = (uint32_t)(((c / KG) * ld + 8 * (c % KG)) * 2);
             } else {
-                int u = t + NT * q;
-                if (Stage<R, RC>::UNITS % NT != 0 && u >= Stage<R, RC>::UNITS)
-                    u = Stage<R, RC>::UNITS - 1;
+                int u = t + NTH * q;
+                if (Stage<R, RC, NTH>::UNITS % NTH != 0 && u >= Stage<R, RC, NTH>::UNITS)
+                    u = Stage<R, RC, NTH>::UNITS - 1;
                 const int kg = u / (R / 8), ib = u % (R / 8);
                 off[q] = (uint32_t)(((int64_t)8 * kg * ld + 8 * ib) * 2);
             }
         }
     }
     // slice base: element (row0, rk) for RC, element (rk, row0) otherwise
-    __device__ __forceinline__ void load(Stage<R, RC> &st, const uint16_t *p, int64_t ld,
+    __device__ __forceinline__ void load(Stage<R, RC, NTH> &st, const uint16_t *p, int64_t ld,
                                          int64_t row0, int64_t rk) const {
         if constexpr (RC) {
             const char *base = reinterpret_cast<const char *>(p + row0 * ld + rk);
@@ -305,7 +305,7 @@ struct TileInfo {
     bool skip;
 };
 
-template <int MODE, int BM, int BN>
+template <int MODE, int BM, int BN, int NTH = NT>
 __device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
     TileInfo ti{};
     ti.skip = false;
@@ -353,7 +353,7 @@ __device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
             // padding rows: exact +0 (rublas: ids outside [0,E) give zero rows)
             const int64_t r1 = ti.row0 + BM < ti.row_end ? ti.row0 + BM : ti.row_end;
             uint16_t *pc = static_cast<uint16_t *>(p.c);
-            for (int64_t idx = t; idx < (r1 - ti.row0) * BN; idx += NT) {
+            for (int64_t idx = t; idx < (r1 - ti.row0) * BN; idx += NTH) {
                 const int64_t i = ti.row0 + idx / BN, j = ti.col0 + idx % BN;
                 if (j < p.cols) pc[i * p.ldc + j] = 0;
             }
@@ -393,9 +393,9 @@ __device__ __forceinline__ void stage_bias(const MfmaArgs &p, int64_t col0, floa
 }
 
 // LDS bytes the epilogue needs (four waves, one 32-row slab each)
-template <int EPI, int WTN>
+template <int EPI, int WTN, int NW = 4>
 constexpr int slab_bytes() {
-    return 4 * 32 * (WTN * (EPI == EPI_ROUND ? 2 : 4) + 16);
+    return NW * 32 * (WTN * (EPI == EPI_ROUND ? 2 : 4) + 16);
 }
 
 // Epilogue.  For block (i, j) a lane holds row (lane & 31) and, for
@@ -492,8 +492,10 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
 }
 
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE>
-__global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
-    static_assert(WGM * WGN == 4, "four waves");
+__global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm_kernel(MfmaArgs p) {
+    constexpr int NW = WGM * WGN;       // waves: 4 (one per SIMD) or 8 (two per SIMD)
+    constexpr int NTH = 64 * NW;
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    const TileInfo ti = decode_tile<MODE, BM, BN>(p, t);
+    const TileInfo ti = decode_tile<MODE, BM, BN, NTH>(p, t);
     if (ti.skip) return;
     const int64_t row0 = ti.row0, row_end = ti.row_end, col0 = ti.col0;
     const int64_t r_begin = ti.r_begin, r_end = ti.r_end;
@@ -519,8 +521,8 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
 
     stage_bias<DT, EPI, BN>(p, col0, lds_bias, t);
 
-    Stage<BM, A_RC> sa;
-    Stage<BN, B_RC> sb;
+    Stage<BM, A_RC, NTH> sa;
+    Stage<BN, B_RC, NTH> sb;
     Comp comp;
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -539,8 +541,8 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
     int64_t s = 0;
     if (int_a && int_b && offsets_fit<BM, A_RC>(p.lda) && offsets_fit<BN, B_RC>(p.ldb)) {
         // ---- lean main loop over full slices ----------------------------------
-        FastAddr<BM, A_RC> fa_addr;
-        FastAddr<BN, B_RC> fb_addr;
+        FastAddr<BM, A_RC, NTH> fa_addr;
+        FastAddr<BN, B_RC, NTH> fb_addr;
         fa_addr.init(p.lda, t);
         fb_addr.init(p.ldb, t);
         if (nfull >= 2) {
@@ -605,7 +607,7 @@ __global__ __launch_bounds__(NT) void mfma_gemm_kernel(MfmaArgs p) {
         __syncthreads();
     }
 
-    static_assert(slab_bytes<EPI, WTN>() <= 2 * KG * (BM + BN) * 16, "slabs fit in the stage buffers");
+    static_assert(slab_bytes<EPI, WTN, NW>() <= 2 * KG * (BM + BN) * 16, "slabs fit in the stage buffers");
     write_tile<DT, EPI, WTM, WTN, FM, FN>(p, ti, acc, reinterpret_cast<char *>(lds_raw), lds_bias,
                                           wave, wm, wn, lane);
 }
@@ -629,12 +631,18 @@ template <> struct TileOf<6> { static constexpr int BM = 64, BN = 64, WGM = 2, W
 template <> struct TileOf<7> { static constexpr int BM = 128, BN = 256, WGM = 2, WGN = 2; };
 template <> struct TileOf<9> { static constexpr int BM = 128, BN = 192, WGM = 2, WGN = 2; };
 template <> struct TileOf<10> { static constexpr int BM = 256, BN = 96, WGM = 4, WGN = 1; };
+// eight waves, two per SIMD
+template <> struct TileOf<11> { static constexpr int BM = 256, BN = 192, WGM = 4, WGN = 2; };
+template <> struct TileOf<12> { static constexpr int BM = 256, BN = 256, WGM = 4, WGN = 2; };
+template <> struct TileOf<13> { static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 2; };
+template <> struct TileOf<14> { static constexpr int BM = 128, BN = 256, WGM = 2, WGN = 4; };
+template <> struct TileOf<15> { static constexpr int BM = 128, BN = 128, WGM = 2, WGN = 4; };
 
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>
 hipError_t launch_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
     using T = TileOf<ID>;
     hipLaunchKernelGGL((mfma_gemm_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE>),
-                       dim3(grid), dim3(NT), 0, s, p);
+                       dim3(grid), dim3(64 * T::WGM * T::WGN), 0, s, p);
     return hipGetLastError();
 }
 

@@ -19,6 +19,8 @@ const TileShape *mfma_tile(int id) {
     static const TileShape shapes[] = {
         {1, 256, 256}, {2, 256, 192}, {3, 256, 128}, {4, 128, 128}, {5, 128, 96},
         {6, 64, 64},   {7, 128, 256}, {9, 128, 192}, {10, 256, 96},
+        // eight-wave workgroups
+        {11, 256, 192}, {12, 256, 256}, {13, 256, 128}, {14, 128, 256}, {15, 128, 128},
     };
     // ids 20 + i: the A-direct kernel on base tile i (same shape)
     static const TileShape ad[] = {

@@ -14,7 +14,7 @@ from parity import check, dev, empty, host
 
 pytestmark = pytest.mark.gpu
 
-TILE_IDS = list(range(1, 11)) + list(range(21, 31))
+TILE_IDS = list(range(1, 16)) + list(range(21, 31))
 
 
 def run_all(fn):
