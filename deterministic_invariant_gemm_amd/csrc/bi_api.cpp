@@ -101,6 +101,19 @@ int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.ch
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
+// Operand extents for the direct-load kernels, and the tile they may use: the
+// direct-load family (ids 40 + base) needs 16-byte-aligned rows whose length is
+// a multiple of 8 elements and operands below 2^30 bytes; otherwise the base
+// tile of the register-staged family runs (same bits).
+constexpr int64_t kDirectMaxBytes = (int64_t)1 << 30;
+int direct_tile(MfmaArgs &a, int tile, int64_t a_bytes, int64_t b_bytes) {
+    a.a_bytes = a_bytes;
+    a.b_bytes = b_bytes;
+    if (tile < 40) return tile;
+    const bool ok = a.vec_a && a.vec_b && a_bytes <= kDirectMaxBytes && b_bytes <= kDirectMaxBytes;
+    return ok ? tile : tile - 40;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,7 +167,8 @@ int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t 
     a.vec_a = aligned16(x) && k % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(y) && n % 4 == 0;
-    return hip_status(launch_mfma_gemm(a, pl.tile, dtype, /*layout A rc, B strided*/ 1, 0, stream));
+    const int tile = direct_tile(a, pl.tile, 2 * m * k, 2 * k * n);
+    return hip_status(launch_mfma_gemm(a, tile, dtype, /*layout A rc, B strided*/ 1, 0, stream));
 }
 
 int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k, int64_t n,
@@ -183,7 +197,8 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
     a.vec_a = aligned16(dy) && n % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(dx) && k % 4 == 0;
-    return hip_status(launch_mfma_gemm(a, pl.tile, dtype, /*both rc*/ 3, 0, stream));
+    const int tile = direct_tile(a, pl.tile, 2 * m * n, 2 * k * n);
+    return hip_status(launch_mfma_gemm(a, tile, dtype, /*both rc*/ 3, 0, stream));
 }
 
 size_t bi_backward_dw_workspace_bytes(int64_t m, int64_t k, int64_t n, int dtype, int tc) {
@@ -228,7 +243,8 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
         a.vec_a = aligned16(x) && k % 8 == 0;
         a.vec_b = aligned16(dy) && n % 8 == 0;
         a.vec_c = epi ? (aligned16(workspace) && n % 4 == 0) : (aligned8(dw) && n % 4 == 0);
-        e = launch_mfma_gemm(a, pl.tile, dtype, /*both strided*/ 0, epi, stream);
+        const int tile = direct_tile(a, pl.tile, 2 * m * k, 2 * m * n);
+        e = launch_mfma_gemm(a, tile, dtype, /*both strided*/ 0, epi, stream);
     }
     if (e != hipSuccess) return BI_ERR_HIP;
     if (chunks > 1)
@@ -303,7 +319,8 @@ int bi_grouped_nt(void *y, const void *input, const void *weights, const uint32_
     a.vec_a = aligned16(input) && k % 8 == 0;
     a.vec_b = aligned16(weights) && k % 8 == 0;
     a.vec_c = aligned8(y) && n % 4 == 0;
-    return hip_status(launch_mfma_gemm(a, pl.tile, dtype, 3, 0, stream));
+    const int tile = direct_tile(a, pl.tile, 2 * m * k, 2 * e * n * k);
+    return hip_status(launch_mfma_gemm(a, tile, dtype, 3, 0, stream));
 }
 
 int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, const void *weights,
@@ -334,7 +351,8 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
             a.vec_a = aligned16(grad_out) && n % 8 == 0;
             a.vec_b = aligned16(weights) && k % 8 == 0;
             a.vec_c = aligned8(dinput) && k % 4 == 0;
-            er = launch_mfma_gemm(a, pl.tile, dtype, 1, 0, stream);
+            const int tile = direct_tile(a, pl.tile, 2 * m * n, 2 * e * n * k);
+            er = launch_mfma_gemm(a, tile, dtype, 1, 0, stream);
         }
         if (er != hipSuccess) return BI_ERR_HIP;
     }
@@ -355,7 +373,8 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
     a.vec_a = aligned16(grad_out) && n % 8 == 0;
     a.vec_b = aligned16(input) && k % 8 == 0;
     a.vec_c = aligned16(dweights) && k % 4 == 0;
-    return hip_status(launch_mfma_gemm(a, pw.tile, dtype, 0, 2, stream));
+    const int tile = direct_tile(a, pw.tile, 2 * m * n, 2 * m * k);
+    return hip_status(launch_mfma_gemm(a, tile, dtype, 0, 2, stream));
 }
 
 }  // extern "C"

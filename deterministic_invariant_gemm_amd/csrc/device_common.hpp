@@ -72,6 +72,22 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two f32 -> two bf16 / f16 values, each rounded once to nearest-even (IEEE
+// overflow to inf and subnormals), packed with `a` in the low half:
+// v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32 in the default rounding mode.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2_rne(float a, float b) {
+    static_assert(DT == DT_BF16 || DT == DT_F16, "16-bit output types");
+    if constexpr (DT == DT_BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
 template <int DT>
 __device__ __forceinline__ void store_elem(void *base, int64_t i, float v) {
     if constexpr (DT == DT_F32) {

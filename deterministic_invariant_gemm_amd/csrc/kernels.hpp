@@ -64,6 +64,8 @@ struct MfmaArgs {
     int64_t c_expert_stride;
     int vec_a, vec_b;  // 16-byte vector loads allowed for A / B
     int vec_c;         // 8-byte (16-bit outputs) / 16-byte (f32) vector stores allowed
+    // bytes readable from a / b (direct-load kernels: reads past them return zero)
+    int64_t a_bytes, b_bytes;
 };
 
 struct Fp8Args {

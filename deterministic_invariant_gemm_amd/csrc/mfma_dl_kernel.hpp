@@ -1,0 +1,335 @@
+// MFMA kernel with both operands copied from global memory straight into LDS
+// ("direct-load" family) for gfx950.
+//
+// Same arithmetic as mfma_gemm_kernel (mfma_kernel.hpp): every output element
+// receives one v_mfma_f32_32x32x16_{bf16,f16} per 16-deep reduction step, in
+// ascending order from +0 over 64-deep stages starting at the first index of
+// its reduction range, reduction indices past the end contributing exact
+// zeros, and the B fragment is the first MFMA operand.  Every tile shape of
+// this family, and of the other kernel families, therefore gives identical
+// bits (sgemm-bi PyPI page, "Determinism contracts": bit-identical tile
+// families; the forward is batch-invariant because no tile reads M).
+//
+// Data movement:
+//   * buffer_load_dwordx4 ... lds: each lane copies 16 bytes from global memory
+//     into LDS at (instruction base + 16 * lane), without passing through
+//     registers, while earlier stages are being multiplied.  Lanes are assigned so that one instruction reads whole
+//     128-byte lines.  A lane whose chunk lies past the end of the reduction
+//     range is given an offset beyond the buffer, which makes the hardware
+//     return zeros; operand rows or columns past the matrix edge are read from
+//     whatever lies there (or zero beyond the allocation) and only feed output
+//     elements that are never stored.
+//   * Reduction-contiguous operands are kept as [rows][64] (128-byte rows);
+//     each MFMA fragment (8 consecutive reduction values of one row per lane)
+//     is one ds_read_b128.  The 16-byte chunks of a row are XOR-permuted by
+//     (row >> 1) & 7 so the 16 rows read in one LDS pass hit distinct banks.
+//   * Row-contiguous operands (reduction index strided in memory) are kept as
+//     [64][rows] and read with two ds_read_b64_tr_b16, which hand each lane
+//     4 consecutive reduction values of one row; the chunks of each reduction
+//     row are XOR-permuted so the 4 rows read together hit distinct banks.
+//   * A ring of NS LDS stages (as many as fit, at most 4): the copies of the
+//     next NS-1 stages are in flight while one stage is multiplied; one
+//     workgroup barrier per stage.
+#pragma once
+
+#include "mfma_kernel.hpp"
+
+#define BI_LDS __attribute__((address_space(3)))
+
+namespace bi {
+namespace mfma {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// byte offset that is past every operand buffer (operands are < 2^30 bytes)
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// s_waitcnt with vmcnt = N and the other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// vmcnt(n * Q) for a run-time n in [0, 2]
+template <int Q>
+__device__ __forceinline__ void wait_vmcnt_stages(int n) {
+    if (n <= 0) wait_vmcnt<0>();
+    else if (n == 1) wait_vmcnt<Q>();
+    else wait_vmcnt<2 * Q>();
+}
+
+// LDS stages of 64 reduction values for a BM x BN tile: as many as fit in
+// 160 KB next to the bias row, at most 4
+constexpr int dl_stages(int bm, int bn) {
+    const int per = 128 * (bm + bn), avail = 160 * 1024 - 4 * bn;
+    return avail / per >= 4 ? 4 : avail / per;
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: 48-bit base, stride 0, `bytes` readable; loads at
+// offsets >= bytes return zeros without touching memory.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, int64_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes at `voff` of the buffer into LDS at
+// `lds_addr` + 16 * lane.  Written as inline assembly so that the compiler does
+// not treat it as an LDS store and wait for it before every later LDS read;
+// the kernel orders these copies itself (s_waitcnt vmcnt + barrier).  M0
+// carries the LDS address and is set right here; nothing else in the kernels
+// keeps a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(i32x4 rs, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rs), "s"(lds_addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// XOR of the 16-byte chunk index inside a row of a reduction-contiguous tile.
+// A fragment read takes one chunk from each of 32 consecutive rows; any 8 (and
+// any 16) of those rows that the LDS serves together land on distinct banks.
+// Depends on row & 15 only, so it is a per-lane constant for fragment reads.
+__device__ __forceinline__ int rc_xor(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+
+// XOR of the 16-byte chunk index inside reduction row k of a row-contiguous
+// tile of R columns.  A transposed fragment read takes 32 bytes (16 lanes) or
+// 64 bytes (32 lanes) from each of 4 consecutive reduction rows; the XOR
+// spreads those rows over distinct banks for either grouping, and it keeps
+// the chunk inside the row (R/8 chunks: a multiple of 16 when R % 128 == 0,
+// of 8 otherwise).  Depends on k & 3 only.
+template <int R>
+__device__ __forceinline__ int rs_xor(int k) {
+    static_assert(R % 64 == 0, "row-contiguous tiles need a multiple of 64 columns");
+    const int t = k & 3;
+    return R % 128 == 0 ? 4 * t + 2 * (t >> 1) : 2 * t;
+}
+
+// Global -> LDS copy of one operand tile per 64-deep stage: R/8 instructions
+// of 1 KB, spread evenly over the NW waves.
+template <int R, bool RC, int NW>
+struct DLoad {
+    static constexpr int NQ = R / 8 / NW;
+    static_assert(NQ >= 1 && NQ * 8 * NW == R, "tile rows must spread evenly over the waves");
+    uint32_t off[NQ];  // byte offset of this lane's chunk in stage 0
+    int kin[NQ];       // reduction index of the chunk within its stage
+    uint32_t sstride;  // bytes between consecutive stages
+
+    // `o0`: first row (RC) or column (row-contiguous) of the tile
+    __device__ __forceinline__ void init(int64_t ld, int64_t o0, int64_t r_begin, int wave,
+                                         int lane) {
+#pragma unroll
+        for (int p = 0; p < NQ; ++p) {
+            const int s = 64 * (wave + NW * p) + lane;  // chunk slot within the stage
+            if constexpr (RC) {
+                const int row = s >> 3, kg = (s & 7) ^ rc_xor(row);
+                off[p] = (uint32_t)(((o0 + row) * ld + r_begin + 8 * kg) * 2);
+                kin[p] = 8 * kg;
+            } else {
+                const int k = s / (R / 8), c = (s % (R / 8)) ^ rs_xor<R>(k);
+                off[p] = (uint32_t)(((r_begin + k) * ld + o0 + 8 * c) * 2);
+                kin[p] = k;
+            }
+        }
+        sstride = RC ? 128u : (uint32_t)(64 * ld * 2);
+    }
+
+    // copy stage s into `stage`; with MASK, chunks at reduction index >= rem
+    // (counted from the stage start) read as zeros
+    template <bool MASK>
+    __device__ __forceinline__ void issue(i32x4 rs, BI_LDS char *stage, int s, int64_t rem,
+                                          int wave) const {
+#pragma unroll
+        for (int p = 0; p < NQ; ++p) {
+            uint32_t o = off[p] + (uint32_t)s * sstride;
+            if (MASK && kin[p] >= rem) o = kOutOfRange;
+            lds_dma16(rs, o, (uint32_t)reinterpret_cast<uintptr_t>(stage + 1024 * (wave + NW * p)));
+        }
+    }
+};
+
+// MFMA fragment reads from a reduction-contiguous stage ([rows][64]).
+struct RcFrag {
+    uint32_t koff[BK / 16];  // per 16-deep step: lane's byte offset inside a 32-row block
+
+    __device__ __forceinline__ void init(int lane) {
+        const int r = lane & 31, hi = lane >> 5;
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk)
+            koff[kk] = (uint32_t)(r * 128 + 16 * ((2 * kk + hi) ^ rc_xor(r)));
+    }
+    // rows base .. base+31 (base a multiple of 32)
+    __device__ __forceinline__ u32x4 read(const BI_LDS char *stage, int base, int kk) const {
+        return *reinterpret_cast<const BI_LDS u32x4 *>(stage + base * 128 + koff[kk]);
+    }
+};
+
+// MFMA fragment reads from a row-contiguous stage ([64][R]) with transposed
+// LDS reads: lane l gets row (l & 31), reduction values 8*(l >> 5) + 0..7.
+template <int R>
+struct RsFrag {
+    static constexpr int PITCH = 2 * R;
+    uint32_t lane_off;
+    int hq;  // XOR of the 32-column block index for this lane's reduction rows
+
+    __device__ __forceinline__ void init(int lane) {
+        const int g = lane >> 4, j = lane & 15;
+        const int kr = 8 * (g >> 1) + (j >> 2);      // first reduction row of the lane
+        const int cl = 2 * (g & 1) + ((j & 3) >> 1);  // 16-byte chunk inside the 32 columns
+        // physical chunk (4F + cl) ^ h = 4 (F ^ (h >> 2)) + (cl ^ (h & 3))
+        const int h = rs_xor<R>(kr);
+        hq = h >> 2;
+        lane_off = (uint32_t)(kr * PITCH + 16 * (cl ^ (h & 3)) + 8 * (j & 1));
+    }
+    // columns 32F .. 32F+31
+    __device__ __forceinline__ u32x4 read(const BI_LDS char *stage, int F, int kk) const {
+        const BI_LDS char *a = stage + lane_off + kk * 16 * PITCH + 64 * (F ^ hq);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BI_LDS s16x4 *)a);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BI_LDS s16x4 *)(a + 4 * PITCH));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    }
+};
+
+template <bool RC, int R>
+struct FragOf {
+    using type = RsFrag<R>;
+};
+template <int R>
+struct FragOf<true, R> {
+    using type = RcFrag;
+};
+
+template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE>
+__global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
+    constexpr int SA = 128 * BM, SB = 128 * BN;  // bytes of one stage of A / B
+    constexpr int NS = dl_stages(BM, BN);
+    static_assert(NS >= 2 && NS <= 4, "two to four stages");
+    static_assert(slab_bytes<EPI, WTN, NW>() <= NS * (SA + SB), "epilogue slabs fit in the stages");
+
+    // NS stages of [A | B]; reused by the epilogue
+    __shared__ __align__(1024) char lds_raw[NS * (SA + SB)];
+    __shared__ __align__(16) float lds_bias[BN];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+
+    const TileInfo ti = decode_tile<MODE, BM, BN, 64 * NW>(p, t);
+    if (ti.skip) return;
+    const int64_t row0 = ti.row0, col0 = ti.col0;
+    const int64_t r_begin = ti.r_begin, r_end = ti.r_end;
+    stage_bias<DT, EPI, BN>(p, col0, lds_bias, t);
+
+    const i32x4 rsa = make_rsrc(p.a, p.a_bytes);
+    const i32x4 rsb = make_rsrc(static_cast<const uint16_t *>(p.b) + ti.b_off, p.b_bytes - 2 * ti.b_off);
+    using LA = DLoad<BM, A_RC, NW>;
+    using LB = DLoad<BN, B_RC, NW>;
+    LA la;
+    LB lb;
+    la.init(p.lda, row0, r_begin, wave, lane);
+    lb.init(p.ldb, col0, r_begin, wave, lane);
+    typename FragOf<A_RC, BM>::type ra;
+    typename FragOf<B_RC, BN>::type rb;
+    ra.init(lane);
+    rb.init(lane);
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    const int64_t red = r_end - r_begin;
+    const int nst = (int)((red + BK - 1) / BK);
+    BI_LDS char *ring = (BI_LDS char *)lds_raw;
+
+    auto issue = [&](int s) {
+        BI_LDS char *da = ring + (s % NS) * (SA + SB);
+        BI_LDS char *db = da + SA;
+        const int64_t rem = red - (int64_t)BK * s;
+        if (rem >= BK) {
+            la.template issue<false>(rsa, da, s, rem, wave);
+            lb.template issue<false>(rsb, db, s, rem, wave);
+        } else {
+            la.template issue<true>(rsa, da, s, rem, wave);
+            lb.template issue<true>(rsb, db, s, rem, wave);
+        }
+    };
+    auto frag_a = [&](const BI_LDS char *st, int i, int kk) {
+        if constexpr (A_RC) return ra.read(st, wm * WTM + 32 * i, kk);
+        else return ra.read(st, (wm * WTM) / 32 + i, kk);
+    };
+    auto frag_b = [&](const BI_LDS char *st, int j, int kk) {
+        if constexpr (B_RC) return rb.read(st, wn * WTN + 32 * j, kk);
+        else return rb.read(st, (wn * WTN) / 32 + j, kk);
+    };
+
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nst) issue(s);
+
+    for (int s = 0; s < nst; ++s) {
+        // stage s has landed once only the later stages' copies are pending
+        const int later = nst - 1 - s < NS - 2 ? nst - 1 - s : NS - 2;
+        wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
+        __syncthreads();  // every wave's share of stage s is in; stage s-1 is free
+        if (s + NS - 1 < nst) issue(s + NS - 1);
+
+        const BI_LDS char *ca = ring + (s % NS) * (SA + SB);
+        const BI_LDS char *cb = ca + SA;
+        u32x4 fa[2][FM], fb[2][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[0][i] = frag_a(ca, i, 0);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[0][j] = frag_b(cb, j, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < BK / 16) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) fa[cur ^ 1][i] = frag_a(ca, i, kk + 1);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) fb[cur ^ 1][j] = frag_b(cb, j, kk + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = mfma_step<DT>(fb[cur][j], fa[cur][i], acc[i][j]);
+        }
+    }
+
+    write_tile<DT, EPI, WTM, WTN, FM, FN>(p, ti, acc, reinterpret_cast<char *>(lds_raw), lds_bias,
+                                          wave, wm, wn, lane);
+}
+
+template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>
+hipError_t launch_dl_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
+    using T = TileOf<ID>;
+    hipLaunchKernelGGL((mfma_dl_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE>),
+                       dim3(grid), dim3(64 * T::WGM * T::WGN), 0, s, p);
+    return hipGetLastError();
+}
+
+// tile ids 40 + base id select the direct-load kernel with base tile `id`
+template <int DT, bool ARC, bool BRC, int EPI, int MODE, int... IDS>
+hipError_t launch_dl_among(const MfmaArgs &p, int tile_id, int64_t grid, hipStream_t s) {
+    hipError_t r = hipErrorInvalidValue;
+    ((tile_id == 40 + IDS ? (void)(r = launch_dl_tile<DT, ARC, BRC, EPI, MODE, IDS>(p, grid, s))
+                          : (void)0),
+     ...);
+    return r;
+}
+
+}  // namespace mfma
+}  // namespace bi

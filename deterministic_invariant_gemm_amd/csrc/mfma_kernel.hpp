@@ -446,11 +446,8 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
 #pragma unroll
                         for (int x = 0; x < 4; ++x) v[x] = v[x] + bias_r[j][g][x];
                     }
-                    uint32_t h[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x)
-                        h[x] = DT == DT_BF16 ? f32_to_bf16_bits(v[x]) : f32_to_f16_bits(v[x]);
-                    *reinterpret_cast<u32x2 *>(dst) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+                    *reinterpret_cast<u32x2 *>(dst) =
+                        u32x2{pack2_rne<DT>(v[0], v[1]), pack2_rne<DT>(v[2], v[3])};
                 } else {
                     *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
                 }

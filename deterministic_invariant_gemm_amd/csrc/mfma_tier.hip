@@ -27,9 +27,17 @@ const TileShape *mfma_tile(int id) {
         {21, 256, 256}, {22, 256, 192}, {23, 256, 128}, {24, 128, 128}, {25, 128, 96},
         {27, 128, 256}, {29, 128, 192}, {30, 256, 96},
     };
+    // ids 40 + i: the direct-load kernel on base tile i (same shape)
+    static const TileShape dl[] = {
+        {41, 256, 256}, {42, 256, 192}, {43, 256, 128}, {44, 128, 128}, {45, 128, 96},
+        {46, 64, 64},   {47, 128, 256}, {49, 128, 192}, {50, 256, 96},  {51, 256, 192},
+        {52, 256, 256}, {53, 256, 128}, {54, 128, 256}, {55, 128, 128},
+    };
     for (const TileShape &s : shapes)
         if (s.id == id) return &s;
     for (const TileShape &s : ad)
+        if (s.id == id) return &s;
+    for (const TileShape &s : dl)
         if (s.id == id) return &s;
     return nullptr;
 }

@@ -57,6 +57,18 @@ def integer_bits(shape, lo, hi, seed, idx, dt):
     return to_bits(v, dt)
 
 
+def wide_exponent_bits(shape, dt, seed, idx, emin, emax):
+    """Values sign * 2^e * (1 + f) with e uniform in [emin, emax] and f a
+    uniformly drawn fraction of the dtype's significand width, so every value
+    is exact in dt (products of two such values span many binades)."""
+    frac_bits = {BF16: 7, F16: 10, F32: 23}[dt]
+    g = rng(seed, idx)
+    sign = np.where(g.integers(0, 2, size=shape) == 1, -1.0, 1.0)
+    e = g.integers(emin, emax + 1, size=shape).astype(np.float64)
+    f = g.integers(0, 1 << frac_bits, size=shape).astype(np.float64) / (1 << frac_bits)
+    return to_bits((sign * np.exp2(e) * (1.0 + f)).astype(np.float32), dt)
+
+
 # --------------------------------------------------------------------------
 # linear workloads
 # --------------------------------------------------------------------------

@@ -221,6 +221,46 @@ def test_config3_batch_invariance_sweep():
     check(host(L.dw(1), np.uint16)[krows], rw, L.dt, "config3 dW")
 
 
+@pytest.mark.parametrize("dt,emin,emax", [(synth.BF16, -60, 64), (synth.F16, -12, 8)],
+                         ids=["bf16", "f16"])
+@pytest.mark.parametrize("tc", [0, 1])
+def test_output_rounding_bit_exact(dt, emin, emax, tc):
+    """Reduction length 1: each output holds one exact product, so the f32
+    accumulator is exact and the only rounding is the final one to the output
+    type.  Operands span many binades (ties to even, overflow to inf, f16
+    subnormal results), and every element of forward, dX and dW must equal the
+    oracle's single round-to-nearest-even bit for bit."""
+    st = np.uint16
+    s = torch.cuda.current_stream()
+    m, k, n = 96, 128, 192
+    # forward: X[m,1] W[1,n]
+    x = synth.wide_exponent_bits((m, 1), dt, 81, 0, emin, emax)
+    w = synth.wide_exponent_bits((1, n), dt, 81, 1, emin, emax)
+    y = empty((m, n), st)
+    dig.check(dig.bi_forward(y, dev(x), dev(w), None, m, 1, n, dt, s, tc))
+    ref = oracle.linear_forward(dt, x, w, None, m, 1, n)
+    assert np.array_equal(host(y, st), ref.out)
+    # dX = dY[m,1] W[k,1]^T
+    dy = synth.wide_exponent_bits((m, 1), dt, 82, 0, emin, emax)
+    wk = synth.wide_exponent_bits((k, 1), dt, 82, 1, emin, emax)
+    dx = empty((m, k), st)
+    dig.check(dig.bi_backward_dx(dx, dev(dy), dev(wk), m, k, 1, dt, s, tc))
+    ref = oracle.linear_dx(dt, dy, wk, m, k, 1)
+    assert np.array_equal(host(dx, st), ref.out)
+    # dW = X[1,k]^T dY[1,n]
+    x1 = synth.wide_exponent_bits((1, k), dt, 83, 0, emin, emax)
+    dy1 = synth.wide_exponent_bits((1, n), dt, 83, 1, emin, emax)
+    dw = empty((k, n), st)
+    dig.check(dig.bi_backward_dw(dw, dev(x1), dev(dy1), 1, k, n, dt, None, 0, s, tc))
+    ref = oracle.linear_dw(dt, x1, dy1, 1, k, n)
+    assert np.array_equal(host(dw, st), ref.out)
+    # the draws really reach overflow (and, for f16, subnormal results)
+    out = host(y, st)
+    assert np.any((out & 0x7FFF) == (0x7F80 if dt == synth.BF16 else 0x7C00))
+    if dt == synth.F16:
+        assert np.any(((out & 0x7C00) == 0) & ((out & 0x3FF) != 0))
+
+
 def test_k_zero_gives_rounded_bias_and_m_zero_dw_is_zero():
     dt = synth.BF16
     b = dev(synth.normal_bits((96,), 1.0, 5, 0, dt))

@@ -1,5 +1,6 @@
-"""Every tile shape of the MFMA tier -- in both kernel families (A staged
-through LDS, and A read directly into registers) -- must give the same bits for
+"""Every tile shape of the MFMA tier -- in all three kernel families (operands
+staged through registers into LDS, A read directly into registers, and both
+operands copied straight from global memory into LDS) -- must give the same bits for
 the same problem: the per-element MFMA sequence does not depend on the tile.
 Tiles are forced with the tuning hook tc = 16 + tile id; ids that an op does
 not instantiate are rejected with BI_ERR_HIP before any launch and skipped."""
@@ -14,7 +15,7 @@ from parity import check, dev, empty, host
 
 pytestmark = pytest.mark.gpu
 
-TILE_IDS = list(range(1, 16)) + list(range(21, 31))
+TILE_IDS = list(range(1, 16)) + list(range(21, 31)) + list(range(41, 56))
 
 
 def run_all(fn):
@@ -31,7 +32,7 @@ def run_all(fn):
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
-@pytest.mark.parametrize("shape", [(300, 200, 260), (520, 136, 392)],
+@pytest.mark.parametrize("shape", [(300, 200, 260), (520, 136, 392), (700, 264, 456)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_linear_tiles_identical(dt, shape):
     m, k, n = shape
