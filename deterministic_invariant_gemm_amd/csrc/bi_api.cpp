@@ -53,24 +53,29 @@ bool mfma_eligible(int op, int dt, int tc, int64_t k, int64_t n) {
 // Tile per op from the non-M output dims only (the kernel's column count is N
 // for forward / fp8 / grouped forward, K for dX / grouped dinput; dW tiles its
 // [K, N] output).  Every tile issues the same MFMA sequence per element, so
-// this choice affects speed only.
+// this choice affects speed only.  Ids 40 + i are the direct-load kernel on
+// shape i (used when operands are aligned, see direct_tile); the fp8 op has
+// its own kernel and takes the base ids.
 int pick_tile(int op, int64_t k, int64_t n) {
     const int64_t cols = (op == OP_DX || op == OP_GDIN) ? k : n;
     switch (op) {
-    case OP_FWD:
     case OP_FP8:
         if (cols >= 2048 && cols % 192 == 0 && cols / 192 <= 16) return 2;  // 256x192
         if (cols >= 2048) return 1;                                           // 256x256
         return cols >= 128 ? 4 : 6;
+    case OP_FWD:
+        if (cols >= 2048 && cols % 192 == 0 && cols / 192 <= 16) return 51;  // 256x192, 8 waves
+        if (cols >= 2048) return 52;                                           // 256x256, 8 waves
+        return cols >= 128 ? 44 : 46;
     case OP_DX:
-        if (cols % 96 == 0 && cols <= 1536) return 5;  // 128x96
-        return cols >= 128 ? 4 : 6;
+        if (cols % 96 == 0 && cols <= 1536) return 45;  // 128x96
+        return cols >= 128 ? 44 : 46;
     case OP_DW:
-        return (k >= 128 && n >= 128) ? 4 : 6;
+        return (k >= 128 && n >= 128) ? 55 : 46;  // 128x128 (8 waves) / 64x64
     case OP_GFWD: case OP_GDIN: case OP_GDW:
-        return 4;
+        return 41;  // 256x256
     }
-    return 4;
+    return 44;
 }
 
 // tc >= 16 is a tuning / test hook: tc = 16 + id forces MFMA tile `id` (when the
@@ -102,16 +107,18 @@ int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.ch
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
 // Operand extents for the direct-load kernels, and the tile they may use: the
-// direct-load family (ids 40 + base) needs 16-byte-aligned rows whose length is
-// a multiple of 8 elements and operands below 2^30 bytes; otherwise the base
-// tile of the register-staged family runs (same bits).
+// direct-load (ids 40 + base) and direct-A (ids 60 + base) families need
+// 16-byte-aligned rows whose length is a multiple of 8 elements and operands
+// below 2^30 bytes; otherwise the base tile of the register-staged family runs
+// (same bits).
 constexpr int64_t kDirectMaxBytes = (int64_t)1 << 30;
 int direct_tile(MfmaArgs &a, int tile, int64_t a_bytes, int64_t b_bytes) {
     a.a_bytes = a_bytes;
     a.b_bytes = b_bytes;
     if (tile < 40) return tile;
     const bool ok = a.vec_a && a.vec_b && a_bytes <= kDirectMaxBytes && b_bytes <= kDirectMaxBytes;
-    return ok ? tile : tile - 40;
+    if (ok) return tile;
+    return tile >= 60 ? tile - 60 : tile - 40;
 }
 
 }  // namespace

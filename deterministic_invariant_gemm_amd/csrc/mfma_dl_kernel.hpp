@@ -28,8 +28,10 @@
 //     4 consecutive reduction values of one row; the chunks of each reduction
 //     row are XOR-permuted so the 4 rows read together hit distinct banks.
 //   * A ring of NS LDS stages (as many as fit, at most 4): the copies of the
-//     next NS-1 stages are in flight while one stage is multiplied; one
-//     workgroup barrier per stage.
+//     next stages are in flight while one stage is multiplied; one workgroup
+//     barrier per stage, placed before the stage's last 16-deep step so that
+//     the first fragments of the next stage are read while that step's MFMAs
+//     run.  Fragments are always read one 16-deep step ahead of their MFMAs.
 #pragma once
 
 #include "mfma_kernel.hpp"
@@ -51,12 +53,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// vmcnt(n * Q) for a run-time n in [0, 2]
+// vmcnt(n * Q) for a run-time n in [0, 3]
 template <int Q>
 __device__ __forceinline__ void wait_vmcnt_stages(int n) {
     if (n <= 0) wait_vmcnt<0>();
     else if (n == 1) wait_vmcnt<Q>();
-    else wait_vmcnt<2 * Q>();
+    else if (n == 2) wait_vmcnt<(2 * Q < 63 ? 2 * Q : 63)>();
+    else wait_vmcnt<(3 * Q < 63 ? 3 * Q : 63)>();
 }
 
 // LDS stages of 64 reduction values for a BM x BN tile: as many as fit in
@@ -274,39 +277,58 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         else return rb.read(st, (wn * WTN) / 32 + j, kk);
     };
 
+    u32x4 fa[2][FM], fb[2][FN];
+    // fragments of 16-deep step kk of the stage at `st` into register set `set`
+    auto read_step = [&](const BI_LDS char *st, int kk, int set) {
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
+        for (int i = 0; i < FM; ++i) fa[set][i] = frag_a(st, i, kk);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[set][j] = frag_b(st + SA, j, kk);
+    };
+    auto mfma_step_all = [&](int set) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<DT>(fb[set][j], fa[set][i], acc[i][j]);
+    };
+
+    // Schedule per stage s (buffer s % NS):
+    //   steps 0..2: read the fragments of step kk+1, then multiply step kk
+    //   (fragments are always read one step ahead of their MFMAs);
+    //   before step 3: wait until stage s+1 has landed, barrier (every wave is
+    //   done reading stage s, so its buffer takes stage s+NS), read step 0 of
+    //   stage s+1, then multiply step 3.
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
         if (s < nst) issue(s);
-
-    for (int s = 0; s < nst; ++s) {
-        // stage s has landed once only the later stages' copies are pending
-        const int later = nst - 1 - s < NS - 2 ? nst - 1 - s : NS - 2;
+    if (nst > 0) {
+        // issued: stages 0 .. min(NS-1, nst-1); wait for stage 0
+        const int later = nst - 1 < NS - 1 ? nst - 1 : NS - 1;
         wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
-        __syncthreads();  // every wave's share of stage s is in; stage s-1 is free
-        if (s + NS - 1 < nst) issue(s + NS - 1);
-
-        const BI_LDS char *ca = ring + (s % NS) * (SA + SB);
-        const BI_LDS char *cb = ca + SA;
-        u32x4 fa[2][FM], fb[2][FN];
+        __syncthreads();
+        read_step(ring, 0, 0);
+    }
+    for (int s = 0; s < nst; ++s) {
+        const BI_LDS char *cur = ring + (s % NS) * (SA + SB);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fa[0][i] = frag_a(ca, i, 0);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[0][j] = frag_b(cb, j, 0);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int cur = kk & 1;
-            if (kk + 1 < BK / 16) {
-#pragma unroll
-                for (int i = 0; i < FM; ++i) fa[cur ^ 1][i] = frag_a(ca, i, kk + 1);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) fb[cur ^ 1][j] = frag_b(cb, j, kk + 1);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = mfma_step<DT>(fb[cur][j], fa[cur][i], acc[i][j]);
+        for (int kk = 0; kk < BK / 16 - 1; ++kk) {
+            read_step(cur, kk + 1, (kk + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step_all(kk & 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (s + 1 < nst) {
+            // issued so far: stages 0 .. min(s+NS-1, nst-1); stage s+1 has
+            // landed once only the copies of the stages after it are pending
+            const int later = nst - 2 - s < NS - 2 ? nst - 2 - s : NS - 2;
+            wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
+            __syncthreads();
+            if (s + NS < nst) issue(s + NS);
+            read_step(ring + ((s + 1) % NS) * (SA + SB), 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step_all(1);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     write_tile<DT, EPI, WTM, WTN, FM, FN>(p, ti, acc, reinterpret_cast<char *>(lds_raw), lds_bias,

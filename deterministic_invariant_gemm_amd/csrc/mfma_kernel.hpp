@@ -634,6 +634,10 @@ template <> struct TileOf<12> { static constexpr int BM = 256, BN = 256, WGM = 4
 template <> struct TileOf<13> { static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 2; };
 template <> struct TileOf<14> { static constexpr int BM = 128, BN = 256, WGM = 2, WGN = 4; };
 template <> struct TileOf<15> { static constexpr int BM = 128, BN = 128, WGM = 2, WGN = 4; };
+// four waves stacked along M (used by the direct-A kernel)
+template <> struct TileOf<16> { static constexpr int BM = 256, BN = 192, WGM = 4, WGN = 1; };
+template <> struct TileOf<18> { static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 1; };
+template <> struct TileOf<19> { static constexpr int BM = 128, BN = 192, WGM = 4, WGN = 1; };
 
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>
 hipError_t launch_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {

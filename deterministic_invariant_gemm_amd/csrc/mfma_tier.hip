@@ -33,6 +33,12 @@ const TileShape *mfma_tile(int id) {
         {46, 64, 64},   {47, 128, 256}, {49, 128, 192}, {50, 256, 96},  {51, 256, 192},
         {52, 256, 256}, {53, 256, 128}, {54, 128, 256}, {55, 128, 128},
     };
+    // ids 60 + i: the direct-A kernel on base tile i (waves stacked along M)
+    static const TileShape da[] = {
+        {65, 128, 96}, {70, 256, 96}, {76, 256, 192}, {78, 256, 128}, {79, 128, 192},
+    };
+    for (const TileShape &s : da)
+        if (s.id == id) return &s;
     for (const TileShape &s : shapes)
         if (s.id == id) return &s;
     for (const TileShape &s : ad)
