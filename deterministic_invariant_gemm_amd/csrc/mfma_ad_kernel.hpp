@@ -98,9 +98,9 @@ __global__ __launch_bounds__(NT) void mfma_ad_kernel(MfmaArgs p) {
     const TileInfo ti = decode_tile<MODE, BM, BN>(p, t);
     if (ti.skip) return;
     const int64_t row0 = ti.row0, row_end = ti.row_end, col0 = ti.col0;
+    const float bias_v = fetch_bias<DT, EPI, BN>(p, col0, t);
     const int64_t r_begin = ti.r_begin, r_end = ti.r_end;
     const uint16_t *pb = static_cast<const uint16_t *>(p.b) + ti.b_off;
-    stage_bias<DT, EPI, BN>(p, col0, lds_bias, t);
 
     DirectA<FM, WTM> da;
     da.init(static_cast<const uint16_t *>(p.a), p.lda, row0, row_end, wm, lrow, lkg);
@@ -166,8 +166,8 @@ __global__ __launch_bounds__(NT) void mfma_ad_kernel(MfmaArgs p) {
     if (s < nst) slice(std::integral_constant<int, 0>{}, s);
 
     static_assert(SLAB_SLOTS <= LDS_SLOTS, "slabs fit");
-    write_tile<DT, EPI, WTM, WTN, FM, FN>(p, ti, acc, reinterpret_cast<char *>(lds_raw), lds_bias,
-                                          wave, wm, wn, lane);
+    write_tile<DT, EPI, WTM, WTN, FM, FN, BN>(p, ti, acc, reinterpret_cast<char *>(lds_raw),
+                                              lds_bias, bias_v, wave, wm, wn, lane);
 }
 
 template <int DT, bool BRC, int EPI, int MODE, int ID>

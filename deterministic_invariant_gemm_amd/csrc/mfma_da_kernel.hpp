@@ -98,8 +98,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_da_kernel(MfmaArgs p) {
     const TileInfo ti = decode_tile<MODE, BM, BN, 64 * NW>(p, t);
     if (ti.skip) return;
     const int64_t row0 = ti.row0, col0 = ti.col0;
+    const float bias_v = fetch_bias<DT, EPI, BN>(p, col0, t);
     const int64_t r_begin = ti.r_begin, r_end = ti.r_end;
-    stage_bias<DT, EPI, BN>(p, col0, lds_bias, t);
 
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void *>(p.a), (short)0, (int)p.a_bytes, 0x00020000);
@@ -203,8 +203,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_da_kernel(MfmaArgs p) {
     if (s < nst) stage(std::integral_constant<int, 0>{}, s);
     if (s + 1 < nst) stage(std::integral_constant<int, 1>{}, s + 1);
 
-    write_tile<DT, EPI, WTM, WTN, FM, FN>(p, ti, acc, reinterpret_cast<char *>(lds_raw), lds_bias,
-                                          wave, wm, 0, lane);
+    write_tile<DT, EPI, WTM, WTN, FM, FN, BN>(p, ti, acc, reinterpret_cast<char *>(lds_raw),
+                                              lds_bias, bias_v, wave, wm, 0, lane);
 }
 
 template <int DT, bool BRC, int EPI, int MODE, int ID>

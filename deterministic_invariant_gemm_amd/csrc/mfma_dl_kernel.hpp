@@ -29,9 +29,8 @@
 //     row are XOR-permuted so the 4 rows read together hit distinct banks.
 //   * A ring of NS LDS stages (as many as fit, at most 4): the copies of the
 //     next stages are in flight while one stage is multiplied; one workgroup
-//     barrier per stage, placed before the stage's last 16-deep step so that
-//     the first fragments of the next stage are read while that step's MFMAs
-//     run.  Fragments are always read one 16-deep step ahead of their MFMAs.
+//     barrier per stage.  MFMA fragments are read three 16-deep steps ahead of
+//     their use (a ring of four register sets), spread between the MFMAs.
 #pragma once
 
 #include "mfma_kernel.hpp"
@@ -230,8 +229,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     const TileInfo ti = decode_tile<MODE, BM, BN, 64 * NW>(p, t);
     if (ti.skip) return;
     const int64_t row0 = ti.row0, col0 = ti.col0;
+    const float bias_v = fetch_bias<DT, EPI, BN>(p, col0, t);
     const int64_t r_begin = ti.r_begin, r_end = ti.r_end;
-    stage_bias<DT, EPI, BN>(p, col0, lds_bias, t);
 
     const i32x4 rsa = make_rsrc(p.a, p.a_bytes);
     const i32x4 rsb = make_rsrc(static_cast<const uint16_t *>(p.b) + ti.b_off, p.b_bytes - 2 * ti.b_off);
@@ -277,8 +276,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         else return rb.read(st, (wn * WTN) / 32 + j, kk);
     };
 
-    u32x4 fa[2][FM], fb[2][FN];
-    // fragments of 16-deep step kk of the stage at `st` into register set `set`
+    // Fragment ring: set kk holds the fragments of 16-deep step kk of the
+    // stage being multiplied or of the next one.  Fragments are read three
+    // steps ahead of their MFMAs, interleaved with the MFMAs of the current step.
+    u32x4 fa[BK / 16][FM], fb[BK / 16][FN];
     auto read_step = [&](const BI_LDS char *st, int kk, int set) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[set][i] = frag_a(st, i, kk);
@@ -291,13 +292,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<DT>(fb[set][j], fa[set][i], acc[i][j]);
     };
+    // reads of one step spread between the MFMAs of another
+    constexpr int NREAD = FM * (A_RC ? 1 : 2) + FN * (B_RC ? 1 : 2);
+    constexpr int NMFMA = FM * FN;
+    constexpr int PER = (NREAD + NMFMA - 1) / NMFMA;
+    auto interleave = [&]() {
+#pragma unroll
+        for (int q = 0; q < NMFMA; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);  // then LDS reads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
-    // Schedule per stage s (buffer s % NS):
-    //   steps 0..2: read the fragments of step kk+1, then multiply step kk
-    //   (fragments are always read one step ahead of their MFMAs);
-    //   before step 3: wait until stage s+1 has landed, barrier (every wave is
-    //   done reading stage s, so its buffer takes stage s+NS), read step 0 of
-    //   stage s+1, then multiply step 3.
+    // Schedule per stage s (buffer s % NS), steps kk = 0..3:
+    //   kk = 0: read step 3 of stage s, multiply step 0; then wait until stage
+    //           s+1 has landed and barrier (every wave has read all of stage s,
+    //           so its buffer takes stage s+NS);
+    //   kk = 1..3: read step kk-1 of stage s+1, multiply step kk.
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         if (s < nst) issue(s);
@@ -306,33 +318,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         const int later = nst - 1 < NS - 1 ? nst - 1 : NS - 1;
         wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
         __syncthreads();
-        read_step(ring, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16 - 1; ++kk) read_step(ring, kk, kk);
+        __builtin_amdgcn_sched_barrier(0);
     }
     for (int s = 0; s < nst; ++s) {
         const BI_LDS char *cur = ring + (s % NS) * (SA + SB);
-#pragma unroll
-        for (int kk = 0; kk < BK / 16 - 1; ++kk) {
-            read_step(cur, kk + 1, (kk + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step_all(kk & 1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (s + 1 < nst) {
+        const BI_LDS char *nxt = ring + ((s + 1) % NS) * (SA + SB);
+        read_step(cur, BK / 16 - 1, BK / 16 - 1);
+        mfma_step_all(0);
+        interleave();
+        const bool more = s + 1 < nst;
+        if (more) {
             // issued so far: stages 0 .. min(s+NS-1, nst-1); stage s+1 has
             // landed once only the copies of the stages after it are pending
             const int later = nst - 2 - s < NS - 2 ? nst - 2 - s : NS - 2;
             wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
             __syncthreads();
             if (s + NS < nst) issue(s + NS);
-            read_step(ring + ((s + 1) % NS) * (SA + SB), 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        mfma_step_all(1);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 1; kk < BK / 16; ++kk) {
+            if (more) read_step(nxt, kk - 1, kk - 1);
+            mfma_step_all(kk);
+            interleave();
+        }
     }
 
-    write_tile<DT, EPI, WTM, WTN, FM, FN>(p, ti, acc, reinterpret_cast<char *>(lds_raw), lds_bias,
-                                          wave, wm, wn, lane);
+    write_tile<DT, EPI, WTM, WTN, FM, FN, BN>(p, ti, acc, reinterpret_cast<char *>(lds_raw),
+                                              lds_bias, bias_v, wave, wm, wn, lane);
 }
 
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>

@@ -379,17 +379,19 @@ __device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
     return ti;
 }
 
-// Stage the bias of this tile's columns into LDS as f32 (read after a barrier).
+// The bias of this tile's columns as f32: thread t < BN fetches column t
+// (clamped to the last column).  Fetched early into a register, written to
+// LDS by the epilogue (write_tile), so its latency hides behind the K loop.
 template <int DT, int EPI, int BN>
-__device__ __forceinline__ void stage_bias(const MfmaArgs &p, int64_t col0, float *lds_bias,
-                                           int t) {
+__device__ __forceinline__ float fetch_bias(const MfmaArgs &p, int64_t col0, int t) {
     if constexpr (EPI == EPI_ROUND) {
         if (p.bias && t < BN) {
             const int64_t j = col0 + t < p.cols ? col0 + t : p.cols - 1;
             const uint16_t b = static_cast<const uint16_t *>(p.bias)[j];
-            lds_bias[t] = DT == DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+            return DT == DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
         }
     }
+    return 0.0f;
 }
 
 // LDS bytes the epilogue needs (four waves, one 32-row slab each)
@@ -404,11 +406,10 @@ constexpr int slab_bytes() {
 // private LDS area (row-major), then writes it out as whole contiguous row
 // segments, 16 bytes per lane.  Starts with a workgroup barrier, after which
 // the stage buffers (`lds`) are free.
-template <int DT, int EPI, int WTM, int WTN, int FM, int FN>
+template <int DT, int EPI, int WTM, int WTN, int FM, int FN, int BN>
 __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti,
-                                           f32x16 (&acc)[FM][FN], char *lds,
-                                           const float *bias_l, int wave, int wm, int wn,
-                                           int lane) {
+                                           f32x16 (&acc)[FM][FN], char *lds, float *bias_l,
+                                           float bias_v, int wave, int wm, int wn, int lane) {
     const int lrow = lane & 31, lkg = lane >> 5;
     const int64_t row0 = ti.row0, row_end = ti.row_end, col0 = ti.col0;
     const int64_t chunk = ti.chunk, c_off = ti.c_off;
@@ -420,6 +421,10 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
     static_assert(ROWB % 16 == 0, "slab rows are whole 16-byte chunks");
     char *slab = lds + wave * 32 * ROWP;
     const bool vec_c = p.vec_c != 0;
+    if constexpr (EPI == EPI_ROUND) {
+        const int t = wave * 64 + lane;
+        if (p.bias && t < BN) bias_l[t] = bias_v;
+    }
     __syncthreads();  // bias visible; every wave done with the stage buffers
     // this lane's bias columns, read from LDS once for all row slabs
     f32x4 bias_r[FN][4];
@@ -475,7 +480,10 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
                 if (gi < row_end) {
                     OutT *dst = base + gi * ld + gj;
                     if (vec_c && gj + 16 / OSZ <= p.cols) {
-                        *reinterpret_cast<u32x4 *>(dst) = val;
+                        // streaming store: the output is not re-read by this
+                        // kernel, and lines written this way need no write-back
+                        // when the kernel ends
+                        __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(dst));
                     } else {
                         const OutT *e = reinterpret_cast<const OutT *>(&val);
 #pragma unroll
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm_kernel(MfmaArgs p) {
     const uint16_t *pa = static_cast<const uint16_t *>(p.a);
     const uint16_t *pb = static_cast<const uint16_t *>(p.b) + ti.b_off;
 
-    stage_bias<DT, EPI, BN>(p, col0, lds_bias, t);
+    const float bias_v = fetch_bias<DT, EPI, BN>(p, col0, t);
 
     Stage<BM, A_RC, NTH> sa;
     Stage<BN, B_RC, NTH> sb;
@@ -605,8 +613,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm_kernel(MfmaArgs p) {
     }
 
     static_assert(slab_bytes<EPI, WTN, NW>() <= 2 * KG * (BM + BN) * 16, "slabs fit in the stage buffers");
-    write_tile<DT, EPI, WTM, WTN, FM, FN>(p, ti, acc, reinterpret_cast<char *>(lds_raw), lds_bias,
-                                          wave, wm, wn, lane);
+    write_tile<DT, EPI, WTM, WTN, FM, FN, BN>(p, ti, acc, reinterpret_cast<char *>(lds_raw),
+                                              lds_bias, bias_v, wave, wm, wn, lane);
 }
 
 }  // namespace mfma
