@@ -107,7 +107,8 @@ int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.ch
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
 // Operand extents for the direct-load kernels, and the tile they may use: the
-// direct-load (ids 40 + base) and direct-A (ids 60 + base) families need
+// direct-load (ids 40 + base), direct-A (ids 60 + base) and ping-pong (ids 80 +
+// base) families need
 // 16-byte-aligned rows whose length is a multiple of 8 elements and operands
 // below 2^30 bytes; otherwise the base tile of the register-staged family runs
 // (same bits).
@@ -118,7 +119,7 @@ int direct_tile(MfmaArgs &a, int tile, int64_t a_bytes, int64_t b_bytes) {
     if (tile < 40) return tile;
     const bool ok = a.vec_a && a.vec_b && a_bytes <= kDirectMaxBytes && b_bytes <= kDirectMaxBytes;
     if (ok) return tile;
-    return tile >= 60 ? tile - 60 : tile - 40;
+    return tile >= 80 ? tile - 80 : tile >= 60 ? tile - 60 : tile - 40;
 }
 
 }  // namespace

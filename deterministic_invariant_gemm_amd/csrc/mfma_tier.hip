@@ -39,6 +39,12 @@ const TileShape *mfma_tile(int id) {
     };
     for (const TileShape &s : da)
         if (s.id == id) return &s;
+    // ids 80 + i: the eight-wave ping-pong kernel on base tile i
+    static const TileShape pp[] = {
+        {91, 256, 192}, {92, 256, 256}, {93, 256, 128}, {94, 128, 256}, {95, 128, 128},
+    };
+    for (const TileShape &s : pp)
+        if (s.id == id) return &s;
     for (const TileShape &s : shapes)
         if (s.id == id) return &s;
     for (const TileShape &s : ad)

@@ -1,7 +1,8 @@
-"""Every tile shape of the MFMA tier -- in all four kernel families (operands
+"""Every tile shape of the MFMA tier -- in all five kernel families (operands
 staged through registers into LDS; A read directly into registers; both
 operands copied straight from global memory into LDS; A loaded into registers
-with B copied into LDS) -- must give the same bits for
+with B copied into LDS; eight waves in two alternating groups) -- must give the
+same bits for
 the same problem: the per-element MFMA sequence does not depend on the tile.
 Tiles are forced with the tuning hook tc = 16 + tile id; ids that an op does
 not instantiate are rejected with BI_ERR_HIP before any launch and skipped."""
@@ -16,7 +17,7 @@ from parity import check, dev, empty, host
 
 pytestmark = pytest.mark.gpu
 
-TILE_IDS = list(range(1, 20)) + list(range(21, 31)) + list(range(41, 56)) + [65, 70, 76, 78, 79]
+TILE_IDS = list(range(1, 20)) + list(range(21, 31)) + list(range(41, 56)) + [65, 70, 76, 78, 79, 91, 92, 93, 94, 95]
 
 
 def run_all(fn):
