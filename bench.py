@@ -92,38 +92,79 @@ def cpu_model() -> str:
     return "unknown"
 
 
-class Timer:
-    """HIP events recorded on the launch stream around every call of one op."""
+class HipEvents:
+    """Timing events created with hipEventDisableSystemFence: recording one
+    enqueues a timestamp without the system-scope cache writeback and
+    invalidation a default event performs, so the events do not slow the
+    kernels they bracket (default events add several microseconds per record
+    on this GPU).  Elapsed times are read only after a device-wide
+    synchronization."""
 
-    def __init__(self, torch, stream):
-        self.torch, self.stream, self.pairs = torch, stream, []
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
-    def run(self, fn):
-        e0 = self.torch.cuda.Event(enable_timing=True)
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e0.record(self.stream)
-        fn()
-        e1.record(self.stream)
-        self.pairs.append((e0, e1))
+    def __init__(self):
+        import ctypes
+        # the HIP runtime torch has already loaded (same soname)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.ct = ctypes
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
 
-    def mean_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(len(self.pairs), 1)
+    def new(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+        self.made.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def ms(self, e0, e1):
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), e0, e1)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return out.value
+
+    def close(self):
+        for ev in self.made:
+            self.hip.hipEventDestroy(ev)
+        self.made = []
 
 
-def timed_steps(torch, stream, ops, steps, warmup):
-    """ops: list of (name, callable).  Returns (ms_per_step, {name: mean ms})."""
+def timed_steps(torch, ops, steps, warmup):
+    """ops: list of (name, fn(stream)); one step runs every op once, in order,
+    through the C ABI.  Every op of every timed step is bracketed by two
+    timing events recorded on the stream it is launched on (created before
+    timing starts).  Returns (wall ms per step, {name: mean event ms per call})."""
+    s = torch.cuda.current_stream()
     for _ in range(warmup):
         for _, fn in ops:
-            fn()
+            fn(s)
+    hev = HipEvents()
+    ev = {name: [(hev.new(), hev.new()) for _ in range(steps)] for name, _ in ops}
     torch.cuda.synchronize()
-    timers = {name: Timer(torch, stream) for name, _ in ops}
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
         for name, fn in ops:
-            timers[name].run(fn)
+            e0, e1 = ev[name][i]
+            hev.record(e0, s)
+            fn(s)
+            hev.record(e1, s)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return wall, {name: t.mean_ms() for name, t in timers.items()}
+    mean = {name: sum(hev.ms(a, b) for a, b in pairs) / max(len(pairs), 1)
+            for name, pairs in ev.items()}
+    hev.close()
+    return wall, mean
 
 
 def cpu_baseline_linear(d, target_s):
@@ -167,14 +208,13 @@ def bench_linear(args, torch, dig, synth):
     dw = torch.empty((k, n), dtype=torch.int16, device="cuda")
     wsb = dig.bi_backward_dw_workspace_bytes(m, k, n, dt, 1)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
-    s = torch.cuda.current_stream()
     ops = [
-        ("fwd", lambda: dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, s, 1))),
-        ("dX", lambda: dig.check(dig.bi_backward_dx(dx, dy, w, m, k, n, dt, s, 1))),
-        ("dW", lambda: dig.check(dig.bi_backward_dw(dw, x, dy, m, k, n, dt,
-                                                    ws if wsb else None, wsb, s, 1))),
+        ("fwd", lambda s: dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, s, 1))),
+        ("dX", lambda s: dig.check(dig.bi_backward_dx(dx, dy, w, m, k, n, dt, s, 1))),
+        ("dW", lambda s: dig.check(dig.bi_backward_dw(dw, x, dy, m, k, n, dt,
+                                                      ws if wsb else None, wsb, s, 1))),
     ]
-    ms, per = timed_steps(torch, s, ops, args.steps, args.warmup)
+    ms, per = timed_steps(torch, ops, args.steps, args.warmup)
     flop = 2.0 * m * k * n
     # algorithmic bytes per launch: each operand read once, the output written once
     bytes_ = {"fwd": 2 * (m * k + k * n + n + m * n), "dX": 2 * (m * n + k * n + m * k),
@@ -217,10 +257,9 @@ def bench_fp8(args, torch, dig, synth):
     db = torch.tensor([float(d["db"])], dtype=torch.float32, device="cuda")
     y = torch.empty((m, n), dtype=torch.int16, device="cuda")
     y16 = torch.empty((16, n), dtype=torch.int16, device="cuda")
-    s = torch.cuda.current_stream()
-    ops = [("fp8_m8192", lambda: dig.check(dig.bi_fp8_mm(y, a, bt, da, db, m, k, n, s, 1))),
-           ("fp8_m16", lambda: dig.check(dig.bi_fp8_mm(y16, a, bt, da, db, 16, k, n, s, 1)))]
-    ms, per = timed_steps(torch, s, ops, args.steps, args.warmup)
+    ops = [("fp8_m8192", lambda s: dig.check(dig.bi_fp8_mm(y, a, bt, da, db, m, k, n, s, 1))),
+           ("fp8_m16", lambda s: dig.check(dig.bi_fp8_mm(y16, a, bt, da, db, 16, k, n, s, 1)))]
+    ms, per = timed_steps(torch, ops, args.steps, args.warmup)
     flop = 2.0 * m * k * n
     ach = flop / (per["fp8_m8192"] * 1e-3) / 1e12
     b16 = 16 * k + n * k + 16 * n * 2
@@ -250,13 +289,12 @@ def bench_grouped(args, torch, dig, synth):
     y = torch.empty((m, n), dtype=torch.int16, device="cuda")
     di = torch.empty((m, k), dtype=torch.int16, device="cuda")
     dwt = torch.empty((e, n, k), dtype=torch.float32, device="cuda")
-    s = torch.cuda.current_stream()
     bt = synth.BF16
-    ops = [("grouped_fwd", lambda: dig.check(dig.bi_grouped_nt(y, inp, w, ids, off, m, k, n, e,
-                                                               bt, s, 1))),
-           ("grouped_bwd", lambda: dig.check(dig.bi_grouped_nt_backward(
+    ops = [("grouped_fwd", lambda s: dig.check(dig.bi_grouped_nt(y, inp, w, ids, off, m, k, n, e,
+                                                                 bt, s, 1))),
+           ("grouped_bwd", lambda s: dig.check(dig.bi_grouped_nt_backward(
                di, dwt, inp, w, dy, ids, off, m, k, n, e, bt, s, 1)))]
-    ms, per = timed_steps(torch, s, ops, args.steps, args.warmup)
+    ms, per = timed_steps(torch, ops, args.steps, args.warmup)
     valid = int(d["offsets"][e])
     flop = 2.0 * valid * k * n
     ach = flop / (per["grouped_fwd"] * 1e-3) / 1e12
@@ -281,13 +319,12 @@ def bench_sweep(args, torch, dig, synth):
     dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
     x, w = dev(d["x"]), dev(d["w"])
     y = torch.empty((m, n), dtype=torch.int16, device="cuda")
-    s = torch.cuda.current_stream()
     bt = synth.BF16
     res = {}
     for mp in (1, 3, 17, 128, 1000, 8192):
-        ops = [(f"m{mp}", lambda mp=mp: dig.check(dig.bi_forward(y, x, w, None, mp, k, n, bt, s,
-                                                                 1)))]
-        _, per = timed_steps(torch, s, ops, max(args.steps // 4, 10), 5)
+        ops = [(f"m{mp}", lambda s, mp=mp: dig.check(dig.bi_forward(y, x, w, None, mp, k, n, bt,
+                                                                    s, 1)))]
+        _, per = timed_steps(torch, ops, max(args.steps // 4, 10), 5)
         us = per[f"m{mp}"] * 1e3
         byt = 2 * (mp * k + k * n + mp * n)
         res[mp] = {"us": round(us, 2), "tflops": round(2.0 * mp * k * n / (us * 1e-6) / 1e12, 2),
@@ -311,8 +348,7 @@ def bench_copy(args, torch, dig, synth):
     n = 256 * 1024 * 1024
     src = torch.ones(n, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
-    s = torch.cuda.current_stream()
-    ms, per = timed_steps(torch, s, [("copy", lambda: dst.copy_(src))], args.steps, args.warmup)
+    ms, per = timed_steps(torch, [("copy", lambda s: dst.copy_(src))], args.steps, args.warmup)
     nbytes = 2 * 2 * n
     gbps = nbytes / (per["copy"] * 1e-3) / 1e9
     return {"metric": "device copy GB/s (read + write)", "value": round(gbps, 1), "unit": "GB/s",

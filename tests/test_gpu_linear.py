@@ -274,3 +274,33 @@ def test_k_zero_gives_rounded_bias_and_m_zero_dw_is_zero():
         dig.check(dig.bi_backward_dw(dw, x, x, 0, 70, 96, dt, None, 0,
                                      torch.cuda.current_stream(), tc))
         assert np.all(host(dw, np.uint16) == 0)
+
+
+@pytest.mark.parametrize("mkn", [(4096, 768, 3072), (2500, 96, 200)], ids=lambda s: "x".join(map(str, s)))
+def test_graph_replay_matches_eager(mkn):
+    """The trio captured in HIP graphs (as the benchmark replays it) gives the
+    eager bytes on every replay; outputs are overwritten with garbage by eager
+    work between replays.  The second shape uses the chunked dW workspace."""
+    m, k, n = mkn
+    d = synth.linear(m, k, n, synth.BF16, seed=31, sigma_w=0.05)
+    L = Linear(d)
+    ref = (digest(L.forward(1)), digest(L.dx(1)), digest(L.dw(1)))
+    y, dx, dw = empty((m, n), np.uint16), empty((m, k), np.uint16), empty((k, n), np.uint16)
+    nbytes = dig.bi_backward_dw_workspace_bytes(m, k, n, L.dt, 1)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        dig.check(dig.bi_forward(y, L.x, L.w, L.b, m, k, n, L.dt, cs, 1))
+        dig.check(dig.bi_backward_dx(dx, L.dy, L.w, m, k, n, L.dt, cs, 1))
+        dig.check(dig.bi_backward_dw(dw, L.x, L.dy, m, k, n, L.dt, ws if nbytes else None,
+                                     nbytes, cs, 1))
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (y, dx, dw, ws):
+            t.fill_(rep + 7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert (digest(y), digest(dx), digest(dw)) == ref, rep
