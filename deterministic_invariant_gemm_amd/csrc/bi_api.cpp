@@ -54,8 +54,9 @@ bool mfma_eligible(int op, int dt, int tc, int64_t k, int64_t n) {
 // for forward / fp8 / grouped forward, K for dX / grouped dinput; dW tiles its
 // [K, N] output).  Every tile issues the same MFMA sequence per element, so
 // this choice affects speed only.  Ids 40 + i are the direct-load kernel on
-// shape i (used when operands are aligned, see direct_tile); the fp8 op has
-// its own kernel and takes the base ids.
+// shape i and 100 + i the same with its copies spread between MFMAs (both used
+// when operands are aligned, see direct_tile); the fp8 op has its own kernel
+// and takes the base ids.
 int pick_tile(int op, int64_t k, int64_t n) {
     const int64_t cols = (op == OP_DX || op == OP_GDIN) ? k : n;
     switch (op) {
@@ -68,10 +69,13 @@ int pick_tile(int op, int64_t k, int64_t n) {
         if (cols >= 2048) return 52;                                           // 256x256, 8 waves
         return cols >= 128 ? 44 : 46;
     case OP_DX:
-        if (cols % 96 == 0 && cols <= 1536) return 45;  // 128x96
-        return cols >= 128 ? 44 : 46;
+        // 128x128, eight waves, copies spread between MFMAs
+        return cols >= 128 ? 115 : 46;
     case OP_DW:
-        return (k >= 128 && n >= 128) ? 55 : 46;  // 128x128 (8 waves) / 64x64
+        // 96x96 (three waves): 256 tiles of a 768 x 3072 output; larger outputs
+        // fill the chip with 128x128 (eight waves, copies spread)
+        if (k >= 128 && n >= 128) return k * n <= (int64_t)256 * 96 * 96 ? 48 : 115;
+        return 46;
     case OP_GFWD: case OP_GDIN: case OP_GDW:
         return 41;  // 256x256
     }
@@ -106,20 +110,33 @@ int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.ch
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
-// Operand extents for the direct-load kernels, and the tile they may use: the
-// direct-load (ids 40 + base), direct-A (ids 60 + base) and ping-pong (ids 80 +
-// base) families need
-// 16-byte-aligned rows whose length is a multiple of 8 elements and operands
-// below 2^30 bytes; otherwise the base tile of the register-staged family runs
-// (same bits).
+// The tile that runs, its operand extents and its grid.  The direct-load (ids
+// 40 + base), direct-A (ids 60 + base) and ping-pong (ids 80 + base) families
+// need 16-byte-aligned rows whose length is a multiple of 8 elements and
+// operands below 2^30 bytes; otherwise the register-staged kernel of the base
+// shape runs, or 128x128 where that family has no such shape (same bits
+// either way).  The grid (tiles_i or seg_tiles, and tiles_j, over rows x
+// cols) is set here from the shape that actually runs.
 constexpr int64_t kDirectMaxBytes = (int64_t)1 << 30;
 int direct_tile(MfmaArgs &a, int tile, int64_t a_bytes, int64_t b_bytes) {
     a.a_bytes = a_bytes;
     a.b_bytes = b_bytes;
-    if (tile < 40) return tile;
-    const bool ok = a.vec_a && a.vec_b && a_bytes <= kDirectMaxBytes && b_bytes <= kDirectMaxBytes;
-    if (ok) return tile;
-    return tile >= 80 ? tile - 80 : tile >= 60 ? tile - 60 : tile - 40;
+    int t = tile;
+    if (tile >= 40) {
+        const bool ok =
+            a.vec_a && a.vec_b && a_bytes <= kDirectMaxBytes && b_bytes <= kDirectMaxBytes;
+        if (!ok) {
+            const int base = tile >= 100 ? tile - 100
+                             : tile >= 80 ? tile - 80
+                             : tile >= 60 ? tile - 60 : tile - 40;
+            t = mfma_tile(base) ? base : 4;
+        }
+    }
+    const TileShape *ts = mfma_tile(t);
+    if (a.offsets) a.seg_tiles = cdiv(a.rows, ts->bm) + a.n_experts;
+    else a.tiles_i = cdiv(a.rows, ts->bm);
+    a.tiles_j = cdiv(a.cols, ts->bn);
+    return t;
 }
 
 }  // namespace
@@ -167,11 +184,9 @@ int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t 
         a.tiles_i = cdiv(m, 64); a.tiles_j = cdiv(n, 64);
         return hip_status(launch_scalar_gemm(a, dtype, dtype, 0, stream));
     }
-    const TileShape *ts = mfma_tile(pl.tile);
     MfmaArgs a{};
     a.a = x; a.lda = k; a.b = w; a.ldb = n; a.c = y; a.ldc = n; a.bias = bias;
     a.rows = m; a.cols = n; a.red = k; a.chunk = kNoSplit; a.nchunks = 1;
-    a.tiles_i = cdiv(m, ts->bm); a.tiles_j = cdiv(n, ts->bn);
     a.vec_a = aligned16(x) && k % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(y) && n % 4 == 0;
@@ -197,11 +212,9 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
         a.tiles_i = cdiv(m, 64); a.tiles_j = cdiv(k, 64);
         return hip_status(launch_scalar_gemm(a, dtype, dtype, 0, stream));
     }
-    const TileShape *ts = mfma_tile(pl.tile);
     MfmaArgs a{};
     a.a = dy; a.lda = n; a.b = w; a.ldb = n; a.c = dx; a.ldc = k;
     a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
-    a.tiles_i = cdiv(m, ts->bm); a.tiles_j = cdiv(k, ts->bn);
     a.vec_a = aligned16(dy) && n % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(dx) && k % 4 == 0;
@@ -242,12 +255,10 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
         a.tiles_i = cdiv(k, 64); a.tiles_j = cdiv(n, 64);
         e = launch_scalar_gemm(a, dtype, epi ? BI_F32 : dtype, epi, stream);
     } else {
-        const TileShape *ts = mfma_tile(pl.tile);
         MfmaArgs a{};
         a.a = x; a.lda = k; a.b = dy; a.ldb = n; a.c = dw; a.ldc = n;
         a.ws = static_cast<float *>(workspace);
         a.rows = k; a.cols = n; a.red = m; a.chunk = pl.chunk; a.nchunks = chunks;
-        a.tiles_i = cdiv(k, ts->bm); a.tiles_j = cdiv(n, ts->bn);
         a.vec_a = aligned16(x) && k % 8 == 0;
         a.vec_b = aligned16(dy) && n % 8 == 0;
         a.vec_c = epi ? (aligned16(workspace) && n % 4 == 0) : (aligned8(dw) && n % 4 == 0);
@@ -317,13 +328,10 @@ int bi_grouped_nt(void *y, const void *input, const void *weights, const uint32_
         return hip_status(launch_grouped_scalar(g, 0, dtype, stream));
     }
     if (!offsets) return BI_ERR_NULL;
-    const TileShape *ts = mfma_tile(pl.tile);
     MfmaArgs a{};
     a.a = input; a.lda = k; a.b = weights; a.ldb = k; a.c = y; a.ldc = n;
     a.rows = m; a.cols = n; a.red = k; a.chunk = kNoSplit; a.nchunks = 1;
-    a.tiles_j = cdiv(n, ts->bn);
     a.offsets = offsets; a.n_experts = e; a.b_expert_stride = n * k;
-    a.seg_tiles = cdiv(m, ts->bm) + e;
     a.vec_a = aligned16(input) && k % 8 == 0;
     a.vec_b = aligned16(weights) && k % 8 == 0;
     a.vec_c = aligned8(y) && n % 4 == 0;
@@ -349,13 +357,10 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
             g.out = dinput; g.m = m; g.k = k; g.n = n; g.e = e;
             er = launch_grouped_scalar(g, 1, dtype, stream);
         } else {
-            const TileShape *ts = mfma_tile(pl.tile);
             MfmaArgs a{};
             a.a = grad_out; a.lda = n; a.b = weights; a.ldb = k; a.c = dinput; a.ldc = k;
             a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
-            a.tiles_j = cdiv(k, ts->bn);
             a.offsets = offsets; a.n_experts = e; a.b_expert_stride = n * k;
-            a.seg_tiles = cdiv(m, ts->bm) + e;
             a.vec_a = aligned16(grad_out) && n % 8 == 0;
             a.vec_b = aligned16(weights) && k % 8 == 0;
             a.vec_c = aligned8(dinput) && k % 4 == 0;
@@ -372,11 +377,9 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
         g.m = m; g.k = k; g.n = n; g.e = e;
         return hip_status(launch_grouped_scalar(g, 2, dtype, stream));
     }
-    const TileShape *ts = mfma_tile(pw.tile);
     MfmaArgs a{};
     a.a = grad_out; a.lda = n; a.b = input; a.ldb = k; a.c = dweights; a.ldc = k;
     a.rows = n; a.cols = k; a.red = m; a.chunk = kNoSplit; a.nchunks = 1;
-    a.tiles_i = cdiv(n, ts->bm); a.tiles_j = cdiv(k, ts->bn);
     a.red_offsets = offsets; a.n_experts = e; a.c_expert_stride = n * k;
     a.vec_a = aligned16(grad_out) && n % 8 == 0;
     a.vec_b = aligned16(input) && k % 8 == 0;

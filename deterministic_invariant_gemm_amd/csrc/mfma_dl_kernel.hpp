@@ -104,12 +104,17 @@ __device__ __forceinline__ int rc_xor(int row) { return (row ^ ((row >> 3) & 1))
 // 64 bytes (32 lanes) from each of 4 consecutive reduction rows; the XOR
 // spreads those rows over distinct banks for either grouping, and it keeps
 // the chunk inside the row (R/8 chunks: a multiple of 16 when R % 128 == 0,
-// of 8 otherwise).  Depends on k & 3 only.
+// of 8 when R % 64 == 0).  When R is an odd multiple of 32 the row pitch is an
+// odd multiple of 64 bytes, so 4 consecutive rows already start in the 4
+// distinct 64-byte quarters of the 256-byte bank space: no XOR.  Depends on
+// k & 3 only.
 template <int R>
 __device__ __forceinline__ int rs_xor(int k) {
-    static_assert(R % 64 == 0, "row-contiguous tiles need a multiple of 64 columns");
+    static_assert(R % 32 == 0, "row-contiguous tiles need a multiple of 32 columns");
     const int t = k & 3;
-    return R % 128 == 0 ? 4 * t + 2 * (t >> 1) : 2 * t;
+    if constexpr (R % 128 == 0) return 4 * t + 2 * (t >> 1);
+    else if constexpr (R % 64 == 0) return 2 * t;
+    else return 0;
 }
 
 // Global -> LDS copy of one operand tile per 64-deep stage: R/8 instructions
@@ -152,6 +157,14 @@ struct DLoad {
             if (MASK && kin[p] >= rem) o = kOutOfRange;
             lds_dma16(rs, o, (uint32_t)reinterpret_cast<uintptr_t>(stage + 1024 * (wave + NW * p)));
         }
+    }
+
+    // copy p (< NQ) of stage s alone, masked as above
+    __device__ __forceinline__ void issue_one(i32x4 rs, BI_LDS char *stage, int s, int64_t rem,
+                                              int wave, int p) const {
+        uint32_t o = off[p] + (uint32_t)s * sstride;
+        if (kin[p] >= rem) o = kOutOfRange;
+        lds_dma16(rs, o, (uint32_t)reinterpret_cast<uintptr_t>(stage + 1024 * (wave + NW * p)));
     }
 };
 
@@ -207,7 +220,8 @@ struct FragOf<true, R> {
     using type = RcFrag;
 };
 
-template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE>
+template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
+          bool SPREAD>
 __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -217,6 +231,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     constexpr int NS = dl_stages(BM, BN);
     static_assert(NS >= 2 && NS <= 4, "two to four stages");
     static_assert(slab_bytes<EPI, WTN, NW>() <= NS * (SA + SB), "epilogue slabs fit in the stages");
+    static_assert(EPI != EPI_ROUND || BN <= 64 * NW, "one thread per bias column");
 
     // NS stages of [A | B]; reused by the epilogue
     __shared__ __align__(1024) char lds_raw[NS * (SA + SB)];
@@ -305,11 +320,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    // SPREAD: the copies of stage s+NS are issued one or a few at a time
+    // between the MFMAs of steps 1..3 of stage s instead of all at once right
+    // after the barrier (a burst of copy instructions can hold up the wave's
+    // MFMA issue while the memory pipeline takes them in).
+    constexpr int NC = LA::NQ + LB::NQ;                 // copies per wave per stage
+    constexpr int NSLOT = (BK / 16 - 1) * NMFMA;         // MFMAs of steps 1..3
+    constexpr int CPS = (NC + NSLOT - 1) / NSLOT;        // copies after each of them
+    auto copy_one = [&](int cs, int c) {
+        BI_LDS char *da = ring + (cs % NS) * (SA + SB);
+        const int64_t rem = red - (int64_t)BK * cs;
+        if (c < LA::NQ) la.issue_one(rsa, da, cs, rem, wave, c);
+        else lb.issue_one(rsb, da + SA, cs, rem, wave, c - LA::NQ);
+    };
+
     // Schedule per stage s (buffer s % NS), steps kk = 0..3:
     //   kk = 0: read step 3 of stage s, multiply step 0; then wait until stage
     //           s+1 has landed and barrier (every wave has read all of stage s,
     //           so its buffer takes stage s+NS);
-    //   kk = 1..3: read step kk-1 of stage s+1, multiply step kk.
+    //   kk = 1..3: read step kk-1 of stage s+1, multiply step kk (SPREAD: per
+    //           MFMA of step kk, its share of those reads, the MFMA, its share
+    //           of the copies of stage s+NS).
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         if (s < nst) issue(s);
@@ -335,14 +366,40 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
             const int later = nst - 2 - s < NS - 2 ? nst - 2 - s : NS - 2;
             wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
             __syncthreads();
-            if (s + NS < nst) issue(s + NS);
+            if (!SPREAD && s + NS < nst) issue(s + NS);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!SPREAD) {
+#pragma unroll
+            for (int kk = 1; kk < BK / 16; ++kk) {
+                if (more) read_step(nxt, kk - 1, kk - 1);
+                mfma_step_all(kk);
+                interleave();
+            }
+            continue;
+        }
+        const bool copies = s + NS < nst;
 #pragma unroll
         for (int kk = 1; kk < BK / 16; ++kk) {
-            if (more) read_step(nxt, kk - 1, kk - 1);
-            mfma_step_all(kk);
-            interleave();
+#pragma unroll
+            for (int q = 0; q < NMFMA; ++q) {
+                if (more) {
+#pragma unroll
+                    for (int f = q; f < FM + FN; f += NMFMA) {
+                        if (f < FM) fa[kk - 1][f] = frag_a(nxt, f, kk - 1);
+                        else fb[kk - 1][f - FM] = frag_b(nxt + SA, f - FM, kk - 1);
+                    }
+                }
+                acc[q / FN][q % FN] =
+                    mfma_step<DT>(fb[kk][q % FN], fa[kk][q / FN], acc[q / FN][q % FN]);
+                if (copies) {
+                    const int c0 = ((kk - 1) * NMFMA + q) * CPS;
+#pragma unroll
+                    for (int c = c0; c < c0 + CPS; ++c)
+                        if (c < NC) copy_one(s + NS, c);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
@@ -350,11 +407,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
                                               lds_bias, bias_v, wave, wm, wn, lane);
 }
 
-template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>
+template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID, bool SPREAD>
 hipError_t launch_dl_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
     using T = TileOf<ID>;
-    hipLaunchKernelGGL((mfma_dl_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE>),
-                       dim3(grid), dim3(64 * T::WGM * T::WGN), 0, s, p);
+    hipLaunchKernelGGL(
+        (mfma_dl_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE, SPREAD>),
+        dim3(grid), dim3(64 * T::WGM * T::WGN), 0, s, p);
     return hipGetLastError();
 }
 
@@ -362,8 +420,20 @@ hipError_t launch_dl_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int... IDS>
 hipError_t launch_dl_among(const MfmaArgs &p, int tile_id, int64_t grid, hipStream_t s) {
     hipError_t r = hipErrorInvalidValue;
-    ((tile_id == 40 + IDS ? (void)(r = launch_dl_tile<DT, ARC, BRC, EPI, MODE, IDS>(p, grid, s))
-                          : (void)0),
+    ((tile_id == 40 + IDS
+          ? (void)(r = launch_dl_tile<DT, ARC, BRC, EPI, MODE, IDS, false>(p, grid, s))
+          : (void)0),
+     ...);
+    return r;
+}
+
+// tile ids 100 + base id: the same kernel with the copies spread between MFMAs
+template <int DT, bool ARC, bool BRC, int EPI, int MODE, int... IDS>
+hipError_t launch_dls_among(const MfmaArgs &p, int tile_id, int64_t grid, hipStream_t s) {
+    hipError_t r = hipErrorInvalidValue;
+    ((tile_id == 100 + IDS
+          ? (void)(r = launch_dl_tile<DT, ARC, BRC, EPI, MODE, IDS, true>(p, grid, s))
+          : (void)0),
      ...);
     return r;
 }

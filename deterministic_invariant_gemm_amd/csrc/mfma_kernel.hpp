@@ -634,6 +634,8 @@ template <> struct TileOf<4> { static constexpr int BM = 128, BN = 128, WGM = 2,
 template <> struct TileOf<5> { static constexpr int BM = 128, BN = 96, WGM = 4, WGN = 1; };
 template <> struct TileOf<6> { static constexpr int BM = 64, BN = 64, WGM = 2, WGN = 2; };
 template <> struct TileOf<7> { static constexpr int BM = 128, BN = 256, WGM = 2, WGN = 2; };
+// three waves (direct-load kernel only): 256 tiles of a 768 x 3072 output
+template <> struct TileOf<8> { static constexpr int BM = 96, BN = 96, WGM = 3, WGN = 1; };
 template <> struct TileOf<9> { static constexpr int BM = 128, BN = 192, WGM = 2, WGN = 2; };
 template <> struct TileOf<10> { static constexpr int BM = 256, BN = 96, WGM = 4, WGN = 1; };
 // eight waves, two per SIMD
@@ -646,6 +648,7 @@ template <> struct TileOf<15> { static constexpr int BM = 128, BN = 128, WGM = 2
 template <> struct TileOf<16> { static constexpr int BM = 256, BN = 192, WGM = 4, WGN = 1; };
 template <> struct TileOf<18> { static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 1; };
 template <> struct TileOf<19> { static constexpr int BM = 128, BN = 192, WGM = 4, WGN = 1; };
+template <> struct TileOf<17> { static constexpr int BM = 96, BN = 96, WGM = 1, WGN = 3; };
 
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>
 hipError_t launch_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {

@@ -17,7 +17,8 @@ from parity import check, dev, empty, host
 
 pytestmark = pytest.mark.gpu
 
-TILE_IDS = list(range(1, 20)) + list(range(21, 31)) + list(range(41, 56)) + [65, 70, 76, 78, 79, 91, 92, 93, 94, 95]
+TILE_IDS = (list(range(1, 20)) + list(range(21, 31)) + list(range(41, 58))
+            + [65, 70, 76, 78, 79, 91, 92, 93, 94, 95, 105, 108, 111, 115])
 
 
 def run_all(fn):
