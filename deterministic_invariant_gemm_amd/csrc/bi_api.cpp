@@ -55,15 +55,15 @@ bool mfma_eligible(int op, int dt, int tc, int64_t k, int64_t n) {
 // [K, N] output).  Every tile issues the same MFMA sequence per element, so
 // this choice affects speed only.  Ids 40 + i are the direct-load kernel on
 // shape i and 100 + i the same with its copies spread between MFMAs (both used
-// when operands are aligned, see direct_tile); the fp8 op has its own kernel
-// and takes the base ids.
+// when operands are aligned, see direct_tile; fp8 otherwise runs its
+// register-staged kernel on 256x256, 128x128 or 64x64).
 int pick_tile(int op, int64_t k, int64_t n) {
     const int64_t cols = (op == OP_DX || op == OP_GDIN) ? k : n;
     switch (op) {
     case OP_FP8:
-        if (cols >= 2048 && cols % 192 == 0 && cols / 192 <= 16) return 2;  // 256x192
-        if (cols >= 2048) return 1;                                           // 256x256
-        return cols >= 128 ? 4 : 6;
+        // 256x256, eight waves, copies spread; 128x128 eight waves below
+        if (cols >= 2048) return 112;
+        return cols >= 128 ? 115 : 46;
     case OP_FWD:
         if (cols >= 2048 && cols % 192 == 0 && cols / 192 <= 16) return 51;  // 256x192, 8 waves
         if (cols >= 2048) return 52;                                           // 256x256, 8 waves
@@ -76,8 +76,12 @@ int pick_tile(int op, int64_t k, int64_t n) {
         // fill the chip with 128x128 (eight waves, copies spread)
         if (k >= 128 && n >= 128) return k * n <= (int64_t)256 * 96 * 96 ? 48 : 115;
         return 46;
-    case OP_GFWD: case OP_GDIN: case OP_GDW:
-        return 41;  // 256x256
+    case OP_GFWD: case OP_GDIN:
+        // 256x192 / 128x128, eight waves, copies spread
+        if (cols >= 1024) return 111;
+        return cols >= 128 ? 115 : 46;
+    case OP_GDW:
+        return (k >= 128 && n >= 128) ? 115 : 46;
     }
     return 44;
 }
@@ -111,12 +115,12 @@ int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.ch
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
 // The tile that runs, its operand extents and its grid.  The direct-load (ids
-// 40 + base), direct-A (ids 60 + base) and ping-pong (ids 80 + base) families
-// need 16-byte-aligned rows whose length is a multiple of 8 elements and
-// operands below 2^30 bytes; otherwise the register-staged kernel of the base
-// shape runs, or 128x128 where that family has no such shape (same bits
-// either way).  The grid (tiles_i or seg_tiles, and tiles_j, over rows x
-// cols) is set here from the shape that actually runs.
+// 40 + base, 100 + base), direct-A (ids 60 + base) and ping-pong (ids 80 +
+// base) families need 16-byte-aligned rows whose length is a multiple of 8
+// elements and operands below 2^30 bytes; otherwise the register-staged kernel
+// runs on the tile every op instantiates that is closest in shape: 256x256,
+// 128x128 or 64x64 (same bits either way).  The grid (tiles_i or seg_tiles,
+// and tiles_j, over rows x cols) is set here from the shape that actually runs.
 constexpr int64_t kDirectMaxBytes = (int64_t)1 << 30;
 int direct_tile(MfmaArgs &a, int tile, int64_t a_bytes, int64_t b_bytes) {
     a.a_bytes = a_bytes;
@@ -126,10 +130,8 @@ int direct_tile(MfmaArgs &a, int tile, int64_t a_bytes, int64_t b_bytes) {
         const bool ok =
             a.vec_a && a.vec_b && a_bytes <= kDirectMaxBytes && b_bytes <= kDirectMaxBytes;
         if (!ok) {
-            const int base = tile >= 100 ? tile - 100
-                             : tile >= 80 ? tile - 80
-                             : tile >= 60 ? tile - 60 : tile - 40;
-            t = mfma_tile(base) ? base : 4;
+            const TileShape *ts = mfma_tile(tile);
+            t = ts->bm >= 256 && ts->bn >= 256 ? 1 : ts->bm <= 64 && ts->bn <= 64 ? 6 : 4;
         }
     }
     const TileShape *ts = mfma_tile(t);
@@ -291,7 +293,22 @@ int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
         s.tiles_i = cdiv(m, 64); s.tiles_j = cdiv(n, 64);
         return hip_status(launch_scalar_gemm(s, 3 /*e4m3*/, BI_BF16, 2, stream));
     }
+    const bool vec = aligned16(a) && aligned16(bt) && k % 16 == 0;
+    if (pl.tile >= 40 && vec && m * k <= kDirectMaxBytes && n * k <= kDirectMaxBytes) {
+        MfmaArgs d{};
+        d.a = a; d.lda = k; d.b = bt; d.ldb = k; d.c = y; d.ldc = n;
+        d.rows = m; d.cols = n; d.red = k; d.chunk = kNoSplit; d.nchunks = 1;
+        d.vec_a = d.vec_b = 1;
+        d.vec_c = aligned8(y) && n % 4 == 0;
+        d.scale_a = a_dequant; d.scale_b = b_dequant;
+        const int tile = direct_tile(d, pl.tile, m * k, n * k);
+        return hip_status(launch_fp8_dl(d, tile, stream));
+    }
+    // register-staged fp8 kernel: 256x256, 128x128 or 64x64 tiles
     const TileShape *ts = mfma_tile(pl.tile);
+    int tile = pl.tile;
+    if (tile >= 40) tile = ts->bm >= 256 && ts->bn >= 256 ? 1 : ts->bm <= 64 ? 6 : 4;
+    ts = mfma_tile(tile);
     Fp8Args f{};
     f.a = static_cast<const uint8_t *>(a);
     f.bt = static_cast<const uint8_t *>(bt);
@@ -299,9 +316,9 @@ int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
     f.scale_a = a_dequant; f.scale_b = b_dequant;
     f.m = m; f.n = n; f.k = k;
     f.tiles_i = cdiv(m, ts->bm); f.tiles_j = cdiv(n, ts->bn);
-    f.vec = aligned16(a) && aligned16(bt) && k % 16 == 0;
+    f.vec = vec;
     f.vec_c = aligned8(y) && n % 4 == 0;
-    return hip_status(launch_fp8_gemm(f, pl.tile, stream));
+    return hip_status(launch_fp8_gemm(f, tile, stream));
 }
 
 static int grouped_validate(int64_t m, int64_t k, int64_t n, int64_t e, int dtype) {

@@ -66,6 +66,8 @@ struct MfmaArgs {
     int vec_c;         // 8-byte (16-bit outputs) / 16-byte (f32) vector stores allowed
     // bytes readable from a / b (direct-load kernels: reads past them return zero)
     int64_t a_bytes, b_bytes;
+    // fp8: per-tensor dequantisation scales (device f32 scalars)
+    const float *scale_a, *scale_b;
 };
 
 struct Fp8Args {
@@ -98,5 +100,9 @@ hipError_t launch_mfma_gemm(const MfmaArgs &p, int tile_id, int dt, int layout, 
                             hipStream_t s);
 
 hipError_t launch_fp8_gemm(const Fp8Args &p, int tile_id, hipStream_t s);
+// fp8 on the direct-load MFMA kernel (tile ids 40 + base, 100 + base):
+// C(i,j) = RNE_bf16((sum_r A(i,r) B(j,r)) * scale_a * scale_b), both operands
+// reduction-contiguous e4m3 bytes.
+hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, hipStream_t s);
 
 }  // namespace bi

@@ -117,9 +117,36 @@ __device__ __forceinline__ int rs_xor(int k) {
     else return 0;
 }
 
-// Global -> LDS copy of one operand tile per 64-deep stage: R/8 instructions
-// of 1 KB, spread evenly over the NW waves.
-template <int R, bool RC, int NW>
+// Per data type: bytes per element, reduction values per LDS stage (one
+// 128-byte row segment of a reduction-contiguous tile), MFMA steps per stage
+// and the MFMA fragment of one lane.
+template <int DT>
+struct DlType {  // bf16 / f16: v_mfma_f32_32x32x16_{bf16,f16}, 16 values per step
+    static constexpr int ESZ = 2, KPS = 64, STEPS = 4;
+    using Frag = u32x4;
+};
+template <>
+struct DlType<DT_E4M3> {  // fp8 e4m3: v_mfma_scale_f32_32x32x64_f8f6f4, 64 per step
+    static constexpr int ESZ = 1, KPS = 128, STEPS = 2;
+    using Frag = i32x8;
+};
+
+// One MFMA step, B fragment first (each lane then holds 4 consecutive output
+// columns of one row).
+template <int DT>
+__device__ __forceinline__ f32x16 dl_mfma(u32x4 b, u32x4 a, f32x16 c) {
+    return mfma_step<DT>(b, a, c);
+}
+template <int DT>
+__device__ __forceinline__ f32x16 dl_mfma(i32x8 b, i32x8 a, f32x16 c) {
+    // format codes 0 / 0: both operands OCP fp8 e4m3; no block scales
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Global -> LDS copy of one operand tile per stage (128 bytes of each row or,
+// row-contiguous, 64 reduction rows): R/8 instructions of 1 KB, spread evenly
+// over the NW waves.  ESZ: bytes per element.
+template <int R, bool RC, int NW, int ESZ = 2>
 struct DLoad {
     static constexpr int NQ = R / 8 / NW;
     static_assert(NQ >= 1 && NQ * 8 * NW == R, "tile rows must spread evenly over the waves");
@@ -135,9 +162,10 @@ struct DLoad {
             const int s = 64 * (wave + NW * p) + lane;  // chunk slot within the stage
             if constexpr (RC) {
                 const int row = s >> 3, kg = (s & 7) ^ rc_xor(row);
-                off[p] = (uint32_t)(((o0 + row) * ld + r_begin + 8 * kg) * 2);
-                kin[p] = 8 * kg;
+                off[p] = (uint32_t)(((o0 + row) * ld + r_begin) * ESZ + 16 * kg);
+                kin[p] = (16 / ESZ) * kg;
             } else {
+                static_assert(RC || ESZ == 2, "row-contiguous tiles are 16-bit");
                 const int k = s / (R / 8), c = (s % (R / 8)) ^ rs_xor<R>(k);
                 off[p] = (uint32_t)(((r_begin + k) * ld + o0 + 8 * c) * 2);
                 kin[p] = k;
@@ -168,19 +196,34 @@ struct DLoad {
     }
 };
 
-// MFMA fragment reads from a reduction-contiguous stage ([rows][64]).
+// MFMA fragment reads from a reduction-contiguous stage ([rows][128 bytes]).
+// 16-bit: lane l takes 16 bytes (8 values) of row l & 31 at value 8 * (l >> 5)
+// of the step; fp8: 32 bytes (two chunks) at value 32 * (l >> 5).
+template <int ESZ = 2>
 struct RcFrag {
-    uint32_t koff[BK / 16];  // per 16-deep step: lane's byte offset inside a 32-row block
+    static constexpr int CH = ESZ == 2 ? 1 : 2;  // 16-byte chunks per lane and step
+    static constexpr int STEPS = 8 / (2 * CH);   // steps per stage
+    uint32_t koff[STEPS][CH];  // lane's byte offsets inside a 32-row block
 
     __device__ __forceinline__ void init(int lane) {
         const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk)
-            koff[kk] = (uint32_t)(r * 128 + 16 * ((2 * kk + hi) ^ rc_xor(r)));
+        for (int kk = 0; kk < STEPS; ++kk)
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                koff[kk][c] = (uint32_t)(r * 128 + 16 * ((2 * CH * kk + CH * hi + c) ^ rc_xor(r)));
     }
     // rows base .. base+31 (base a multiple of 32)
-    __device__ __forceinline__ u32x4 read(const BI_LDS char *stage, int base, int kk) const {
-        return *reinterpret_cast<const BI_LDS u32x4 *>(stage + base * 128 + koff[kk]);
+    __device__ __forceinline__ auto read(const BI_LDS char *stage, int base, int kk) const {
+        const BI_LDS char *row = stage + base * 128;
+        if constexpr (CH == 1) {
+            return *reinterpret_cast<const BI_LDS u32x4 *>(row + koff[kk][0]);
+        } else {
+            const u32x4 lo = *reinterpret_cast<const BI_LDS u32x4 *>(row + koff[kk][0]);
+            const u32x4 hi = *reinterpret_cast<const BI_LDS u32x4 *>(row + koff[kk][1]);
+            return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
     }
 };
 
@@ -211,13 +254,13 @@ struct RsFrag {
     }
 };
 
-template <bool RC, int R>
+template <bool RC, int R, int ESZ = 2>
 struct FragOf {
     using type = RsFrag<R>;
 };
-template <int R>
-struct FragOf<true, R> {
-    using type = RcFrag;
+template <int R, int ESZ>
+struct FragOf<true, R, ESZ> {
+    using type = RcFrag<ESZ>;
 };
 
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
@@ -230,6 +273,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     constexpr int SA = 128 * BM, SB = 128 * BN;  // bytes of one stage of A / B
     constexpr int NS = dl_stages(BM, BN);
     static_assert(NS >= 2 && NS <= 4, "two to four stages");
+    using TY = DlType<DT>;
+    constexpr int KPS = TY::KPS, STEPS = TY::STEPS;
+    using Frag = typename TY::Frag;
+    static_assert(DT != DT_E4M3 || (A_RC && B_RC), "fp8 operands are reduction-contiguous");
     static_assert(slab_bytes<EPI, WTN, NW>() <= NS * (SA + SB), "epilogue slabs fit in the stages");
     static_assert(EPI != EPI_ROUND || BN <= 64 * NW, "one thread per bias column");
 
@@ -249,14 +296,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
 
     const i32x4 rsa = make_rsrc(p.a, p.a_bytes);
     const i32x4 rsb = make_rsrc(static_cast<const uint16_t *>(p.b) + ti.b_off, p.b_bytes - 2 * ti.b_off);
-    using LA = DLoad<BM, A_RC, NW>;
-    using LB = DLoad<BN, B_RC, NW>;
+    using LA = DLoad<BM, A_RC, NW, TY::ESZ>;
+    using LB = DLoad<BN, B_RC, NW, TY::ESZ>;
     LA la;
     LB lb;
     la.init(p.lda, row0, r_begin, wave, lane);
     lb.init(p.ldb, col0, r_begin, wave, lane);
-    typename FragOf<A_RC, BM>::type ra;
-    typename FragOf<B_RC, BN>::type rb;
+    typename FragOf<A_RC, BM, TY::ESZ>::type ra;
+    typename FragOf<B_RC, BN, TY::ESZ>::type rb;
     ra.init(lane);
     rb.init(lane);
 
@@ -267,14 +314,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
     const int64_t red = r_end - r_begin;
-    const int nst = (int)((red + BK - 1) / BK);
+    const int nst = (int)((red + KPS - 1) / KPS);
     BI_LDS char *ring = (BI_LDS char *)lds_raw;
 
     auto issue = [&](int s) {
         BI_LDS char *da = ring + (s % NS) * (SA + SB);
         BI_LDS char *db = da + SA;
-        const int64_t rem = red - (int64_t)BK * s;
-        if (rem >= BK) {
+        const int64_t rem = red - (int64_t)KPS * s;
+        if (rem >= KPS) {
             la.template issue<false>(rsa, da, s, rem, wave);
             lb.template issue<false>(rsb, db, s, rem, wave);
         } else {
@@ -291,10 +338,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         else return rb.read(st, (wn * WTN) / 32 + j, kk);
     };
 
-    // Fragment ring: set kk holds the fragments of 16-deep step kk of the
-    // stage being multiplied or of the next one.  Fragments are read three
-    // steps ahead of their MFMAs, interleaved with the MFMAs of the current step.
-    u32x4 fa[BK / 16][FM], fb[BK / 16][FN];
+    // Fragment ring: set kk holds the fragments of step kk of the stage being
+    // multiplied or of the next one.  Fragments are read STEPS - 1 steps ahead
+    // of their MFMAs, interleaved with the MFMAs of the current step.
+    Frag fa[STEPS][FM], fb[STEPS][FN];
     auto read_step = [&](const BI_LDS char *st, int kk, int set) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) fa[set][i] = frag_a(st, i, kk);
@@ -305,10 +352,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma_step<DT>(fb[set][j], fa[set][i], acc[i][j]);
+            for (int j = 0; j < FN; ++j) acc[i][j] = dl_mfma<DT>(fb[set][j], fa[set][i], acc[i][j]);
     };
     // reads of one step spread between the MFMAs of another
-    constexpr int NREAD = FM * (A_RC ? 1 : 2) + FN * (B_RC ? 1 : 2);
+    constexpr int RCR = TY::ESZ == 2 ? 1 : 2;  // LDS reads per reduction-contiguous fragment
+    constexpr int NREAD = FM * (A_RC ? RCR : 2) + FN * (B_RC ? RCR : 2);
     constexpr int NMFMA = FM * FN;
     constexpr int PER = (NREAD + NMFMA - 1) / NMFMA;
     auto interleave = [&]() {
@@ -325,11 +373,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     // after the barrier (a burst of copy instructions can hold up the wave's
     // MFMA issue while the memory pipeline takes them in).
     constexpr int NC = LA::NQ + LB::NQ;                 // copies per wave per stage
-    constexpr int NSLOT = (BK / 16 - 1) * NMFMA;         // MFMAs of steps 1..3
+    constexpr int NSLOT = (STEPS - 1) * NMFMA;           // MFMAs of steps 1..STEPS-1
     constexpr int CPS = (NC + NSLOT - 1) / NSLOT;        // copies after each of them
     auto copy_one = [&](int cs, int c) {
         BI_LDS char *da = ring + (cs % NS) * (SA + SB);
-        const int64_t rem = red - (int64_t)BK * cs;
+        const int64_t rem = red - (int64_t)KPS * cs;
         if (c < LA::NQ) la.issue_one(rsa, da, cs, rem, wave, c);
         else lb.issue_one(rsb, da + SA, cs, rem, wave, c - LA::NQ);
     };
@@ -350,13 +398,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
         __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < BK / 16 - 1; ++kk) read_step(ring, kk, kk);
+        for (int kk = 0; kk < STEPS - 1; ++kk) read_step(ring, kk, kk);
         __builtin_amdgcn_sched_barrier(0);
     }
     for (int s = 0; s < nst; ++s) {
         const BI_LDS char *cur = ring + (s % NS) * (SA + SB);
         const BI_LDS char *nxt = ring + ((s + 1) % NS) * (SA + SB);
-        read_step(cur, BK / 16 - 1, BK / 16 - 1);
+        read_step(cur, STEPS - 1, STEPS - 1);
         mfma_step_all(0);
         interleave();
         const bool more = s + 1 < nst;
@@ -371,7 +419,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (!SPREAD) {
 #pragma unroll
-            for (int kk = 1; kk < BK / 16; ++kk) {
+            for (int kk = 1; kk < STEPS; ++kk) {
                 if (more) read_step(nxt, kk - 1, kk - 1);
                 mfma_step_all(kk);
                 interleave();
@@ -380,7 +428,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         }
         const bool copies = s + NS < nst;
 #pragma unroll
-        for (int kk = 1; kk < BK / 16; ++kk) {
+        for (int kk = 1; kk < STEPS; ++kk) {
 #pragma unroll
             for (int q = 0; q < NMFMA; ++q) {
                 if (more) {
@@ -391,7 +439,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
                     }
                 }
                 acc[q / FN][q % FN] =
-                    mfma_step<DT>(fb[kk][q % FN], fa[kk][q / FN], acc[q / FN][q % FN]);
+                    dl_mfma<DT>(fb[kk][q % FN], fa[kk][q / FN], acc[q / FN][q % FN]);
                 if (copies) {
                     const int c0 = ((kk - 1) * NMFMA + q) * CPS;
 #pragma unroll

@@ -51,7 +51,8 @@ constexpr int KG = BK / 8;  // 8-element groups per slice
 constexpr int NT = 256;     // threads per workgroup (4 waves)
 
 enum Mode : int { MODE_PLAIN = 0, MODE_SEGMENTS = 1, MODE_EXPERT_RED = 2 };
-enum Epi : int { EPI_ROUND = 0, EPI_PARTIAL = 1, EPI_F32 = 2 };
+// EPI_SCALE: fp8 output, RNE_bf16((acc * scale_a) * scale_b)
+enum Epi : int { EPI_ROUND = 0, EPI_PARTIAL = 1, EPI_F32 = 2, EPI_SCALE = 3 };
 
 __device__ __forceinline__ int swz(int row, int kg) {
     return (row & ~7) | ((row ^ (row >> 3) ^ kg) & 7);
@@ -397,7 +398,7 @@ __device__ __forceinline__ float fetch_bias(const MfmaArgs &p, int64_t col0, int
 // LDS bytes the epilogue needs (four waves, one 32-row slab each)
 template <int EPI, int WTN, int NW = 4>
 constexpr int slab_bytes() {
-    return NW * 32 * (WTN * (EPI == EPI_ROUND ? 2 : 4) + 16);
+    return NW * 32 * (WTN * (EPI == EPI_ROUND || EPI == EPI_SCALE ? 2 : 4) + 16);
 }
 
 // Epilogue.  For block (i, j) a lane holds row (lane & 31) and, for
@@ -413,7 +414,8 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
     const int lrow = lane & 31, lkg = lane >> 5;
     const int64_t row0 = ti.row0, row_end = ti.row_end, col0 = ti.col0;
     const int64_t chunk = ti.chunk, c_off = ti.c_off;
-    using OutT = typename std::conditional<EPI == EPI_ROUND, uint16_t, float>::type;
+    using OutT =
+        typename std::conditional<EPI == EPI_ROUND || EPI == EPI_SCALE, uint16_t, float>::type;
     constexpr int OSZ = (int)sizeof(OutT);
     constexpr int ROWB = WTN * OSZ;           // bytes of one slab row
     constexpr int ROWP = ROWB + 16;           // padded LDS row pitch (spreads banks)
@@ -426,6 +428,8 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
         if (p.bias && t < BN) bias_l[t] = bias_v;
     }
     __syncthreads();  // bias visible; every wave done with the stage buffers
+    float scale_a = 0.0f, scale_b = 0.0f;
+    if constexpr (EPI == EPI_SCALE) scale_a = p.scale_a[0], scale_b = p.scale_b[0];
     // this lane's bias columns, read from LDS once for all row slabs
     f32x4 bias_r[FN][4];
     if constexpr (EPI == EPI_ROUND) {
@@ -453,6 +457,11 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
                     }
                     *reinterpret_cast<u32x2 *>(dst) =
                         u32x2{pack2_rne<DT>(v[0], v[1]), pack2_rne<DT>(v[2], v[3])};
+                } else if constexpr (EPI == EPI_SCALE) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) v[x] = (v[x] * scale_a) * scale_b;
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{pack2_rne<DT_BF16>(v[0], v[1]),
+                                                            pack2_rne<DT_BF16>(v[2], v[3])};
                 } else {
                     *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
                 }

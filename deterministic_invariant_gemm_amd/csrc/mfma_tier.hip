@@ -42,7 +42,7 @@ const TileShape *mfma_tile(int id) {
         if (s.id == id) return &s;
     // ids 100 + i: the direct-load kernel with copies spread between MFMAs
     static const TileShape dls[] = {
-        {105, 128, 96}, {108, 96, 96}, {111, 256, 192}, {115, 128, 128},
+        {105, 128, 96}, {108, 96, 96}, {111, 256, 192}, {112, 256, 256}, {115, 128, 128},
     };
     for (const TileShape &s : dls)
         if (s.id == id) return &s;

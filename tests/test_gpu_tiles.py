@@ -18,7 +18,7 @@ from parity import check, dev, empty, host
 pytestmark = pytest.mark.gpu
 
 TILE_IDS = (list(range(1, 20)) + list(range(21, 31)) + list(range(41, 58))
-            + [65, 70, 76, 78, 79, 91, 92, 93, 94, 95, 105, 108, 111, 115])
+            + [65, 70, 76, 78, 79, 91, 92, 93, 94, 95, 105, 108, 111, 112, 115])
 
 
 def run_all(fn):
@@ -100,3 +100,40 @@ def test_grouped_tiles_identical(dt):
         for tid, o in outs.items():
             assert np.array_equal(o, base), (name, tid)
         print(name, "tiles", sorted(outs))
+
+
+FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 55, 111, 112, 115]
+
+
+@pytest.mark.parametrize("shape", [(300, 256, 260), (520, 384, 392), (700, 1008, 456),
+                                   (260, 200, 300)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_tiles_identical(shape):
+    """The register-staged fp8 kernel and every direct-load fp8 tile give the
+    same bits (rows of 16-byte multiples use the direct-load kernel; the last
+    shape's K = 200 sends every tile to the register-staged kernel)."""
+    m, k, n = shape
+    d = synth.fp8(m, k, n, seed=81 + m)
+    a, bt = dev(d["a8"]), dev(d["bt8"])
+    da = torch.tensor([float(d["da"])], dtype=torch.float32, device="cuda")
+    db = torch.tensor([float(d["db"])], dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def run(tc):
+        y = empty((m, n), np.uint16)
+        dig.check(dig.bi_fp8_mm(y, a, bt, da, db, m, k, n, s, tc))
+        return host(y, np.uint16)
+
+    base = run(1)
+    check(base, oracle.fp8_mm(d["a8"], d["bt8"], d["da"], d["db"], m, k, n), synth.BF16,
+          "fp8 default tile")
+    outs = {}
+    for tid in FP8_TILE_IDS:
+        try:
+            outs[tid] = run(16 + tid)
+        except dig.BIError as e:
+            assert e.status == -6
+    assert len(outs) >= 3, sorted(outs)
+    for tid, o in outs.items():
+        assert np.array_equal(o, base), tid
+    print("fp8 tiles", sorted(outs))
