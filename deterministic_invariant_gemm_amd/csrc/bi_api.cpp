@@ -69,13 +69,11 @@ int pick_tile(int op, int64_t k, int64_t n) {
         if (cols >= 2048) return 52;                                           // 256x256, 8 waves
         return cols >= 128 ? 44 : 46;
     case OP_DX:
-        // 128x128, eight waves, copies spread between MFMAs
-        return cols >= 128 ? 115 : 46;
+        if (cols % 96 == 0 && cols <= 1536) return 45;  // 128x96, four waves along M
+        return cols >= 128 ? 115 : 46;                  // 128x128, eight waves, spread
     case OP_DW:
-        // 96x96 (three waves): 256 tiles of a 768 x 3072 output; larger outputs
-        // fill the chip with 128x128 (eight waves, copies spread)
-        if (k >= 128 && n >= 128) return k * n <= (int64_t)256 * 96 * 96 ? 48 : 115;
-        return 46;
+        // 128x128, eight waves, copies spread between MFMAs
+        return (k >= 128 && n >= 128) ? 115 : 46;
     case OP_GFWD: case OP_GDIN:
         // 256x192 / 128x128, eight waves, copies spread
         if (cols >= 1024) return 111;

@@ -354,12 +354,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) acc[i][j] = dl_mfma<DT>(fb[set][j], fa[set][i], acc[i][j]);
     };
-    // reads of one step spread between the MFMAs of another
     constexpr int RCR = TY::ESZ == 2 ? 1 : 2;  // LDS reads per reduction-contiguous fragment
-    constexpr int NREAD = FM * (A_RC ? RCR : 2) + FN * (B_RC ? RCR : 2);
+    constexpr int NREAD = FM * (A_RC ? RCR : 2) + FN * (B_RC ? RCR : 2);  // per step
     constexpr int NMFMA = FM * FN;
-    constexpr int PER = (NREAD + NMFMA - 1) / NMFMA;
-    auto interleave = [&]() {
+    // LDS reads of `sets` steps spread between the MFMAs of one step
+    auto interleave = [&](auto sets_tag) {
+        constexpr int PER = (decltype(sets_tag)::value * NREAD + NMFMA - 1) / NMFMA;
 #pragma unroll
         for (int q = 0; q < NMFMA; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
@@ -368,12 +368,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // SPREAD: the copies of stage s+NS are issued one or a few at a time
-    // between the MFMAs of steps 1..3 of stage s instead of all at once right
-    // after the barrier (a burst of copy instructions can hold up the wave's
-    // MFMA issue while the memory pipeline takes them in).
+    // Schedule per stage s (buffer s % NS).  The workgroup barrier that hands
+    // buffer s to the copies of stage s+NS and makes stage s+1 visible comes
+    // after MFMA step BAR; the last reads of buffer s (step STEPS-1, issued at
+    // step 0) then have a step of MFMAs to complete before the barrier waits
+    // for them.
+    //   step 0:             read step STEPS-1 of stage s, multiply step 0
+    //   steps 1..BAR:       multiply
+    //   barrier:            wait until stage s+1 has landed; barrier; copies of
+    //                       stage s+NS into buffer s
+    //   steps BAR+1..:      read steps 0..STEPS-2 of stage s+1 (step kk reads
+    //                       sets first(kk) .. first(kk+1)-1), multiply step kk
+    // The reads of stage s+1 are issued also after the last stage (from a
+    // buffer holding older data, never used) so that they need no branch and
+    // interleave freely with the MFMAs.  SPREAD: per MFMA of steps BAR+1..,
+    // its share of the reads, the MFMA, its share of the copies of stage s+NS
+    // (a burst of copy instructions can hold up the wave's MFMA issue while
+    // the memory pipeline takes them in).
+    constexpr int BAR = STEPS >= 4 ? 1 : 0;
+    auto first_set = [](int kk) { return kk <= BAR + 1 ? 0 : kk - 1; };
     constexpr int NC = LA::NQ + LB::NQ;                 // copies per wave per stage
-    constexpr int NSLOT = (STEPS - 1) * NMFMA;           // MFMAs of steps 1..STEPS-1
+    constexpr int NSLOT = (STEPS - 1 - BAR) * NMFMA;     // MFMAs after the barrier
     constexpr int CPS = (NC + NSLOT - 1) / NSLOT;        // copies after each of them
     auto copy_one = [&](int cs, int c) {
         BI_LDS char *da = ring + (cs % NS) * (SA + SB);
@@ -382,13 +397,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         else lb.issue_one(rsb, da + SA, cs, rem, wave, c - LA::NQ);
     };
 
-    // Schedule per stage s (buffer s % NS), steps kk = 0..3:
-    //   kk = 0: read step 3 of stage s, multiply step 0; then wait until stage
-    //           s+1 has landed and barrier (every wave has read all of stage s,
-    //           so its buffer takes stage s+NS);
-    //   kk = 1..3: read step kk-1 of stage s+1, multiply step kk (SPREAD: per
-    //           MFMA of step kk, its share of those reads, the MFMA, its share
-    //           of the copies of stage s+NS).
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         if (s < nst) issue(s);
@@ -406,9 +414,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         const BI_LDS char *nxt = ring + ((s + 1) % NS) * (SA + SB);
         read_step(cur, STEPS - 1, STEPS - 1);
         mfma_step_all(0);
-        interleave();
-        const bool more = s + 1 < nst;
-        if (more) {
+        interleave(std::integral_constant<int, 1>{});
+#pragma unroll
+        for (int kk = 1; kk <= BAR; ++kk) {
+            mfma_step_all(kk);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (s + 1 < nst) {
             // issued so far: stages 0 .. min(s+NS-1, nst-1); stage s+1 has
             // landed once only the copies of the stages after it are pending
             const int later = nst - 2 - s < NS - 2 ? nst - 2 - s : NS - 2;
@@ -419,34 +431,37 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (!SPREAD) {
 #pragma unroll
-            for (int kk = 1; kk < STEPS; ++kk) {
-                if (more) read_step(nxt, kk - 1, kk - 1);
+            for (int kk = BAR + 1; kk < STEPS; ++kk) {
+#pragma unroll
+                for (int x = first_set(kk); x < first_set(kk + 1); ++x) read_step(nxt, x, x);
                 mfma_step_all(kk);
-                interleave();
+                if (kk == BAR + 1) interleave(std::integral_constant<int, BAR + 1>{});
+                else interleave(std::integral_constant<int, 1>{});
             }
-            continue;
-        }
-        const bool copies = s + NS < nst;
+        } else {
+            const bool copies = s + NS < nst;
 #pragma unroll
-        for (int kk = 1; kk < STEPS; ++kk) {
+            for (int kk = BAR + 1; kk < STEPS; ++kk) {
+                const int x0 = first_set(kk), nx = first_set(kk + 1) - x0;
 #pragma unroll
-            for (int q = 0; q < NMFMA; ++q) {
-                if (more) {
+                for (int q = 0; q < NMFMA; ++q) {
+                    // fragments (set x0 + f / (FM+FN), index f % (FM+FN)) with f = q mod NMFMA
 #pragma unroll
-                    for (int f = q; f < FM + FN; f += NMFMA) {
-                        if (f < FM) fa[kk - 1][f] = frag_a(nxt, f, kk - 1);
-                        else fb[kk - 1][f - FM] = frag_b(nxt + SA, f - FM, kk - 1);
+                    for (int f = q; f < nx * (FM + FN); f += NMFMA) {
+                        const int x = x0 + f / (FM + FN), g = f % (FM + FN);
+                        if (g < FM) fa[x][g] = frag_a(nxt, g, x);
+                        else fb[x][g - FM] = frag_b(nxt + SA, g - FM, x);
                     }
-                }
-                acc[q / FN][q % FN] =
-                    dl_mfma<DT>(fb[kk][q % FN], fa[kk][q / FN], acc[q / FN][q % FN]);
-                if (copies) {
-                    const int c0 = ((kk - 1) * NMFMA + q) * CPS;
+                    acc[q / FN][q % FN] =
+                        dl_mfma<DT>(fb[kk][q % FN], fa[kk][q / FN], acc[q / FN][q % FN]);
+                    if (copies) {
+                        const int c0 = ((kk - BAR - 1) * NMFMA + q) * CPS;
 #pragma unroll
-                    for (int c = c0; c < c0 + CPS; ++c)
-                        if (c < NC) copy_one(s + NS, c);
+                        for (int c = c0; c < c0 + CPS; ++c)
+                            if (c < NC) copy_one(s + NS, c);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
