@@ -108,6 +108,23 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
     return pl;
 }
 
+// Tile for the batch at hand (forward, dX, fp8): the default tile of (k, n)
+// while it gives at least 192 workgroups (three quarters of the CUs), else
+// 128x128 (eight waves) if that does, else the narrow 64x32 tile, which gives
+// the most column tiles to spread the stream of B over.  The tile may follow
+// m because every tile issues the same MFMA sequence per element (the bits do
+// not change); the tier never follows m.  Forced tiles are kept.
+int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols) {
+    if (pl.tile < 40 || tc >= kForceBase) return pl.tile;
+    auto wgs = [&](int id) {
+        const TileShape *ts = mfma_tile(id);
+        return cdiv(m, ts->bm) * cdiv(cols, ts->bn);
+    };
+    if (wgs(pl.tile) >= 192) return pl.tile;
+    if (wgs(115) >= 192) return 115;
+    return 120;
+}
+
 int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.chunk); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
@@ -190,7 +207,7 @@ int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t 
     a.vec_a = aligned16(x) && k % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(y) && n % 4 == 0;
-    const int tile = direct_tile(a, pl.tile, 2 * m * k, 2 * k * n);
+    const int tile = direct_tile(a, batch_tile(pl, tc, m, n), 2 * m * k, 2 * k * n);
     return hip_status(launch_mfma_gemm(a, tile, dtype, /*layout A rc, B strided*/ 1, 0, stream));
 }
 
@@ -218,7 +235,7 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
     a.vec_a = aligned16(dy) && n % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(dx) && k % 4 == 0;
-    const int tile = direct_tile(a, pl.tile, 2 * m * n, 2 * k * n);
+    const int tile = direct_tile(a, batch_tile(pl, tc, m, k), 2 * m * n, 2 * k * n);
     return hip_status(launch_mfma_gemm(a, tile, dtype, /*both rc*/ 3, 0, stream));
 }
 
@@ -299,7 +316,7 @@ int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
         d.vec_a = d.vec_b = 1;
         d.vec_c = aligned8(y) && n % 4 == 0;
         d.scale_a = a_dequant; d.scale_b = b_dequant;
-        const int tile = direct_tile(d, pl.tile, m * k, n * k);
+        const int tile = direct_tile(d, batch_tile(pl, tc, m, n), m * k, n * k);
         return hip_status(launch_fp8_dl(d, tile, stream));
     }
     // register-staged fp8 kernel: 256x256, 128x128 or 64x64 tiles

@@ -15,6 +15,8 @@ hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, hipStream_t s) {
     const int64_t grid = p.tiles_i * p.tiles_j;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (tile_id >= 120)
+        return launch_dl_among<DT_E4M3, true, true, EPI_SCALE, MODE_PLAIN, 20>(p, tile_id, grid, s);
     if (tile_id >= 100)
         return launch_dls_among<DT_E4M3, true, true, EPI_SCALE, MODE_PLAIN, 11, 12, 15>(
             p, tile_id, grid, s);

@@ -52,20 +52,27 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// vmcnt(n * Q) for a run-time n in [0, 3]
-template <int Q>
+// vmcnt(n * Q) for a run-time n in [0, 7] (a count above 63 is lowered to 63,
+// which only waits longer)
+template <int Q, int I = 0>
 __device__ __forceinline__ void wait_vmcnt_stages(int n) {
-    if (n <= 0) wait_vmcnt<0>();
-    else if (n == 1) wait_vmcnt<Q>();
-    else if (n == 2) wait_vmcnt<(2 * Q < 63 ? 2 * Q : 63)>();
-    else wait_vmcnt<(3 * Q < 63 ? 3 * Q : 63)>();
+    constexpr int C = I * Q < 63 ? I * Q : 63;
+    if constexpr (I >= 7) {
+        wait_vmcnt<C>();
+    } else {
+        if (n <= I) wait_vmcnt<C>();
+        else wait_vmcnt_stages<Q, I + 1>(n);
+    }
 }
 
-// LDS stages of 64 reduction values for a BM x BN tile: as many as fit in
-// 160 KB next to the bias row, at most 4
+// LDS stages (128 bytes of every tile row each) for a BM x BN tile: as many as
+// fit in 160 KB next to the bias row, at most 4 -- at most 8 for small tiles,
+// whose stages are short and which need more of them in flight to keep
+// memory busy (small-M shapes stream the whole of B through a few rows of A)
 constexpr int dl_stages(int bm, int bn) {
     const int per = 128 * (bm + bn), avail = 160 * 1024 - 4 * bn;
-    return avail / per >= 4 ? 4 : avail / per;
+    const int cap = bm + bn <= 128 ? 8 : 4;
+    return avail / per >= cap ? cap : avail / per;
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
     constexpr int SA = 128 * BM, SB = 128 * BN;  // bytes of one stage of A / B
     constexpr int NS = dl_stages(BM, BN);
-    static_assert(NS >= 2 && NS <= 4, "two to four stages");
+    static_assert(NS >= 2 && NS <= 8, "two to eight stages");
     using TY = DlType<DT>;
     constexpr int KPS = TY::KPS, STEPS = TY::STEPS;
     using Frag = typename TY::Frag;
@@ -479,20 +486,26 @@ hipError_t launch_dl_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
     return hipGetLastError();
 }
 
-// tile ids 40 + base id select the direct-load kernel with base tile `id`
+// tile id of the direct-load kernel on base tile `base`: 40 + base for bases
+// 1..19, 100 + base for bases 20..39
+constexpr int dl_id(int base) { return base < 20 ? 40 + base : 100 + base; }
+
+// tile ids dl_id(base) select the direct-load kernel with base tile `base`
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int... IDS>
 hipError_t launch_dl_among(const MfmaArgs &p, int tile_id, int64_t grid, hipStream_t s) {
     hipError_t r = hipErrorInvalidValue;
-    ((tile_id == 40 + IDS
+    ((tile_id == dl_id(IDS)
           ? (void)(r = launch_dl_tile<DT, ARC, BRC, EPI, MODE, IDS, false>(p, grid, s))
           : (void)0),
      ...);
     return r;
 }
 
-// tile ids 100 + base id: the same kernel with the copies spread between MFMAs
+// tile ids 100 + base id (bases 1..19): the same kernel with the copies spread
+// between MFMAs
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int... IDS>
 hipError_t launch_dls_among(const MfmaArgs &p, int tile_id, int64_t grid, hipStream_t s) {
+    static_assert(((IDS < 20) && ...), "spread variants exist for bases 1..19");
     hipError_t r = hipErrorInvalidValue;
     ((tile_id == 100 + IDS
           ? (void)(r = launch_dl_tile<DT, ARC, BRC, EPI, MODE, IDS, true>(p, grid, s))

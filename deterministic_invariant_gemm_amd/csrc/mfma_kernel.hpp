@@ -658,6 +658,8 @@ template <> struct TileOf<16> { static constexpr int BM = 256, BN = 192, WGM = 4
 template <> struct TileOf<18> { static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 1; };
 template <> struct TileOf<19> { static constexpr int BM = 128, BN = 192, WGM = 4, WGN = 1; };
 template <> struct TileOf<17> { static constexpr int BM = 96, BN = 96, WGM = 1, WGN = 3; };
+// small-M shapes (direct-load kernel only, tile id 120): many narrow column tiles
+template <> struct TileOf<20> { static constexpr int BM = 64, BN = 32, WGM = 2, WGN = 1; };
 
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>
 hipError_t launch_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {

@@ -170,7 +170,12 @@ const char *bi_status_string(int status);
  * op: 0 forward, 1 dX, 2 dW, 3 fp8, 4 grouped forward, 5 grouped dinput,
  * 6 grouped dweights.  Returns 0 for the scalar tier, a positive tile id for
  * the MFMA tier, or a negative bi_status.  Depends on (op, dtype, tc, k, n)
- * only.  For dW, *chunk_rows (if not NULL) receives the chunk length C. */
+ * only: the tier and the dW chunk length C never depend on m.  The tile
+ * reported is the default for large batches; forward, dX and fp8 calls whose
+ * m gives that tile fewer than 192 workgroups run 128x128 or a narrow 64x32
+ * tile instead (every tile issues the same MFMA sequence per element, so the
+ * bits are the same).  For dW, *chunk_rows (if not NULL) receives the chunk
+ * length C. */
 int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows);
 
 #ifdef __cplusplus

@@ -18,7 +18,7 @@ from parity import check, dev, empty, host
 pytestmark = pytest.mark.gpu
 
 TILE_IDS = (list(range(1, 20)) + list(range(21, 31)) + list(range(41, 58))
-            + [65, 70, 76, 78, 79, 91, 92, 93, 94, 95, 105, 108, 111, 112, 115])
+            + [65, 70, 76, 78, 79, 91, 92, 93, 94, 95, 104, 105, 108, 111, 112, 115, 120])
 
 
 def run_all(fn):
@@ -102,7 +102,7 @@ def test_grouped_tiles_identical(dt):
         print(name, "tiles", sorted(outs))
 
 
-FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 55, 111, 112, 115]
+FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 55, 111, 112, 115, 120]
 
 
 @pytest.mark.parametrize("shape", [(300, 256, 260), (520, 384, 392), (700, 1008, 456),
