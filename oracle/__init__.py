@@ -7,7 +7,7 @@ accumulation, one round-to-nearest-even at the end); this module only marshals
 numpy arrays into it with ctypes.
 
 Dtype codes: 0 = f32, 1 = bf16, 2 = f16 (storage as uint32 / uint16 bit
-patterns), e4m3fn codes are uint8.
+patterns); fp8 formats 3 = e4m3fn, 4 = e5m2 (codes are uint8).
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 SRC_PATH = os.path.join(HERE, "oracle.c")
 
-F32, BF16, F16, E4M3 = 0, 1, 2, 3
+F32, BF16, F16, E4M3, E5M2 = 0, 1, 2, 3, 4
 STORAGE = {F32: np.uint32, BF16: np.uint16, F16: np.uint16}
 
 
@@ -63,6 +63,17 @@ def lib():
         L.orc_rne_f32.restype = ctypes.c_uint32
         L.orc_rne_e4m3_sat.argtypes = [ctypes.c_double]
         L.orc_rne_e4m3_sat.restype = ctypes.c_uint8
+        L.orc_decode_e5m2.argtypes = [ctypes.c_uint8]
+        L.orc_decode_e5m2.restype = ctypes.c_double
+        L.orc_rne_e5m2_sat.argtypes = [ctypes.c_double]
+        L.orc_rne_e5m2_sat.restype = ctypes.c_uint8
+        f32 = ctypes.c_float
+        L.orc_fp8_quantize.argtypes = [i32, vp, f32, i64, vp, vp]
+        L.orc_fp8_transpose_quantize.argtypes = [i32, vp, f32, i64, i64, vp, vp]
+        L.orc_fp8_linear_forward.argtypes = [vp, vp, vp, f32, f32, f32, f32, i64, i64, i64, vp,
+                                             i64, vp, vp, vp, vp, vp, i32]
+        L.orc_fp8_linear_backward.argtypes = [i32, vp, vp, vp, f32, f32, f32, f32, f32, f32,
+                                              i64, i64, i64, vp, i64, vp, vp, vp, vp, i32]
         common = [i64, i64, i64, vp, i64, vp, vp, vp, i32]
         L.orc_linear_forward.argtypes = [i32, vp, vp, vp] + common
         L.orc_linear_dx.argtypes = [i32, vp, vp] + common
@@ -73,7 +84,9 @@ def lib():
         L.orc_grouped_dinput.argtypes = [i32, vp, vp] + gcommon
         L.orc_grouped_dweights.argtypes = [i32, vp, vp] + gcommon
         for f in ("orc_linear_forward", "orc_linear_dx", "orc_linear_dw", "orc_fp8_mm",
-                  "orc_grouped_fwd", "orc_grouped_dinput", "orc_grouped_dweights"):
+                  "orc_grouped_fwd", "orc_grouped_dinput", "orc_grouped_dweights",
+                  "orc_fp8_quantize", "orc_fp8_transpose_quantize", "orc_fp8_linear_forward",
+                  "orc_fp8_linear_backward"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -171,6 +184,70 @@ def fp8_mm(a8, bt8, da, db, m, k, n, rows=None, threads=None):
     return Result(out, s, a)
 
 
+def fp8_quantize(fmt, src, scale_inv):
+    """(codes, amax): codes[i] = FP8(f32(src[i]) * scale_inv) (RNE, saturating),
+    amax = max |src| over the unscaled bf16 source.  src: uint16 bf16 bits (any
+    shape); fmt: E4M3 or E5M2; scale_inv: an f32 value."""
+    src = np.ascontiguousarray(src, dtype=np.uint16)
+    dst = np.zeros(src.shape, dtype=np.uint8)
+    amax = ctypes.c_float(0.0)
+    rc = lib().orc_fp8_quantize(fmt, _ptr(src), float(np.float32(scale_inv)), src.size,
+                                _ptr(dst), ctypes.byref(amax))
+    assert rc == 0
+    return dst, amax.value
+
+
+def fp8_transpose_quantize(fmt, src, scale_inv, rows, cols):
+    """(codes [cols, rows], amax) for src [rows, cols] bf16 bits."""
+    src = np.ascontiguousarray(src, dtype=np.uint16).reshape(rows, cols)
+    dst = np.zeros((cols, rows), dtype=np.uint8)
+    amax = ctypes.c_float(0.0)
+    rc = lib().orc_fp8_transpose_quantize(fmt, _ptr(src), float(np.float32(scale_inv)), rows,
+                                          cols, _ptr(dst), ctypes.byref(amax))
+    assert rc == 0
+    return dst, amax.value
+
+
+def fp8_linear_forward(x, w, bias, sx, sw, sx_inv, sw_inv, m, k, n, rows=None, threads=None):
+    """Y = RNE_bf16((q(x) q(w)^T) * sx * sw + b); x: [m,k], w: [n,k], bias: [n]
+    or None (bf16 bits).  Returns a Result with .amax_x and .amax_w."""
+    x, w = _c(x, np.uint16), _c(w, np.uint16)
+    bias = None if bias is None else _c(bias, np.uint16)
+    r, nr = _rows_arg(rows, m)
+    out, s, a = _alloc(nr, n, BF16)
+    ax, aw = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    f = lambda v: float(np.float32(v))
+    rc = lib().orc_fp8_linear_forward(_ptr(x), _ptr(w), _ptr(bias), f(sx), f(sw), f(sx_inv),
+                                      f(sw_inv), m, k, n, _ptr(r), nr, _ptr(out), _ptr(s),
+                                      _ptr(a), ctypes.byref(ax), ctypes.byref(aw),
+                                      threads or default_threads())
+    assert rc == 0
+    res = Result(out, s, a)
+    res.amax_x, res.amax_w = ax.value, aw.value
+    return res
+
+
+def fp8_linear_backward(which, g, x, w, sg, sw, sx, sg_inv, sw_inv, sx_inv, m, k, n, rows=None,
+                        threads=None):
+    """which = "dx": dX = RNE_bf16((q(g) q(w)) * sg * sw), rows of M, [nrows, k];
+    which = "dw": dW = RNE_bf16((q(g)^T q(x)) * sg * sx), rows of N, [nrows, k].
+    g: [m,n], x: [m,k], w: [n,k] bf16 bits.  Returns a Result with .amax_g."""
+    g, x, w = _c(g, np.uint16), _c(x, np.uint16), _c(w, np.uint16)
+    code = {"dx": 1, "dw": 2}[which]
+    r, nr = _rows_arg(rows, m if code == 1 else n)
+    out, s, a = _alloc(nr, k, BF16)
+    ag = ctypes.c_float(0.0)
+    f = lambda v: float(np.float32(v))
+    rc = lib().orc_fp8_linear_backward(code, _ptr(g), _ptr(x), _ptr(w), f(sg), f(sw), f(sx),
+                                       f(sg_inv), f(sw_inv), f(sx_inv), m, k, n, _ptr(r), nr,
+                                       _ptr(out), _ptr(s), _ptr(a), ctypes.byref(ag),
+                                       threads or default_threads())
+    assert rc == 0
+    res = Result(out, s, a)
+    res.amax_g = ag.value
+    return res
+
+
 def grouped_fwd(dt, inp, weights, row_experts, m, k, n, e, rows=None, threads=None):
     """Y[m] = RNE_T(in[m] Wt[e(m)]^T), zero rows for ids outside [0,E)."""
     st = STORAGE[dt]
@@ -220,3 +297,5 @@ def rne_bf16(x): return lib().orc_rne_bf16(float(x))
 def rne_f16(x): return lib().orc_rne_f16(float(x))
 def rne_f32(x): return lib().orc_rne_f32(float(x))
 def rne_e4m3_sat(x): return lib().orc_rne_e4m3_sat(float(x))
+def decode_e5m2(b): return lib().orc_decode_e5m2(int(b))
+def rne_e5m2_sat(x): return lib().orc_rne_e5m2_sat(float(x))

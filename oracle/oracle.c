@@ -41,6 +41,22 @@
  *            Y[m,n] = sum_k input[m,k] weights[expert(m),n,k].
  *   The grouped oracle routes rows by row_experts alone; it never reads an
  *   offsets array.
+ *   quantize  q[i] = FP8( f32( f32(src[i]) * scale_inv ) ), amax = max |src[i]|
+ *            AstrAI fp8_mm.cu, quantize_kernel and cast_fp8: the bf16 value
+ *            times the inverse scale in f32, then converted to e4m3fn or e5m2
+ *            with round-to-nearest-even, values beyond the largest finite one
+ *            saturating to it (NaN stays NaN); amax is the max-abs of the
+ *            unscaled source (NaN ignored).  transpose_quantize_kernel: the
+ *            same per element, stored transposed ([rows,cols] -> [cols,rows]).
+ *   fp8 linear forward (fp8_linear_forward_scaled)
+ *            Y[m,n] = RNE_bf16( (sum_k qx[m,k] qw[n,k]) * sx * sw + b[n] )
+ *            with qx = quantize(x, 1/sx), qw = quantize(w, 1/sw), w stored
+ *            [N,K]; the bias joins before the single rounding.
+ *   fp8 linear backward (fp8_linear_backward_scaled)
+ *            dX[m,k] = RNE_bf16( (sum_n qg[m,n] qw[n,k]) * sg * sw )
+ *            dW[n,k] = RNE_bf16( (sum_m qg[m,n] qx[m,k]) * sg * sx )
+ *            with qg = quantize(g, 1/sg); quantising a transposed copy gives
+ *            the transposed codes, so the sums are written on qg, qw, qx.
  *
  * Every function also reports, per output element, the exact-in-double
  * pre-rounding value S and the absolute scale A = sum |a*b| (+ |bias|), which
@@ -60,6 +76,7 @@
 #define ORC_BF16 1
 #define ORC_F16 2
 #define ORC_E4M3 3
+#define ORC_E5M2 4
 
 /* ------------------------------------------------------------------------- */
 /* Decoding: bit pattern -> exact double                                      */
@@ -549,4 +566,179 @@ int orc_grouped_dweights(int dt, const void *input, const void *grad_out,
                          double *s_out, double *a_out, int nthreads) {
     return grp_common(2, dt, input, NULL, grad_out, row_experts, m, k, n, e, rows, nrows, out,
                       s_out, a_out, nthreads);
+}
+
+/* ------------------------------------------------------------------------- */
+/* fp8 producer side: e5m2, quantisation, scaled fp8 linear                   */
+/* ------------------------------------------------------------------------- */
+
+/* OCP fp8 e5m2: sign, 5 exponent bits (bias 15), 2 fraction bits; subnormals
+ * are frac * 2^-16; exponent 31 holds +-inf (frac 0) and NaN.  The largest
+ * finite value is 1.75 * 2^15 = 57344. */
+double orc_decode_e5m2(uint8_t bits) {
+    int sign = (bits >> 7) & 1;
+    int ex = (bits >> 2) & 0x1f;
+    int frac = bits & 0x3;
+    double v;
+    if (ex == 31)
+        v = frac ? NAN : INFINITY;
+    else if (ex == 0)
+        v = ldexp((double)frac, -16);
+    else
+        v = ldexp((double)(4 + frac), ex - 17);
+    return sign ? -v : v;
+}
+
+/* double -> e5m2 bits, RNE, saturating to +-57344 (inf included). */
+uint8_t orc_rne_e5m2_sat(double x) {
+    if (isnan(x)) return 0x7f;
+    int neg = signbit(x) ? 1 : 0;
+    double r = round_mag(fabs(x), 3, -14, 57344.0);
+    if (isinf(r)) r = 57344.0;
+    uint8_t mag;
+    if (r == 0.0) {
+        mag = 0;
+    } else {
+        int e2;
+        frexp(r, &e2);
+        int lead = e2 - 1;
+        if (lead < -14)
+            mag = (uint8_t)ldexp(r, 16);
+        else
+            mag = (uint8_t)(((lead + 15) << 2) | (int)(ldexp(r, 2 - lead) - 4.0));
+    }
+    return (uint8_t)(mag | (neg << 7));
+}
+
+/* One quantised code: the bf16 source times the inverse scale, multiplied in
+ * f32 (an IEEE single multiplication, round to nearest even: the compiler is
+ * told not to contract or widen), then RNE to the fp8 format. */
+static uint8_t quant_code(int fmt, uint16_t src_bits, float scale_inv) {
+    const float raw = (float)orc_decode_bf16(src_bits); /* exact */
+    volatile float v = raw * scale_inv;
+    return fmt == ORC_E5M2 ? orc_rne_e5m2_sat((double)v) : orc_rne_e4m3_sat((double)v);
+}
+
+static float amax_of(const uint16_t *src, int64_t n) {
+    float mx = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        const float a = fabsf((float)orc_decode_bf16(src[i]));
+        if (a > mx) mx = a; /* NaN compares false: ignored */
+    }
+    return mx;
+}
+
+/* src: n bf16 bit patterns; dst: n codes; *amax = max |src|.  fmt: 3 e4m3fn,
+ * 4 e5m2. */
+int orc_fp8_quantize(int fmt, const uint16_t *src, float scale_inv, int64_t n, uint8_t *dst,
+                     float *amax) {
+    if (fmt != ORC_E4M3 && fmt != ORC_E5M2) return -2;
+    for (int64_t i = 0; i < n; ++i) dst[i] = quant_code(fmt, src[i], scale_inv);
+    if (amax) *amax = amax_of(src, n);
+    return 0;
+}
+
+/* src: [rows, cols] bf16, row-major; dst: [cols, rows] codes. */
+int orc_fp8_transpose_quantize(int fmt, const uint16_t *src, float scale_inv, int64_t rows,
+                               int64_t cols, uint8_t *dst, float *amax) {
+    if (fmt != ORC_E4M3 && fmt != ORC_E5M2) return -2;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            dst[c * rows + r] = quant_code(fmt, src[r * cols + c], scale_inv);
+    if (amax) *amax = amax_of(src, rows * cols);
+    return 0;
+}
+
+/* Decoded e4m3 codes of quantize(src, scale_inv) (caller frees). */
+static double *quant_decoded(const uint16_t *src, float scale_inv, int64_t cnt) {
+    double *d = (double *)malloc((size_t)(cnt > 0 ? cnt : 1) * sizeof(double));
+    if (!d) return NULL;
+    for (int64_t i = 0; i < cnt; ++i)
+        d[i] = orc_decode_e4m3(quant_code(ORC_E4M3, src[i], scale_inv));
+    return d;
+}
+
+struct fp8lin_ctx {
+    int op; /* 0 forward, 1 dX, 2 dW */
+    int64_t m, k, n;
+    const double *QX, *QW, *QG, *B;
+    double sa, sb;
+    const int64_t *rows;
+    uint16_t *out;
+    double *s_out, *a_out;
+};
+
+static void fp8lin_row(void *p, int64_t i) {
+    struct fp8lin_ctx *c = (struct fp8lin_ctx *)p;
+    int64_t r = c->rows ? c->rows[i] : i;
+    int64_t ncols = c->op == 0 ? c->n : c->k;
+    double *s = (double *)malloc((size_t)ncols * sizeof(double));
+    double *ab = (double *)malloc((size_t)ncols * sizeof(double));
+    double *arow = NULL;
+    if (c->op == 0) {
+        /* Y[r, j] = sum_k QX[r,k] QW[j,k] : B(k, j) = QW[j*K + k] */
+        row_dot(c->QX + r * c->k, c->k, c->QW, 1, c->k, c->n, s, ab);
+    } else if (c->op == 1) {
+        /* dX[r, j] = sum_n QG[r,n] QW[n,j] : B(n, j) = QW[n*K + j] */
+        row_dot(c->QG + r * c->n, c->n, c->QW, c->k, 1, c->k, s, ab);
+    } else {
+        /* dW[r, j] = sum_m QG[m,r] QX[m,j] : a_row[m] = QG[m*N + r] */
+        arow = (double *)malloc((size_t)(c->m > 0 ? c->m : 1) * sizeof(double));
+        for (int64_t mm = 0; mm < c->m; ++mm) arow[mm] = c->QG[mm * c->n + r];
+        row_dot(arow, c->m, c->QX, c->k, 1, c->k, s, ab);
+    }
+    for (int64_t j = 0; j < ncols; ++j) {
+        double v = s[j] * c->sa * c->sb;
+        double a = ab[j] * fabs(c->sa) * fabs(c->sb);
+        if (c->B) v += c->B[j], a += fabs(c->B[j]);
+        if (c->out) c->out[i * ncols + j] = orc_rne_bf16(v);
+        if (c->s_out) c->s_out[i * ncols + j] = v;
+        if (c->a_out) c->a_out[i * ncols + j] = a;
+    }
+    free(arow);
+    free(s);
+    free(ab);
+}
+
+/* x: [m,k] bf16, w: [n,k] bf16, bias: [n] bf16 or NULL; out: [nrows, n] bf16. */
+int orc_fp8_linear_forward(const uint16_t *x, const uint16_t *w, const uint16_t *bias, float sx,
+                           float sw, float sx_inv, float sw_inv, int64_t m, int64_t k,
+                           int64_t n, const int64_t *rows, int64_t nrows, uint16_t *out,
+                           double *s_out, double *a_out, float *amax_x, float *amax_w,
+                           int nthreads) {
+    struct fp8lin_ctx c;
+    memset(&c, 0, sizeof c);
+    double *QX = quant_decoded(x, sx_inv, m * k);
+    double *QW = quant_decoded(w, sw_inv, n * k);
+    double *B = bias ? decode_all(ORC_BF16, bias, n) : NULL;
+    c.op = 0, c.m = m, c.k = k, c.n = n, c.QX = QX, c.QW = QW, c.B = B;
+    c.sa = (double)sx, c.sb = (double)sw, c.rows = rows;
+    c.out = out, c.s_out = s_out, c.a_out = a_out;
+    run_rows(fp8lin_row, &c, nrows, nthreads);
+    if (amax_x) *amax_x = amax_of(x, m * k);
+    if (amax_w) *amax_w = amax_of(w, n * k);
+    free(QX), free(QW), free(B);
+    return 0;
+}
+
+/* g: [m,n], x: [m,k], w: [n,k] (bf16).  which = 1: dX rows (indices into M),
+ * out [nrows, k]; which = 2: dW rows (indices into N), out [nrows, k]. */
+int orc_fp8_linear_backward(int which, const uint16_t *g, const uint16_t *x, const uint16_t *w,
+                            float sg, float sw, float sx, float sg_inv, float sw_inv,
+                            float sx_inv, int64_t m, int64_t k, int64_t n, const int64_t *rows,
+                            int64_t nrows, uint16_t *out, double *s_out, double *a_out,
+                            float *amax_g, int nthreads) {
+    if (which != 1 && which != 2) return -2;
+    struct fp8lin_ctx c;
+    memset(&c, 0, sizeof c);
+    double *QG = quant_decoded(g, sg_inv, m * n);
+    double *QW = which == 1 ? quant_decoded(w, sw_inv, n * k) : NULL;
+    double *QX = which == 2 ? quant_decoded(x, sx_inv, m * k) : NULL;
+    c.op = which, c.m = m, c.k = k, c.n = n, c.QX = QX, c.QW = QW, c.QG = QG;
+    c.sa = (double)sg, c.sb = which == 1 ? (double)sw : (double)sx, c.rows = rows;
+    c.out = out, c.s_out = s_out, c.a_out = a_out;
+    run_rows(fp8lin_row, &c, nrows, nthreads);
+    if (amax_g) *amax_g = amax_of(g, m * n);
+    free(QG), free(QW), free(QX);
+    return 0;
 }

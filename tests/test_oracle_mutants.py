@@ -38,6 +38,23 @@ MUTANTS = {
                                    "if ((int64_t)c->row_experts[mm] > ee) continue;"),
     "dw_reads_dy_transposed": ("row_dot(arow, c->m, c->DY, c->n, 1, c->n, s, ab);",
                                "row_dot(arow, c->m, c->DY, 1, c->m, c->n, s, ab);"),
+    "e5m2_exponent_bias": ("v = ldexp((double)(4 + frac), ex - 17);",
+                           "v = ldexp((double)(4 + frac), ex - 16);"),
+    "e5m2_no_saturation": ("if (isinf(r)) r = 57344.0;", "if (isinf(r)) r = 49152.0;"),
+    "quantize_product_in_double": ("return fmt == ORC_E5M2 ? orc_rne_e5m2_sat((double)v) : orc_rne_e4m3_sat((double)v);",
+                                   "return fmt == ORC_E5M2 ? orc_rne_e5m2_sat((double)raw * scale_inv) : orc_rne_e4m3_sat((double)raw * scale_inv);"),
+    "quantize_ignores_format": ("return fmt == ORC_E5M2 ? orc_rne_e5m2_sat((double)v) : orc_rne_e4m3_sat((double)v);",
+                                "return orc_rne_e4m3_sat((double)v);"),
+    "transpose_quantize_not_transposed": ("dst[c * rows + r] = quant_code(fmt, src[r * cols + c], scale_inv);",
+                                          "dst[r * cols + c] = quant_code(fmt, src[r * cols + c], scale_inv);"),
+    "amax_signed": ("const float a = fabsf((float)orc_decode_bf16(src[i]));",
+                    "const float a = (float)orc_decode_bf16(src[i]);"),
+    "fp8_linear_bias_dropped": ("if (c->B) v += c->B[j], a += fabs(c->B[j]);",
+                                "if (c->B) a += fabs(c->B[j]);"),
+    "fp8_linear_dx_w_untransposed": ("row_dot(c->QG + r * c->n, c->n, c->QW, c->k, 1, c->k, s, ab);",
+                                     "row_dot(c->QG + r * c->n, c->n, c->QW, 1, c->n, c->k, s, ab);"),
+    "fp8_linear_dw_wrong_scale": ("c.sa = (double)sg, c.sb = which == 1 ? (double)sw : (double)sx, c.rows = rows;",
+                                  "c.sa = (double)sg, c.sb = (double)sw, c.rows = rows;"),
     "f16_overflow_saturates": ("double r = round_mag(fabs(x), 11, -14, 65504.0);\n    uint16_t mag;\n    if (isinf(r)) {\n        mag = 0x7c00;",
                                "double r = round_mag(fabs(x), 11, -14, 65504.0);\n    uint16_t mag;\n    if (isinf(r)) {\n        mag = 0x7bff;"),
 }

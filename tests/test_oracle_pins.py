@@ -423,3 +423,139 @@ def test_empty_reduction_is_positive_zero_plus_bias():
     assert np.array_equal(y.out, np.tile(b, (3, 1)))
     dw = oracle.linear_dw(dt, np.zeros((0, 4), np.uint16), np.zeros((0, 5), np.uint16), 0, 4, 5)
     assert np.all(dw.out == 0)
+
+
+# ---------------------------------------------------------------------------
+# fp8 producer side: e5m2, quantisation, scaled fp8 linear
+# ---------------------------------------------------------------------------
+
+def test_decode_e5m2_exhaustive_vs_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+    for c in range(256):
+        assert _same(oracle.decode_e5m2(c), ref[c]), hex(c)
+    assert oracle.decode_e5m2(0x7B) == 57344.0          # largest finite
+    assert oracle.decode_e5m2(0x7C) == math.inf
+    assert oracle.decode_e5m2(0x01) == 2.0 ** -16       # smallest subnormal
+    assert oracle.decode_e5m2(0x04) == 2.0 ** -14       # smallest normal
+
+
+E4M3_MAX, E5M2_MAX = Fraction(448), Fraction(57344)
+
+
+def _exact_round_sat(x, p, emin, max_finite):
+    r = _exact_round(x, p, emin, max_finite)
+    # _exact_round reports overflow as +-10^400; saturation keeps the sign
+    return (max_finite if x > 0 else -max_finite) if abs(r) > max_finite else r
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_encoders_vs_exact_rational_and_torch(fmt):
+    enc, dec = ((oracle.rne_e4m3_sat, oracle.decode_e4m3) if fmt == "e4m3"
+                else (oracle.rne_e5m2_sat, oracle.decode_e5m2))
+    p, emin, mx = (4, -6, E4M3_MAX) if fmt == "e4m3" else (3, -14, E5M2_MAX)
+    tdt = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e5m2
+    xs = list(_random_doubles(3000, emin - 4, 18, 11))
+    # every representable value and every midpoint between neighbours
+    vals = sorted({dec(c) for c in range(256) if math.isfinite(dec(c)) and dec(c) >= 0})
+    xs += vals + [(a + b) / 2 for a, b in zip(vals, vals[1:])]
+    xs += [-v for v in xs] + [1e30, -1e30, float(mx) * 1.03, float(mx) * 1.1]
+    for x in map(float, xs):
+        code = enc(x)
+        assert dec(code) == _exact_round_sat(x, p, emin, mx), (fmt, x)
+        # torch's cast is an independent correctly rounded conversion (it
+        # does not saturate, so only in-range values are compared)
+        if abs(x) <= float(mx) and x != 0.0:
+            ref = int(torch.tensor([x], dtype=torch.float64).to(tdt).view(torch.uint8)[0])
+            assert code == ref, (fmt, x)
+
+
+def _bf16(vals):
+    return synth.to_bits(np.asarray(vals, dtype=np.float32), synth.BF16)
+
+
+def test_quantize_hand_cases():
+    # bf16 sources times scale_inv = 2, e4m3fn codes written out by hand from
+    # the format definition: 2.0 = 0x40, -3.0 = 0xC4, 6.0 = 0x4C, +0, -0, 2000
+    # saturates to 448 = 0x7E, 2^-9 is the smallest subnormal 0x01
+    src = _bf16([1.0, -1.5, 3.0, 0.0, -0.0, 1000.0, 2.0 ** -10])
+    codes, amax = oracle.fp8_quantize(oracle.E4M3, src, 2.0)
+    assert list(codes) == [0x40, 0xC4, 0x4C, 0x00, 0x80, 0x7E, 0x01]
+    assert amax == 1000.0
+    # e5m2: 2.0 = 0x40, -3.0 = 0xC2, 6.0 = 0x46, 2000 = 1.953125 * 2^10 ->
+    # RNE to 2048 = 0x68 (1.75*2^10 = 1792 and 2048 are the neighbours)
+    codes, _ = oracle.fp8_quantize(oracle.E5M2, src, 2.0)
+    assert list(codes[[0, 1, 2, 5]]) == [0x40, 0xC2, 0x46, 0x68]
+    # transposed: [2,3] -> [3,2], element (r, c) lands at (c, r)
+    src = _bf16([[1.0, 2.0, 4.0], [-1.0, -2.0, 0.5]])
+    t, amax = oracle.fp8_transpose_quantize(oracle.E4M3, src, 1.0, 2, 3)
+    assert t.tolist() == [[0x38, 0xB8], [0x40, 0xC0], [0x48, 0x30]] and amax == 4.0
+
+
+def test_quantize_rounds_the_product_to_f32_first():
+    # raw = 1 + 2^-7 (bf16), scale_inv = the f32 value just above
+    # 1.0625 / raw.  The exact product is a hair above the e4m3 midpoint
+    # 1.0625 (between 1.0 and 1.125) and would round up; rounded to f32 first
+    # it is exactly the midpoint and goes to the even neighbour 1.0 (0x38).
+    raw = Fraction(1) + Fraction(1, 128)
+    target = Fraction(17, 16) / raw
+    s = np.float32(float(target))
+    if Fraction(float(s)) < target:
+        s = np.nextafter(s, np.float32(2))
+    prod = raw * Fraction(float(s))
+    assert prod > Fraction(17, 16) and prod - Fraction(17, 16) < Fraction(1, 2 ** 24)
+    codes, _ = oracle.fp8_quantize(oracle.E4M3, _bf16([1 + 2.0 ** -7]), float(s))
+    assert codes[0] == 0x38
+
+
+def _torch_quant(bits, scale_inv, dt=torch.float8_e4m3fn):
+    """Independent quantisation: f32 product by torch, then torch's fp8 cast
+    (values stay inside the format's range here, where it agrees with the
+    saturating rule)."""
+    f = torch.from_numpy(synth.to_f32(bits, synth.BF16).astype(np.float32))
+    q = (f * torch.tensor(np.float32(scale_inv))).to(dt)
+    return q.to(torch.float64).numpy()
+
+
+def test_fp8_linear_forward_vs_numpy():
+    m, k, n = 37, 150, 29
+    d = synth.linear(m, k, n, synth.BF16, seed=5, sigma_w=1.0)
+    x, b = d["x"], d["b"]
+    w = synth.normal_bits((n, k), 1.0, 5, 9, synth.BF16)        # [N,K]
+    sx_inv, sw_inv, sx, sw = 96.0, 80.0, 1 / 96.0, 1 / 80.0
+    r = oracle.fp8_linear_forward(x, w, b, sx, sw, sx_inv, sw_inv, m, k, n)
+    qx, qw = _torch_quant(x, sx_inv), _torch_quant(w, sw_inv)
+    S = (qx @ qw.T) * float(np.float32(sx)) * float(np.float32(sw)) \
+        + synth.to_f32(b, synth.BF16).astype(np.float64)
+    assert np.allclose(r.s, S, rtol=1e-12, atol=1e-12)
+    assert r.amax_x == np.abs(synth.to_f32(x, synth.BF16)).max()
+    assert r.amax_w == np.abs(synth.to_f32(w, synth.BF16)).max()
+    # integer codes with unit scales: every step exact, so the rounded output
+    # is the exact integer result
+    xi = _bf16(np.random.default_rng(3).integers(-6, 7, (m, k)))
+    wi = _bf16(np.random.default_rng(4).integers(-6, 7, (n, k)))
+    bi = _bf16(np.random.default_rng(5).integers(-9, 10, n))
+    r = oracle.fp8_linear_forward(xi, wi, bi, 1.0, 1.0, 1.0, 1.0, m, k, n)
+    ref = synth.to_f32(xi, synth.BF16).astype(np.int64) @ \
+        synth.to_f32(wi, synth.BF16).astype(np.int64).T + synth.to_f32(bi, synth.BF16).astype(np.int64)
+    assert np.array_equal(r.out, _bf16(ref.astype(np.float32)))
+
+
+def test_fp8_linear_backward_vs_numpy():
+    m, k, n = 41, 70, 53
+    g = synth.normal_bits((m, n), 1.0, 6, 1, synth.BF16)
+    x = synth.normal_bits((m, k), 1.0, 6, 2, synth.BF16)
+    w = synth.normal_bits((n, k), 0.5, 6, 3, synth.BF16)
+    sg_inv, sw_inv, sx_inv = 100.0, 150.0, 90.0
+    sg, sw, sx = 1 / sg_inv, 1 / sw_inv, 1 / sx_inv
+    f = lambda v: float(np.float32(v))
+    rdx = oracle.fp8_linear_backward("dx", g, x, w, sg, sw, sx, sg_inv, sw_inv, sx_inv, m, k, n)
+    rdw = oracle.fp8_linear_backward("dw", g, x, w, sg, sw, sx, sg_inv, sw_inv, sx_inv, m, k, n)
+    qg, qw, qx = _torch_quant(g, sg_inv), _torch_quant(w, sw_inv), _torch_quant(x, sx_inv)
+    assert np.allclose(rdx.s, (qg @ qw) * f(sg) * f(sw), rtol=1e-12, atol=1e-12)
+    assert np.allclose(rdw.s, (qg.T @ qx) * f(sg) * f(sx), rtol=1e-12, atol=1e-12)
+    assert rdx.amax_g == np.abs(synth.to_f32(g, synth.BF16)).max()
+    # row selection gives the same rows
+    sel = oracle.fp8_linear_backward("dw", g, x, w, sg, sw, sx, sg_inv, sw_inv, sx_inv, m, k, n,
+                                     rows=[0, 17, 52])
+    assert np.array_equal(sel.out, rdw.out[[0, 17, 52]])
