@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbi.so")
 
 BI_F32, BI_BF16, BI_F16 = 0, 1, 2
+BI_FP8_E4M3, BI_FP8_E5M2 = 3, 4
 BI_OK = 0
 STATUS = {0: "BI_OK", -1: "BI_ERR_NULL", -2: "BI_ERR_DTYPE", -3: "BI_ERR_SHAPE",
           -4: "BI_ERR_TOO_LARGE", -5: "BI_ERR_WORKSPACE", -6: "BI_ERR_HIP",
@@ -51,6 +52,15 @@ def load() -> ctypes.CDLL:
     L.bi_grouped_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, i32]
     L.bi_grouped_nt_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
                                          vp, i32]
+    L.bi_fp8_quantize.argtypes = [vp, vp, vp, vp, i64, i32, vp]
+    L.bi_fp8_transpose_quantize.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
+    L.bi_fp8_linear_workspace_bytes.argtypes = [i64, i64, i64]
+    L.bi_fp8_linear_workspace_bytes.restype = sz
+    L.bi_fp8_linear_forward.argtypes = [vp] * 10 + [i64] * 3 + [vp, sz, vp, i32]
+    L.bi_fp8_linear_backward.argtypes = [vp] * 12 + [i64] * 3 + [vp, sz, vp, i32]
+    for f in ("bi_fp8_quantize", "bi_fp8_transpose_quantize", "bi_fp8_linear_forward",
+              "bi_fp8_linear_backward"):
+        getattr(L, f).restype = i32
     L.bi_status_string.argtypes = [i32]
     L.bi_status_string.restype = ctypes.c_char_p
     L.bi_plan.argtypes = [i32, i32, i32, i64, i64, ctypes.POINTER(i64)]
@@ -110,6 +120,33 @@ def bi_backward_dw(dw, x, dy, m, k, n, dtype, workspace, workspace_bytes, stream
 def bi_fp8_mm(y, a, bt, a_dequant, b_dequant, m, k, n, stream=None, tc=1) -> int:
     return load().bi_fp8_mm(_p(y), _p(a), _p(bt), _p(a_dequant), _p(b_dequant), m, k, n,
                             _s(stream), tc)
+
+
+def bi_fp8_quantize(dst, src, scale_inv, amax, n, fmt, stream=None) -> int:
+    return load().bi_fp8_quantize(_p(dst), _p(src), _p(scale_inv), _p(amax), n, fmt, _s(stream))
+
+
+def bi_fp8_transpose_quantize(dst, src, scale_inv, amax, rows, cols, fmt, stream=None) -> int:
+    return load().bi_fp8_transpose_quantize(_p(dst), _p(src), _p(scale_inv), _p(amax), rows,
+                                            cols, fmt, _s(stream))
+
+
+def bi_fp8_linear_workspace_bytes(m, k, n) -> int:
+    return load().bi_fp8_linear_workspace_bytes(m, k, n)
+
+
+def bi_fp8_linear_forward(y, x, w, bias, sx, sw, sx_inv, sw_inv, amax_x, amax_w, m, k, n,
+                          workspace, workspace_bytes, stream=None, tc=1) -> int:
+    return load().bi_fp8_linear_forward(_p(y), _p(x), _p(w), _p(bias), _p(sx), _p(sw),
+                                        _p(sx_inv), _p(sw_inv), _p(amax_x), _p(amax_w), m, k, n,
+                                        _p(workspace), workspace_bytes, _s(stream), tc)
+
+
+def bi_fp8_linear_backward(dx, dw, g, x, w, sg, sw, sx, sg_inv, sw_inv, sx_inv, amax_g, m, k, n,
+                           workspace, workspace_bytes, stream=None, tc=1) -> int:
+    return load().bi_fp8_linear_backward(_p(dx), _p(dw), _p(g), _p(x), _p(w), _p(sg), _p(sw),
+                                         _p(sx), _p(sg_inv), _p(sw_inv), _p(sx_inv), _p(amax_g),
+                                         m, k, n, _p(workspace), workspace_bytes, _s(stream), tc)
 
 
 def bi_grouped_nt(y, inp, weights, row_experts, offsets, m, k, n, e, dtype, stream=None,

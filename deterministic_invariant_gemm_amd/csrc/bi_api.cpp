@@ -289,9 +289,15 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
     return hip_status(e);
 }
 
-int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
-              const float *b_dequant, int64_t m, int64_t k, int64_t n, hipStream_t stream,
-              int tc) {
+}  // extern "C"
+
+namespace {
+
+// Y = RNE_bf16((A B^T) * a_dequant * b_dequant [+ bias]): the fp8 GEMM behind
+// bi_fp8_mm and the scaled fp8 linear.  Validates like bi_fp8_mm.
+int fp8_gemm(void *y, const void *a, const void *bt, const float *a_dequant,
+             const float *b_dequant, const void *bias, int64_t m, int64_t k, int64_t n,
+             hipStream_t stream, int tc) {
     if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
     if (checked_elems(m, k) < 0 || checked_elems(n, k) < 0 || checked_elems(m, n) < 0)
         return BI_ERR_TOO_LARGE;
@@ -303,6 +309,7 @@ int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
         s.a = a; s.a_is = k; s.a_rs = 1;
         s.b = bt; s.b_rs = 1; s.b_js = k;
         s.scale_a = a_dequant; s.scale_b = b_dequant;
+        s.bias = bias;
         s.c = y; s.ldc = n;
         s.rows = m; s.cols = n; s.red = k; s.chunk = kNoSplit; s.nchunks = 1;
         s.tiles_i = cdiv(m, 64); s.tiles_j = cdiv(n, 64);
@@ -316,6 +323,7 @@ int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
         d.vec_a = d.vec_b = 1;
         d.vec_c = aligned8(y) && n % 4 == 0;
         d.scale_a = a_dequant; d.scale_b = b_dequant;
+        d.bias = bias;
         const int tile = direct_tile(d, batch_tile(pl, tc, m, n), m * k, n * k);
         return hip_status(launch_fp8_dl(d, tile, stream));
     }
@@ -329,11 +337,118 @@ int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
     f.bt = static_cast<const uint8_t *>(bt);
     f.c = static_cast<uint16_t *>(y);
     f.scale_a = a_dequant; f.scale_b = b_dequant;
+    f.bias = static_cast<const uint16_t *>(bias);
     f.m = m; f.n = n; f.k = k;
     f.tiles_i = cdiv(m, ts->bm); f.tiles_j = cdiv(n, ts->bn);
     f.vec = vec;
     f.vec_c = aligned8(y) && n % 4 == 0;
     return hip_status(launch_fp8_gemm(f, tile, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
+              const float *b_dequant, int64_t m, int64_t k, int64_t n, hipStream_t stream,
+              int tc) {
+    return fp8_gemm(y, a, bt, a_dequant, b_dequant, nullptr, m, k, n, stream, tc);
+}
+
+static bool fp8_fmt_ok(int fmt) { return fmt == BI_FP8_E4M3 || fmt == BI_FP8_E5M2; }
+static size_t align256(int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); }
+
+int bi_fp8_quantize(void *dst, const void *src, const float *scale_inv, float *amax, int64_t n,
+                    int fmt, hipStream_t stream) {
+    if (!fp8_fmt_ok(fmt)) return BI_ERR_DTYPE;
+    if (n < 0) return BI_ERR_SHAPE;
+    if (n > kMaxElems) return BI_ERR_TOO_LARGE;
+    if (n == 0) return BI_OK;
+    if (!dst || !src || !scale_inv) return BI_ERR_NULL;
+    return hip_status(launch_quantize(src, scale_inv, dst, amax, n, fmt, stream));
+}
+
+int bi_fp8_transpose_quantize(void *dst, const void *src, const float *scale_inv, float *amax,
+                              int64_t rows, int64_t cols, int fmt, hipStream_t stream) {
+    if (!fp8_fmt_ok(fmt)) return BI_ERR_DTYPE;
+    if (rows < 0 || cols < 0) return BI_ERR_SHAPE;
+    if (checked_elems(rows, cols) < 0 || rows > (int64_t)65535 * 64) return BI_ERR_TOO_LARGE;
+    if (rows == 0 || cols == 0) return BI_OK;
+    if (!dst || !src || !scale_inv) return BI_ERR_NULL;
+    return hip_status(launch_transpose_quantize(src, scale_inv, dst, amax, rows, cols, fmt,
+                                                stream));
+}
+
+size_t bi_fp8_linear_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+    if (m < 0 || k < 0 || n < 0) return 0;
+    if (checked_elems(m, k) < 0 || checked_elems(n, k) < 0 || checked_elems(m, n) < 0) return 0;
+    const size_t fwd = align256(m * k) + align256(n * k);
+    const size_t bwd = align256(m * n) + align256(k * n) + align256(n * m) + align256(k * m) + 256;
+    return fwd > bwd ? fwd : bwd;
+}
+
+int bi_fp8_linear_forward(void *y, const void *x, const void *w, const void *bias,
+                          const float *sx, const float *sw, const float *sx_inv,
+                          const float *sw_inv, float *amax_x, float *amax_w, int64_t m,
+                          int64_t k, int64_t n, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream, int tc) {
+    if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, k) < 0 || checked_elems(n, k) < 0 || checked_elems(m, n) < 0 ||
+        m > (int64_t)65535 * 64 || n > (int64_t)65535 * 64)
+        return BI_ERR_TOO_LARGE;
+    if (!sx || !sw || !sx_inv || !sw_inv) return BI_ERR_NULL;
+    if ((m > 0 && n > 0 && !y) || (m * k > 0 && !x) || (n * k > 0 && !w)) return BI_ERR_NULL;
+    const size_t need = align256(m * k) + align256(n * k);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return BI_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    void *x8 = ws, *w8 = ws + align256(m * k);
+    if (amax_x || amax_w)
+        if (launch_zero3(amax_x, amax_w, nullptr, stream) != hipSuccess) return BI_ERR_HIP;
+    int st = bi_fp8_quantize(x8, x, sx_inv, amax_x, m * k, BI_FP8_E4M3, stream);
+    if (st != BI_OK) return st;
+    st = bi_fp8_quantize(w8, w, sw_inv, amax_w, n * k, BI_FP8_E4M3, stream);
+    if (st != BI_OK) return st;
+    return fp8_gemm(y, x8, w8, sx, sw, bias, m, k, n, stream, tc);
+}
+
+int bi_fp8_linear_backward(void *dx, void *dw, const void *g, const void *x, const void *w,
+                           const float *sg, const float *sw, const float *sx,
+                           const float *sg_inv, const float *sw_inv, const float *sx_inv,
+                           float *amax_g, int64_t m, int64_t k, int64_t n, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream, int tc) {
+    if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, k) < 0 || checked_elems(n, k) < 0 || checked_elems(m, n) < 0 ||
+        m > (int64_t)65535 * 64 || n > (int64_t)65535 * 64)
+        return BI_ERR_TOO_LARGE;
+    if (!sg || !sw || !sx || !sg_inv || !sw_inv || !sx_inv) return BI_ERR_NULL;
+    if ((m * n > 0 && !g) || (dx && n * k > 0 && !w) || (dw && m * k > 0 && !x))
+        return BI_ERR_NULL;
+    const size_t o_wt = align256(m * n), o_gt = o_wt + align256(k * n);
+    const size_t o_xt = o_gt + align256(n * m), o_amax = o_xt + align256(k * m);
+    const size_t need = o_amax + 256;
+    if (!workspace || workspace_bytes < need) return BI_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    float *scratch = reinterpret_cast<float *>(ws + o_amax);  // amax of the transposed copies
+    if (launch_zero3(amax_g, scratch, nullptr, stream) != hipSuccess) return BI_ERR_HIP;
+    int st = bi_fp8_quantize(ws, g, sg_inv, amax_g, m * n, BI_FP8_E4M3, stream);
+    if (st != BI_OK) return st;
+    if (dx && m > 0 && k > 0) {
+        // dX[m,k] = (g8[m,n] . wt8[k,n]^T) * sg * sw
+        st = bi_fp8_transpose_quantize(ws + o_wt, w, sw_inv, scratch, n, k, BI_FP8_E4M3, stream);
+        if (st != BI_OK) return st;
+        st = fp8_gemm(dx, ws, ws + o_wt, sg, sw, nullptr, m, n, k, stream, tc);
+        if (st != BI_OK) return st;
+    }
+    if (dw && n > 0 && k > 0) {
+        // dW[n,k] = (gt8[n,m] . xt8[k,m]^T) * sg * sx
+        st = bi_fp8_transpose_quantize(ws + o_gt, g, sg_inv, scratch, m, n, BI_FP8_E4M3, stream);
+        if (st != BI_OK) return st;
+        st = bi_fp8_transpose_quantize(ws + o_xt, x, sx_inv, scratch, m, k, BI_FP8_E4M3, stream);
+        if (st != BI_OK) return st;
+        st = fp8_gemm(dw, ws + o_gt, ws + o_xt, sg, sx, nullptr, n, m, k, stream, tc);
+        if (st != BI_OK) return st;
+    }
+    return BI_OK;
 }
 
 static int grouped_validate(int64_t m, int64_t k, int64_t n, int64_t e, int dtype) {

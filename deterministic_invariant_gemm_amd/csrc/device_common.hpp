@@ -10,7 +10,7 @@
 
 namespace bi {
 
-enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_E4M3 = 3 };
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -191,6 +191,7 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
                 for (int x = 0; x < 4; ++x) {
                     float v = acc[i][j][4 * g4 + x] * sa_v;
                     v = v * sb_v;
+                    if (p.bias && gj + x < p.n) v = v + bf16_bits_to_f32(p.bias[gj + x]);
                     h[x] = f32_to_bf16_bits(v);
                 }
                 uint16_t *pc = p.c + gi * p.n + gj;

@@ -75,6 +75,7 @@ struct Fp8Args {
     const uint8_t *bt;  // [n,k]
     uint16_t *c;        // [m,n] bf16
     const float *scale_a, *scale_b;
+    const uint16_t *bias;  // [n] bf16 or null, added after the scales
     int64_t m, n, k;
     int64_t tiles_i, tiles_j;
     int vec;    // 16-byte vector loads allowed
@@ -104,5 +105,15 @@ hipError_t launch_fp8_gemm(const Fp8Args &p, int tile_id, hipStream_t s);
 // C(i,j) = RNE_bf16((sum_r A(i,r) B(j,r)) * scale_a * scale_b), both operands
 // reduction-contiguous e4m3 bytes.
 hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, hipStream_t s);
+// fp8 quantisation (quant.hip): fmt DT_E4M3 or DT_E5M2; amax (nullable)
+// receives max(*amax, max |src|).  quantize: n elements; transpose_quantize:
+// src [rows, cols] -> dst [cols, rows].
+hipError_t launch_quantize(const void *src, const float *scale_inv, void *dst, float *amax,
+                           int64_t n, int fmt, hipStream_t s);
+hipError_t launch_transpose_quantize(const void *src, const float *scale_inv, void *dst,
+                                     float *amax, int64_t rows, int64_t cols, int fmt,
+                                     hipStream_t s);
+// *a = *b = *c = +0 (null pointers skipped), one tiny kernel
+hipError_t launch_zero3(float *a, float *b, float *c, hipStream_t s);
 
 }  // namespace bi

@@ -285,7 +285,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     using Frag = typename TY::Frag;
     static_assert(DT != DT_E4M3 || (A_RC && B_RC), "fp8 operands are reduction-contiguous");
     static_assert(slab_bytes<EPI, WTN, NW>() <= NS * (SA + SB), "epilogue slabs fit in the stages");
-    static_assert(EPI != EPI_ROUND || BN <= 64 * NW, "one thread per bias column");
+    static_assert((EPI != EPI_ROUND && EPI != EPI_SCALE) || BN <= 64 * NW,
+                  "one thread per bias column");
 
     // NS stages of [A | B]; reused by the epilogue
     __shared__ __align__(1024) char lds_raw[NS * (SA + SB)];

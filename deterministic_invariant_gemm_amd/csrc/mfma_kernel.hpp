@@ -51,7 +51,7 @@ constexpr int KG = BK / 8;  // 8-element groups per slice
 constexpr int NT = 256;     // threads per workgroup (4 waves)
 
 enum Mode : int { MODE_PLAIN = 0, MODE_SEGMENTS = 1, MODE_EXPERT_RED = 2 };
-// EPI_SCALE: fp8 output, RNE_bf16((acc * scale_a) * scale_b)
+// EPI_SCALE: fp8 operands, RNE_bf16((acc * scale_a) * scale_b [+ bias])
 enum Epi : int { EPI_ROUND = 0, EPI_PARTIAL = 1, EPI_F32 = 2, EPI_SCALE = 3 };
 
 __device__ __forceinline__ int swz(int row, int kg) {
@@ -385,11 +385,12 @@ __device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
 // LDS by the epilogue (write_tile), so its latency hides behind the K loop.
 template <int DT, int EPI, int BN>
 __device__ __forceinline__ float fetch_bias(const MfmaArgs &p, int64_t col0, int t) {
-    if constexpr (EPI == EPI_ROUND) {
+    if constexpr (EPI == EPI_ROUND || EPI == EPI_SCALE) {
         if (p.bias && t < BN) {
             const int64_t j = col0 + t < p.cols ? col0 + t : p.cols - 1;
             const uint16_t b = static_cast<const uint16_t *>(p.bias)[j];
-            return DT == DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+            // the bias has the output's 16-bit type (bf16 for fp8 operands)
+            return DT == DT_F16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
         }
     }
     return 0.0f;
@@ -423,7 +424,7 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
     static_assert(ROWB % 16 == 0, "slab rows are whole 16-byte chunks");
     char *slab = lds + wave * 32 * ROWP;
     const bool vec_c = p.vec_c != 0;
-    if constexpr (EPI == EPI_ROUND) {
+    if constexpr (EPI == EPI_ROUND || EPI == EPI_SCALE) {
         const int t = wave * 64 + lane;
         if (p.bias && t < BN) bias_l[t] = bias_v;
     }
@@ -432,7 +433,7 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
     if constexpr (EPI == EPI_SCALE) scale_a = p.scale_a[0], scale_b = p.scale_b[0];
     // this lane's bias columns, read from LDS once for all row slabs
     f32x4 bias_r[FN][4];
-    if constexpr (EPI == EPI_ROUND) {
+    if constexpr (EPI == EPI_ROUND || EPI == EPI_SCALE) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -460,6 +461,10 @@ __device__ __forceinline__ void write_tile(const MfmaArgs &p, const TileInfo &ti
                 } else if constexpr (EPI == EPI_SCALE) {
 #pragma unroll
                     for (int x = 0; x < 4; ++x) v[x] = (v[x] * scale_a) * scale_b;
+                    if (p.bias) {
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) v[x] = v[x] + bias_r[j][g][x];
+                    }
                     *reinterpret_cast<u32x2 *>(dst) = u32x2{pack2_rne<DT_BF16>(v[0], v[1]),
                                                             pack2_rne<DT_BF16>(v[2], v[3])};
                 } else {

@@ -1,0 +1,208 @@
+// fp8 quantisation (AstrAI fp8_mm.cu: quantize_kernel, transpose_quantize_kernel
+// and cast_fp8): every bf16 element times the inverse scale, multiplied in f32,
+// converted to OCP e4m3fn or e5m2 with round-to-nearest-even, values beyond the
+// largest finite one saturating to it (NaN stays NaN); the max-abs of the
+// unscaled source is folded into *amax (NaN ignored).  The max of non-negative
+// floats is the max of their bit patterns read as unsigned integers, so one
+// atomic max per workgroup gives the same result in any order.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace bi {
+
+namespace {
+
+constexpr int QT = 256;  // threads per workgroup
+
+template <int FMT>
+__device__ __forceinline__ float saturate(float v) {
+    constexpr float M = FMT == DT_E5M2 ? 57344.0f : 448.0f;
+    return v > M ? M : (v < -M ? -M : v);  // NaN: both tests false, passes through
+}
+
+// two f32 values -> two fp8 codes in bytes 0-1 (HI false) or 2-3 (HI true) of `old`
+template <int FMT, bool HI>
+__device__ __forceinline__ int cvt2(float a, float b, int old) {
+    a = saturate<FMT>(a);
+    b = saturate<FMT>(b);
+    if constexpr (FMT == DT_E5M2) return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+    else return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint8_t cvt1(float a) {
+    return (uint8_t)(cvt2<FMT, false>(a, 0.0f, 0) & 0xff);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// max over the workgroup, then one atomic max on the bit pattern
+__device__ __forceinline__ void fold_amax(float mx, float *amax) {
+    __shared__ float part[QT / 64];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = part[0];
+#pragma unroll
+        for (int w = 1; w < QT / 64; ++w) m = fmaxf(m, part[w]);
+        atomicMax(reinterpret_cast<unsigned int *>(amax), __float_as_uint(m));
+    }
+}
+
+// vec: src and dst 16-byte aligned; 16 elements per thread and step, the
+// n % 16 tail element by element
+template <int FMT>
+__global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t *src, const float *scale_inv,
+                                                      uint8_t *dst, float *amax, int64_t n,
+                                                      int vec) {
+    const float s = *scale_inv;
+    float mx = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * QT;
+    const int64_t tid = (int64_t)blockIdx.x * QT + threadIdx.x;
+    int64_t done = 0;
+    if (vec) {
+        const int64_t nchunk = n / 16;
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
+        for (int64_t c = tid; c < nchunk; c += stride) {
+            const u32x4 a = __builtin_nontemporal_load(s4 + 2 * c);
+            const u32x4 b = __builtin_nontemporal_load(s4 + 2 * c + 1);
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            int o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float f0 = lo_bf16(w[2 * q]), f1 = hi_bf16(w[2 * q]);
+                const float f2 = lo_bf16(w[2 * q + 1]), f3 = hi_bf16(w[2 * q + 1]);
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))));
+                o[q] = cvt2<FMT, true>(f2 * s, f3 * s, cvt2<FMT, false>(f0 * s, f1 * s, 0));
+            }
+            reinterpret_cast<u32x4 *>(dst)[c] =
+                u32x4{(uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]};
+        }
+        done = nchunk * 16;
+    }
+    for (int64_t i = done + tid; i < n; i += stride) {
+        const float f = bf16_bits_to_f32(src[i]);
+        mx = fmaxf(mx, fabsf(f));
+        dst[i] = cvt1<FMT>(f * s);
+    }
+    if (amax) fold_amax(mx, amax);
+}
+
+// [rows, cols] -> [cols, rows] through a 64 x 64 byte tile in LDS.
+// vec_in: cols % 8 == 0 and src 16-byte aligned; vec_out: rows % 16 == 0 and
+// dst 16-byte aligned.
+template <int FMT>
+__global__ __launch_bounds__(QT) void transpose_quantize_kernel(
+    const uint16_t *src, const float *scale_inv, uint8_t *dst, float *amax, int64_t rows,
+    int64_t cols, int vec_in, int vec_out) {
+    __shared__ uint32_t tile[64][64 / 4 + 1];  // bytes of row r at tile[r][..], padded
+    const float s = *scale_inv;
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int t = threadIdx.x;
+    float mx = 0.0f;
+    {
+        // thread t: tile row t / 4, columns 16 * (t % 4) .. +15
+        const int rr = t >> 2, cc = 16 * (t & 3);
+        const int64_t gr = r0 + rr, gc = c0 + cc;
+        float f[16];
+        if (vec_in && gr < rows && gc + 16 <= cols) {
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(src + gr * cols + gc);
+            const u32x4 a = p[0], b = p[1];
+            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) f[2 * q] = lo_bf16(w[q]), f[2 * q + 1] = hi_bf16(w[q]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                f[q] = (gr < rows && gc + q < cols) ? bf16_bits_to_f32(src[gr * cols + gc + q])
+                                                    : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            mx = fmaxf(mx, fmaxf(fmaxf(fabsf(f[4 * q]), fabsf(f[4 * q + 1])),
+                                 fmaxf(fabsf(f[4 * q + 2]), fabsf(f[4 * q + 3]))));
+            tile[rr][cc / 4 + q] = (uint32_t)cvt2<FMT, true>(
+                f[4 * q + 2] * s, f[4 * q + 3] * s, cvt2<FMT, false>(f[4 * q] * s, f[4 * q + 1] * s, 0));
+        }
+    }
+    __syncthreads();
+    {
+        // thread t: output row c0 + t / 4, source rows 16 * (t % 4) .. +15
+        const int oc = t >> 2, rb = 16 * (t & 3);
+        const int64_t go = c0 + oc, gr = r0 + rb;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t b = (tile[rb + i][oc >> 2] >> (8 * (oc & 3))) & 0xffu;
+            w[i >> 2] |= b << (8 * (i & 3));
+        }
+        if (go < cols) {
+            uint8_t *d = dst + go * rows + gr;
+            if (vec_out && gr + 16 <= rows) {
+                *reinterpret_cast<u32x4 *>(d) = u32x4{w[0], w[1], w[2], w[3]};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (gr + i < rows) d[i] = (uint8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xffu);
+            }
+        }
+    }
+    if (amax) fold_amax(mx, amax);
+}
+
+__global__ void zero_kernel(float *a, float *b, float *c) {
+    if (threadIdx.x == 0) {
+        if (a) *a = 0.0f;
+        if (b) *b = 0.0f;
+        if (c) *c = 0.0f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *src, const float *scale_inv, void *dst, float *amax,
+                           int64_t n, int fmt, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+    int64_t grid = (n / 16 + QT - 1) / QT;
+    if (grid < 1) grid = 1;
+    if (grid > 2048) grid = 2048;
+    const uint16_t *sp = static_cast<const uint16_t *>(src);
+    uint8_t *dp = static_cast<uint8_t *>(dst);
+    if (fmt == DT_E5M2)
+        hipLaunchKernelGGL(quantize_kernel<DT_E5M2>, dim3(grid), dim3(QT), 0, s, sp, scale_inv, dp,
+                           amax, n, vec);
+    else
+        hipLaunchKernelGGL(quantize_kernel<DT_E4M3>, dim3(grid), dim3(QT), 0, s, sp, scale_inv, dp,
+                           amax, n, vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_quantize(const void *src, const float *scale_inv, void *dst,
+                                     float *amax, int64_t rows, int64_t cols, int fmt,
+                                     hipStream_t s) {
+    if (rows <= 0 || cols <= 0) return hipSuccess;
+    const int64_t gx = (cols + 63) / 64, gy = (rows + 63) / 64;
+    if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
+    const int vec_in = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+    const int vec_out = rows % 16 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+    const uint16_t *sp = static_cast<const uint16_t *>(src);
+    uint8_t *dp = static_cast<uint8_t *>(dst);
+    if (fmt == DT_E5M2)
+        hipLaunchKernelGGL(transpose_quantize_kernel<DT_E5M2>, dim3(gx, gy), dim3(QT), 0, s, sp,
+                           scale_inv, dp, amax, rows, cols, vec_in, vec_out);
+    else
+        hipLaunchKernelGGL(transpose_quantize_kernel<DT_E4M3>, dim3(gx, gy), dim3(QT), 0, s, sp,
+                           scale_inv, dp, amax, rows, cols, vec_in, vec_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero3(float *a, float *b, float *c, hipStream_t s) {
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, a, b, c);
+    return hipGetLastError();
+}
+
+}  // namespace bi

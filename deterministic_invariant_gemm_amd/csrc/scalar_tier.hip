@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
                 if constexpr (EPI == EPI_FP8) {
                     v = v * p.scale_a[0];
                     v = v * p.scale_b[0];
+                    if (p.bias) v = v + load_elem<DT_OUT>(p.bias, gj);  // bf16 bias
                 } else {
                     if (p.bias) v = v + load_elem<DT_IN>(p.bias, gj);
                 }

@@ -7,6 +7,11 @@
  *   bi_backward_dx          dX = RNE_T(dY W^T)
  *   bi_backward_dw          dW = RNE_T(X^T dY)           (fixed-order two-pass)
  *   bi_fp8_mm               Y  = RNE_bf16((A B^T) dA dB) (fp8 e4m3fn inputs)
+ *   bi_fp8_quantize         q  = FP8(bf16 * scale_inv), amax (e4m3fn / e5m2)
+ *   bi_fp8_transpose_quantize   the same into the transposed layout
+ *   bi_fp8_linear_forward   Y  = RNE_bf16((q(x) q(w)^T) sx sw + b)
+ *   bi_fp8_linear_backward  dX = RNE_bf16((q(g) q(w)) sg sw),
+ *                           dW = RNE_bf16((q(g)^T q(x)) sg sx)
  *   bi_grouped_nt           Y[m] = in[m] Wt[e(m)]^T, zero rows for padding ids
  *   bi_grouped_nt_backward  dIn and f32 dWt of the grouped GEMM
  *
@@ -76,6 +81,12 @@ typedef enum {
     BI_F16 = 2   /* IEEE binary16 */
 } bi_dtype;
 
+/* fp8 storage formats of the quantisers (one byte per element) */
+typedef enum {
+    BI_FP8_E4M3 = 3, /* OCP e4m3fn: bias 7, no infinities, largest finite 448 */
+    BI_FP8_E5M2 = 4  /* OCP e5m2: bias 15, infinities, largest finite 57344 */
+} bi_fp8_format;
+
 typedef enum {
     BI_OK = 0,
     BI_ERR_NULL = -1,        /* a required pointer is NULL */
@@ -131,6 +142,64 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
 int bi_fp8_mm(void *y, const void *a, const void *bt, const float *a_dequant,
               const float *b_dequant, int64_t m, int64_t k, int64_t n, hipStream_t stream,
               int tc);
+
+/* fp8 quantisation (AstrAI fp8_mm.cu: quantize_kernel and cast_fp8):
+ *   dst[i] = FP8( f32(src[i]) * (*scale_inv) ),  0 <= i < n
+ * src: n bf16 elements, dst: n bytes of `fmt` (BI_FP8_E4M3 or BI_FP8_E5M2).
+ * The product is an f32 multiplication; the conversion rounds to nearest even
+ * and saturates values beyond the largest finite one to it (NaN stays NaN).
+ * amax (nullable, device f32): *amax = max(*amax, max_i |src[i]|) over the
+ * unscaled source, NaN ignored -- the caller sets *amax (e.g. to 0) first, as
+ * the page's kernel expects a zeroed amax.  The max is exact, so the result
+ * does not depend on the order in which workgroups fold it in.
+ * n == 0 does nothing.  Errors: BI_ERR_DTYPE (fmt), BI_ERR_SHAPE (n < 0),
+ * BI_ERR_NULL (a pointer other than amax is NULL while n > 0). */
+int bi_fp8_quantize(void *dst, const void *src, const float *scale_inv, float *amax, int64_t n,
+                    int fmt, hipStream_t stream);
+
+/* Transposing fp8 quantisation (fp8_mm.cu: transpose_quantize_kernel): src
+ * [rows, cols] bf16 row-major, dst [cols, rows] codes, dst[c*rows + r] =
+ * FP8(f32(src[r*cols + c]) * (*scale_inv)); amax as in bi_fp8_quantize.
+ * rows must not exceed 65535 * 64 (BI_ERR_TOO_LARGE).  rows or cols == 0 does
+ * nothing. */
+int bi_fp8_transpose_quantize(void *dst, const void *src, const float *scale_inv, float *amax,
+                              int64_t rows, int64_t cols, int fmt, hipStream_t stream);
+
+/* Workspace bytes for bi_fp8_linear_forward and bi_fp8_linear_backward on
+ * (m, k, n): the larger of the two needs (quantised copies of the operands),
+ * so one buffer serves both.  0 for invalid arguments.  A 256-byte-aligned
+ * workspace keeps the fp8 GEMMs on their fast path. */
+size_t bi_fp8_linear_workspace_bytes(int64_t m, int64_t k, int64_t n);
+
+/* Scaled fp8 linear forward (fp8_mm.cu: fp8_linear_forward_scaled):
+ *   y[m,n] = RNE_bf16( ((sum_k qx[m,k] * qw[n,k]) * sx) * sw + bias[n] )
+ *   qx = FP8_e4m3(x * sx_inv), qw = FP8_e4m3(w * sw_inv)
+ * x: [m,k] bf16, w: [n,k] bf16 (weight stored [out,in] as on the page),
+ * bias: [n] bf16 or NULL, y: [m,n] bf16; sx, sw, sx_inv, sw_inv: device f32
+ * scalars (sx_inv = 1/sx is the caller's); amax_x / amax_w (nullable) are set
+ * to max |x| and max |w|.  The bias joins in f32 before the single rounding
+ * (the page adds it to the rounded bf16 output, which rounds twice).
+ * workspace: at least bi_fp8_linear_workspace_bytes(m, k, n) bytes. */
+int bi_fp8_linear_forward(void *y, const void *x, const void *w, const void *bias,
+                          const float *sx, const float *sw, const float *sx_inv,
+                          const float *sw_inv, float *amax_x, float *amax_w, int64_t m,
+                          int64_t k, int64_t n, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream, int tc);
+
+/* Scaled fp8 linear backward (fp8_mm.cu: fp8_linear_backward_scaled):
+ *   dx[m,k] = RNE_bf16( ((sum_n qg[m,n] * qw[n,k]) * sg) * sw )
+ *   dw[n,k] = RNE_bf16( ((sum_m qg[m,n] * qx[m,k]) * sg) * sx )
+ *   qg = FP8_e4m3(g * sg_inv), qw, qx as in the forward
+ * g: [m,n], x: [m,k], w: [n,k] bf16; dx (nullable: skipped) [m,k] and dw
+ * (nullable: skipped) [n,k] bf16.  amax_g (nullable) is set to max |g|; the
+ * transposed copies' max-abs goes to workspace scratch, never to amax_g.  The
+ * bias gradient is not computed here.  workspace: at least
+ * bi_fp8_linear_workspace_bytes(m, k, n) bytes. */
+int bi_fp8_linear_backward(void *dx, void *dw, const void *g, const void *x, const void *w,
+                           const float *sg, const float *sw, const float *sx,
+                           const float *sg_inv, const float *sw_inv, const float *sx_inv,
+                           float *amax_g, int64_t m, int64_t k, int64_t n, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream, int tc);
 
 /* Row-routed grouped GEMM (rublas tensor_grouped/mod.rs, grouped_matmul_nt:
  * [M,K] @ [E,N,K]^T selecting one expert per row; ids outside [0,E) are padding

@@ -71,14 +71,15 @@ def lib():
         L.orc_fp8_quantize.argtypes = [i32, vp, f32, i64, vp, vp]
         L.orc_fp8_transpose_quantize.argtypes = [i32, vp, f32, i64, i64, vp, vp]
         L.orc_fp8_linear_forward.argtypes = [vp, vp, vp, f32, f32, f32, f32, i64, i64, i64, vp,
-                                             i64, vp, vp, vp, vp, vp, i32]
+                                             i64, vp, vp, vp, vp, vp, vp, i32]
         L.orc_fp8_linear_backward.argtypes = [i32, vp, vp, vp, f32, f32, f32, f32, f32, f32,
-                                              i64, i64, i64, vp, i64, vp, vp, vp, vp, i32]
+                                              i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, i32]
         common = [i64, i64, i64, vp, i64, vp, vp, vp, i32]
         L.orc_linear_forward.argtypes = [i32, vp, vp, vp] + common
         L.orc_linear_dx.argtypes = [i32, vp, vp] + common
         L.orc_linear_dw.argtypes = [i32, vp, vp] + common
-        L.orc_fp8_mm.argtypes = [vp, vp, ctypes.c_float, ctypes.c_float] + common
+        L.orc_fp8_mm.argtypes = [vp, vp, ctypes.c_float, ctypes.c_float, i64, i64, i64, vp, i64,
+                                 vp, vp, vp, vp, i32]
         gcommon = [vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i32]
         L.orc_grouped_fwd.argtypes = [i32, vp, vp] + gcommon
         L.orc_grouped_dinput.argtypes = [i32, vp, vp] + gcommon
@@ -119,10 +120,12 @@ def _rows_arg(rows, total):
 
 class Result:
     """Rounded output bits plus the exact pre-rounding value S and the
-    absolute-product scale A for every computed element."""
+    absolute-product scale A for every computed element (fp8 results also
+    carry .g: the sum over 8-index groups of the largest |product|)."""
 
     def __init__(self, out, s, a):
         self.out, self.s, self.a = out, s, a
+        self.g = None
 
 
 def _alloc(nrows, ncols, dt):
@@ -177,11 +180,14 @@ def fp8_mm(a8, bt8, da, db, m, k, n, rows=None, threads=None):
     out = np.zeros((nr, n), dtype=np.uint16)
     s = np.zeros((nr, n), dtype=np.float64)
     a = np.zeros((nr, n), dtype=np.float64)
+    g = np.zeros((nr, n), dtype=np.float64)
     rc = lib().orc_fp8_mm(_ptr(a8), _ptr(bt8), float(np.float32(da)), float(np.float32(db)),
-                          m, k, n, _ptr(r), nr, _ptr(out), _ptr(s), _ptr(a),
+                          m, k, n, _ptr(r), nr, _ptr(out), _ptr(s), _ptr(a), _ptr(g),
                           threads or default_threads())
     assert rc == 0
-    return Result(out, s, a)
+    res = Result(out, s, a)
+    res.g = g
+    return res
 
 
 def fp8_quantize(fmt, src, scale_inv):
@@ -215,14 +221,16 @@ def fp8_linear_forward(x, w, bias, sx, sw, sx_inv, sw_inv, m, k, n, rows=None, t
     bias = None if bias is None else _c(bias, np.uint16)
     r, nr = _rows_arg(rows, m)
     out, s, a = _alloc(nr, n, BF16)
+    g = np.zeros_like(s)
     ax, aw = ctypes.c_float(0.0), ctypes.c_float(0.0)
     f = lambda v: float(np.float32(v))
     rc = lib().orc_fp8_linear_forward(_ptr(x), _ptr(w), _ptr(bias), f(sx), f(sw), f(sx_inv),
                                       f(sw_inv), m, k, n, _ptr(r), nr, _ptr(out), _ptr(s),
-                                      _ptr(a), ctypes.byref(ax), ctypes.byref(aw),
+                                      _ptr(a), _ptr(g), ctypes.byref(ax), ctypes.byref(aw),
                                       threads or default_threads())
     assert rc == 0
     res = Result(out, s, a)
+    res.g = g
     res.amax_x, res.amax_w = ax.value, aw.value
     return res
 
@@ -236,14 +244,16 @@ def fp8_linear_backward(which, g, x, w, sg, sw, sx, sg_inv, sw_inv, sx_inv, m, k
     code = {"dx": 1, "dw": 2}[which]
     r, nr = _rows_arg(rows, m if code == 1 else n)
     out, s, a = _alloc(nr, k, BF16)
+    gg = np.zeros_like(s)
     ag = ctypes.c_float(0.0)
     f = lambda v: float(np.float32(v))
     rc = lib().orc_fp8_linear_backward(code, _ptr(g), _ptr(x), _ptr(w), f(sg), f(sw), f(sx),
                                        f(sg_inv), f(sw_inv), f(sx_inv), m, k, n, _ptr(r), nr,
-                                       _ptr(out), _ptr(s), _ptr(a), ctypes.byref(ag),
+                                       _ptr(out), _ptr(s), _ptr(a), _ptr(gg), ctypes.byref(ag),
                                        threads or default_threads())
     assert rc == 0
     res = Result(out, s, a)
+    res.g = gg
     res.amax_g = ag.value
     return res
 

@@ -144,6 +144,24 @@ def fp8(m, k, n, seed):
     return {"a8": a8, "bt8": b8, "da": da, "db": db, "m": m, "k": k, "n": n}
 
 
+def fp8_linear(m, k, n, seed, sigma_w=0.02, bias=True):
+    """bf16 operands of the scaled fp8 linear: x [m,k] ~ N(0,1), w [n,k]
+    ([out,in]) ~ N(0, sigma_w), bias [n] ~ N(0, 0.02), g [m,n] ~ N(0,1), and
+    per-tensor scales from each tensor's max-abs (delayed-scaling style:
+    scale = amax / 448 as an f32, scale_inv = 448 / amax)."""
+    x = normal_bits((m, k), 1.0, seed, 0, BF16)
+    w = normal_bits((n, k), sigma_w, seed, 1, BF16)
+    g = normal_bits((m, n), 1.0, seed, 3, BF16)
+    b = normal_bits((n,), 0.02, seed, 2, BF16) if bias else None
+    out = {"x": x, "w": w, "g": g, "b": b, "m": m, "k": k, "n": n}
+    for name in ("x", "w", "g"):
+        amax = float(np.abs(to_f32(out[name], BF16)).max()) if out[name].size else 1.0
+        amax = amax if amax > 0 else 1.0
+        out["s" + name] = np.float32(amax / E4M3_MAX)
+        out["s" + name + "_inv"] = np.float32(E4M3_MAX / amax)
+    return out
+
+
 def config4():
     """fp8 e4m3: A[8192,4096], B^T[4096,4096] from N(0,1) bf16."""
     return fp8(8192, 4096, 4096, seed=4)

@@ -99,3 +99,33 @@ def test_plan_is_shape_only_and_follows_fallback_rule(lib):
     # the scalar-tier dW chunk does not depend on dtype (bf16 == upcast f32)
     for k, n in [(768, 48), (64, 64), (4096, 4096)]:
         assert dig.bi_plan(dig.OP_DW, dig.BI_BF16, 0, k, n) == dig.bi_plan(dig.OP_DW, dig.BI_F32, 0, k, n)
+
+
+def test_fp8_producer_validation(lib):
+    assert dig.bi_fp8_quantize(F, F, F, None, 4, 7) == -2
+    assert dig.bi_fp8_quantize(F, F, F, None, -1, dig.BI_FP8_E4M3) == -3
+    assert dig.bi_fp8_quantize(None, F, F, None, 4, dig.BI_FP8_E5M2) == -1
+    assert dig.bi_fp8_quantize(F, F, None, F, 4, dig.BI_FP8_E4M3) == -1
+    assert dig.bi_fp8_quantize(None, None, None, None, 0, dig.BI_FP8_E4M3) == 0
+    assert dig.bi_fp8_transpose_quantize(F, F, F, None, 4, -2, dig.BI_FP8_E4M3) == -3
+    assert dig.bi_fp8_transpose_quantize(F, F, F, None, 65535 * 64 + 1, 1, 3) == -4
+    assert dig.bi_fp8_transpose_quantize(F, F, F, None, 0, 9, dig.BI_FP8_E4M3) == 0
+    # workspace: forward needs the two quantised operands, backward four plus
+    # a scratch line; 256-byte aligned pieces
+    a = lambda b: (b + 255) // 256 * 256
+    m, k, n = 64, 32, 16
+    fwd = a(m * k) + a(n * k)
+    bwd = a(m * n) + a(k * n) + a(n * m) + a(k * m) + 256
+    assert dig.bi_fp8_linear_workspace_bytes(m, k, n) == max(fwd, bwd)
+    assert dig.bi_fp8_linear_workspace_bytes(-1, k, n) == 0
+    ws = dig.bi_fp8_linear_workspace_bytes(m, k, n)
+    assert dig.bi_fp8_linear_forward(F, F, F, None, F, F, F, None, None, None, m, k, n,
+                                     F, ws) == -1
+    assert dig.bi_fp8_linear_forward(F, F, F, None, F, F, F, F, None, None, m, k, n,
+                                     F, 16) == -5
+    assert dig.bi_fp8_linear_forward(F, F, F, None, F, F, F, F, None, None, m, -k, n,
+                                     F, ws) == -3
+    assert dig.bi_fp8_linear_backward(F, F, F, F, F, None, F, F, F, F, F, None, m, k, n,
+                                      F, ws) == -1
+    assert dig.bi_fp8_linear_backward(F, F, F, F, F, F, F, F, F, F, F, None, m, k, n,
+                                      F, 100) == -5

@@ -16,8 +16,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 MUTANTS = {
-    "dropped_last_term": ("for (int64_t r = 0; r < red; ++r) {",
-                          "for (int64_t r = 0; r < red - 1; ++r) {"),
+    "dropped_last_term": ("s[j] = 0.0, ab[j] = 0.0;\n    for (int64_t r = 0; r < red; ++r) {",
+                          "s[j] = 0.0, ab[j] = 0.0;\n    for (int64_t r = 0; r < red - 1; ++r) {"),
+    "fp8_dropped_last_term": ("g[j] = 0.0;\n    for (int64_t r = 0; r < red; ++r) {",
+                              "g[j] = 0.0;\n    for (int64_t r = 0; r < red - 1; ++r) {"),
     "bias_sign": ("s[j] += c->B[j], ab[j] += fabs(c->B[j]);",
                   "s[j] -= c->B[j], ab[j] += fabs(c->B[j]);"),
     "forward_transposed_w": ("row_dot(c->X + r * c->k, c->k, c->W, c->n, 1, c->n, s, ab);",
@@ -51,10 +53,11 @@ MUTANTS = {
                     "const float a = (float)orc_decode_bf16(src[i]);"),
     "fp8_linear_bias_dropped": ("if (c->B) v += c->B[j], a += fabs(c->B[j]);",
                                 "if (c->B) a += fabs(c->B[j]);"),
-    "fp8_linear_dx_w_untransposed": ("row_dot(c->QG + r * c->n, c->n, c->QW, c->k, 1, c->k, s, ab);",
-                                     "row_dot(c->QG + r * c->n, c->n, c->QW, 1, c->n, c->k, s, ab);"),
+    "fp8_linear_dx_w_untransposed": ("row_dot_g8(c->QG + r * c->n, c->n, c->QW, c->k, 1, c->k, s, ab, g);",
+                                     "row_dot_g8(c->QG + r * c->n, c->n, c->QW, 1, c->n, c->k, s, ab, g);"),
     "fp8_linear_dw_wrong_scale": ("c.sa = (double)sg, c.sb = which == 1 ? (double)sw : (double)sx, c.rows = rows;",
                                   "c.sa = (double)sg, c.sb = (double)sw, c.rows = rows;"),
+    "fp8_group_of_16": ("if (r % 8 == 7 || r == red - 1)", "if (r % 16 == 15 || r == red - 1)"),
     "f16_overflow_saturates": ("double r = round_mag(fabs(x), 11, -14, 65504.0);\n    uint16_t mag;\n    if (isinf(r)) {\n        mag = 0x7c00;",
                                "double r = round_mag(fabs(x), 11, -14, 65504.0);\n    uint16_t mag;\n    if (isinf(r)) {\n        mag = 0x7bff;"),
 }

@@ -559,3 +559,19 @@ def test_fp8_linear_backward_vs_numpy():
     sel = oracle.fp8_linear_backward("dw", g, x, w, sg, sw, sx, sg_inv, sw_inv, sx_inv, m, k, n,
                                      rows=[0, 17, 52])
     assert np.array_equal(sel.out, rdw.out[[0, 17, 52]])
+
+
+def test_fp8_group_max_statistic_by_hand():
+    # one output element, reduction of 10: products 1..10 (a = 1..10 as e4m3
+    # codes of exact small integers, b = 1): groups {0..7} and {8, 9} have
+    # maxima 8 and 10, so G = 18; with scales 0.5 and 0.25, G = 18 / 8
+    vals = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10]
+    a8 = np.array([[oracle.rne_e4m3_sat(v) for v in vals]], np.uint8)
+    bt8 = np.array([[oracle.rne_e4m3_sat(1.0)] * 10], np.uint8)
+    r = oracle.fp8_mm(a8, bt8, 0.5, 0.25, 1, 10, 1)
+    assert r.g[0, 0] == 18 / 8 and r.s[0, 0] == 55 / 8
+    # the same statistic from the fp8 linear (negative products count by size)
+    x = _bf16([[1, -2, 3, -4, 5, -6, 7, -8, 9, -10]])
+    w = _bf16([[1] * 10])
+    f = oracle.fp8_linear_forward(x, w, None, 1.0, 1.0, 1.0, 1.0, 1, 10, 1)
+    assert f.g[0, 0] == 18 and f.s[0, 0] == -5
