@@ -12,7 +12,8 @@ time of the timed steps), a per-kernel roofline entry for the dominant kernel
 second pass over the same steps), and the CPU oracle's throughput on a bounded
 sample of the same workload.
 
-Other workloads (--workload): fp8 (e4m3 GEMM 8192x4096x4096), grouped (8
+Other workloads (--workload): fp8 (e4m3 GEMM 8192x4096x4096), fp8_linear
+(scaled fp8 linear forward + backward with quantisation), grouped (8
 experts, 16384x2048 -> 1408, forward + dinput + dweights), sweep (forward of
 W[4096,4096] at M in {1,3,17,128,1000,8192}).
 """
@@ -40,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="linear",
-                    choices=["linear", "fp8", "grouped", "sweep", "copy"])
+                    choices=["linear", "fp8", "fp8_linear", "grouped", "sweep", "copy"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -294,6 +295,64 @@ def bench_fp8(args, torch, dig, synth):
     }
 
 
+def bench_fp8_linear(args, torch, dig, synth):
+    """Scaled fp8 linear on x[8192,4096], w[4096,4096] ([out,in]), g[8192,4096]:
+    forward (quantise x and w, fp8 GEMM + bias) and backward (quantise g,
+    transposed copies of w, g and x, the dX and dW fp8 GEMMs), all through the
+    C ABI; plus the quantiser and the transposing quantiser alone on x."""
+    d = synth.fp8_linear(8192, 4096, 4096, seed=45)
+    m, k, n = d["m"], d["k"], d["n"]
+    dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
+    x, w, g, b = dev(d["x"]), dev(d["w"]), dev(d["g"]), dev(d["b"])
+    sc = {key: torch.tensor([float(d[key])], dtype=torch.float32, device="cuda")
+          for key in ("sx", "sw", "sg", "sx_inv", "sw_inv", "sg_inv")}
+    amax = torch.zeros(4, dtype=torch.float32, device="cuda")
+    y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.int16, device="cuda")
+    dw = torch.empty((n, k), dtype=torch.int16, device="cuda")
+    nb = dig.bi_fp8_linear_workspace_bytes(m, k, n)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    q = torch.empty(m * k, dtype=torch.uint8, device="cuda")
+    a0, a1, a2 = (amax[i:i + 1] for i in range(3))
+    step = [
+        ("forward", lambda s: dig.check(dig.bi_fp8_linear_forward(
+            y, x, w, b, sc["sx"], sc["sw"], sc["sx_inv"], sc["sw_inv"], a0, a1, m, k, n, ws, nb,
+            s, 1))),
+        ("backward", lambda s: dig.check(dig.bi_fp8_linear_backward(
+            dx, dw, g, x, w, sc["sg"], sc["sw"], sc["sx"], sc["sg_inv"], sc["sw_inv"],
+            sc["sx_inv"], a2, m, k, n, ws, nb, s, 1))),
+    ]
+    ms, per = timed_steps(torch, step, args.steps, args.warmup)
+    alone = [
+        ("quantize", lambda s: dig.check(dig.bi_fp8_quantize(q, x, sc["sx_inv"], a0, m * k,
+                                                             dig.BI_FP8_E4M3, s))),
+        ("transpose_quantize", lambda s: dig.check(dig.bi_fp8_transpose_quantize(
+            q, x, sc["sx_inv"], a0, m, k, dig.BI_FP8_E4M3, s))),
+    ]
+    _, qper = timed_steps(torch, alone, args.steps, args.warmup)
+    flop = 3 * 2.0 * m * k * n
+    qbytes = 3 * m * k  # 2 bytes read + 1 byte written per element
+    qgbps = {name: qbytes / (v * 1e-3) / 1e9 for name, v in qper.items()}
+    dominant = max(qgbps, key=lambda name: qper[name])
+    return {
+        "metric": "scaled fp8 linear step TFLOP/s (quantisation included)",
+        "value": round(flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "scaled fp8 linear x[8192,4096] w[4096,4096] g[8192,4096]: "
+                               "forward + backward (dX, dW), e4m3fn, bias", "M": m, "K": k,
+                   "N": n},
+        "ops": {name: {"us": round(v * 1e3, 2)} for name, v in per.items()},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(qgbps[dominant], 1),
+                     "peak": HBM_PEAK, "unit": "GB/s",
+                     "frac": round(qgbps[dominant] / HBM_PEAK, 4), "traffic": None,
+                     "algorithmic_bytes": qbytes},
+        "quantizers": {name: {"us": round(v * 1e3, 2), "GBps": round(qgbps[name], 1)}
+                       for name, v in qper.items()},
+    }
+
+
 def bench_grouped(args, torch, dig, synth):
     d = synth.config5()
     m, k, n, e = d["m"], d["k"], d["n"], d["e"]
@@ -389,7 +448,8 @@ def main():
     import deterministic_invariant_gemm_amd as dig
     import synth
     dig.load()
-    fn = {"linear": bench_linear, "fp8": bench_fp8, "grouped": bench_grouped,
+    fn = {"linear": bench_linear, "fp8": bench_fp8, "fp8_linear": bench_fp8_linear,
+          "grouped": bench_grouped,
           "sweep": bench_sweep, "copy": bench_copy}[args.workload]
     out = fn(args, torch, dig, synth)
     print(json.dumps(out), flush=True)

@@ -52,8 +52,25 @@ __device__ __forceinline__ void fold_amax(float mx, float *amax) {
     }
 }
 
-// vec: src and dst 16-byte aligned; 16 elements per thread and step, the
-// n % 16 tail element by element
+// vec: src and dst 16-byte aligned.  Each thread converts UN chunks of 16
+// elements per step (all loads issued first, so more bytes are in flight),
+// the remainder element by element.
+constexpr int UN = 4;
+
+template <int FMT>
+__device__ __forceinline__ u32x4 convert16(const u32x4 a, const u32x4 b, float s, float &mx) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    int o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float f0 = lo_bf16(w[2 * q]), f1 = hi_bf16(w[2 * q]);
+        const float f2 = lo_bf16(w[2 * q + 1]), f3 = hi_bf16(w[2 * q + 1]);
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))));
+        o[q] = cvt2<FMT, true>(f2 * s, f3 * s, cvt2<FMT, false>(f0 * s, f1 * s, 0));
+    }
+    return u32x4{(uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]};
+}
+
 template <int FMT>
 __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t *src, const float *scale_inv,
                                                       uint8_t *dst, float *amax, int64_t n,
@@ -66,21 +83,22 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t *src, const
     if (vec) {
         const int64_t nchunk = n / 16;
         const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
-        for (int64_t c = tid; c < nchunk; c += stride) {
-            const u32x4 a = __builtin_nontemporal_load(s4 + 2 * c);
-            const u32x4 b = __builtin_nontemporal_load(s4 + 2 * c + 1);
-            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-            int o[4];
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
+        int64_t c = tid;
+        // full steps: chunks c, c + stride, ..., c + (UN-1) stride all exist
+        for (; c + (UN - 1) * stride < nchunk; c += UN * stride) {
+            u32x4 a[UN], b[UN];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float f0 = lo_bf16(w[2 * q]), f1 = hi_bf16(w[2 * q]);
-                const float f2 = lo_bf16(w[2 * q + 1]), f3 = hi_bf16(w[2 * q + 1]);
-                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))));
-                o[q] = cvt2<FMT, true>(f2 * s, f3 * s, cvt2<FMT, false>(f0 * s, f1 * s, 0));
+            for (int u = 0; u < UN; ++u) {
+                a[u] = __builtin_nontemporal_load(s4 + 2 * (c + u * stride));
+                b[u] = __builtin_nontemporal_load(s4 + 2 * (c + u * stride) + 1);
             }
-            reinterpret_cast<u32x4 *>(dst)[c] =
-                u32x4{(uint32_t)o[0], (uint32_t)o[1], (uint32_t)o[2], (uint32_t)o[3]};
+#pragma unroll
+            for (int u = 0; u < UN; ++u)
+                __builtin_nontemporal_store(convert16<FMT>(a[u], b[u], s, mx), d4 + c + u * stride);
         }
+        for (; c < nchunk; c += stride)
+            d4[c] = convert16<FMT>(s4[2 * c], s4[2 * c + 1], s, mx);
         done = nchunk * 16;
     }
     for (int64_t i = done + tid; i < n; i += stride) {
@@ -91,21 +109,25 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t *src, const
     if (amax) fold_amax(mx, amax);
 }
 
-// [rows, cols] -> [cols, rows] through a 64 x 64 byte tile in LDS.
-// vec_in: cols % 8 == 0 and src 16-byte aligned; vec_out: rows % 16 == 0 and
-// dst 16-byte aligned.
+// [rows, cols] -> [cols, rows] through a TR x 64 byte tile in LDS (TR source
+// rows, 64 source columns): the source is read in 128-byte row pieces and the
+// destination written in TR-byte row pieces.  vec_in: cols % 8 == 0 and src
+// 16-byte aligned; vec_out: rows % 16 == 0 and dst 16-byte aligned.
+constexpr int TR = 256;
+
 template <int FMT>
 __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
     const uint16_t *src, const float *scale_inv, uint8_t *dst, float *amax, int64_t rows,
     int64_t cols, int vec_in, int vec_out) {
-    __shared__ uint32_t tile[64][64 / 4 + 1];  // bytes of row r at tile[r][..], padded
+    __shared__ uint32_t tile[TR][64 / 4 + 1];  // bytes of source row r at tile[r][..], padded
     const float s = *scale_inv;
-    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * 64;
     const int t = threadIdx.x;
     float mx = 0.0f;
-    {
-        // thread t: tile row t / 4, columns 16 * (t % 4) .. +15
-        const int rr = t >> 2, cc = 16 * (t & 3);
+    // read: TR rows x 4 pieces of 16 columns; thread t takes rows t / 4 + 64 j
+#pragma unroll
+    for (int j = 0; j < TR / 64; ++j) {
+        const int rr = (t >> 2) + 64 * j, cc = 16 * (t & 3);
         const int64_t gr = r0 + rr, gc = c0 + cc;
         float f[16];
         if (vec_in && gr < rows && gc + 16 <= cols) {
@@ -129,9 +151,14 @@ __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
         }
     }
     __syncthreads();
-    {
-        // thread t: output row c0 + t / 4, source rows 16 * (t % 4) .. +15
-        const int oc = t >> 2, rb = 16 * (t & 3);
+    // write: 64 destination rows x TR/16 pieces of 16 bytes; thread t takes
+    // destination row t / 4 (+ 64 per pass over the pieces) ... mapped so a
+    // wave covers whole TR-byte row pieces
+    constexpr int PIECES = TR / 16;  // 16-byte pieces per destination row
+#pragma unroll
+    for (int j = 0; j < 64 * PIECES / QT; ++j) {
+        const int idx = t + QT * j;
+        const int oc = idx / PIECES, rb = 16 * (idx % PIECES);
         const int64_t go = c0 + oc, gr = r0 + rb;
         uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -142,7 +169,8 @@ __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
         if (go < cols) {
             uint8_t *d = dst + go * rows + gr;
             if (vec_out && gr + 16 <= rows) {
-                *reinterpret_cast<u32x4 *>(d) = u32x4{w[0], w[1], w[2], w[3]};
+                __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
+                                            reinterpret_cast<u32x4 *>(d));
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
@@ -167,7 +195,7 @@ hipError_t launch_quantize(const void *src, const float *scale_inv, void *dst, f
                            int64_t n, int fmt, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     const int vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
-    int64_t grid = (n / 16 + QT - 1) / QT;
+    int64_t grid = (n / 16 + QT * UN - 1) / (QT * UN);
     if (grid < 1) grid = 1;
     if (grid > 2048) grid = 2048;
     const uint16_t *sp = static_cast<const uint16_t *>(src);
@@ -185,7 +213,7 @@ hipError_t launch_transpose_quantize(const void *src, const float *scale_inv, vo
                                      float *amax, int64_t rows, int64_t cols, int fmt,
                                      hipStream_t s) {
     if (rows <= 0 || cols <= 0) return hipSuccess;
-    const int64_t gx = (cols + 63) / 64, gy = (rows + 63) / 64;
+    const int64_t gx = (cols + 63) / 64, gy = (rows + TR - 1) / TR;
     if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
     const int vec_in = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0;
     const int vec_out = rows % 16 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
