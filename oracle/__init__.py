@@ -84,6 +84,8 @@ def lib():
         L.orc_grouped_fwd.argtypes = [i32, vp, vp] + gcommon
         L.orc_grouped_dinput.argtypes = [i32, vp, vp] + gcommon
         L.orc_grouped_dweights.argtypes = [i32, vp, vp] + gcommon
+        L.orc_bias_grad.argtypes = [i32, vp, i64, i64, vp, vp, vp]
+        L.orc_bias_grad.restype = i32
         for f in ("orc_linear_forward", "orc_linear_dx", "orc_linear_dw", "orc_fp8_mm",
                   "orc_grouped_fwd", "orc_grouped_dinput", "orc_grouped_dweights",
                   "orc_fp8_quantize", "orc_fp8_transpose_quantize", "orc_fp8_linear_forward",
@@ -188,6 +190,15 @@ def fp8_mm(a8, bt8, da, db, m, k, n, rows=None, threads=None):
     res = Result(out, s, a)
     res.g = g
     return res
+
+
+def bias_grad(dt, dy, m, n):
+    """db = RNE_T(column sums of dY); dy: [m, n] bit patterns."""
+    dy = _c(dy, STORAGE[dt])
+    out, s, a = _alloc(1, n, dt)
+    rc = lib().orc_bias_grad(dt, _ptr(dy), m, n, _ptr(out), _ptr(s), _ptr(a))
+    assert rc == 0
+    return Result(out[0], s[0], a[0])
 
 
 def fp8_quantize(fmt, src, scale_inv):

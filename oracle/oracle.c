@@ -48,6 +48,9 @@
  *            saturating to it (NaN stays NaN); amax is the max-abs of the
  *            unscaled source (NaN ignored).  transpose_quantize_kernel: the
  *            same per element, stored transposed ([rows,cols] -> [cols,rows]).
+ *   bias gradient  db[n] = RNE_T( sum_m dY[m,n] )
+ *            ffma.py, _FFMAAddmm.backward (gb = gy.sum(0) in f32, cast back
+ *            to the bias dtype).
  *   fp8 linear forward (fp8_linear_forward_scaled)
  *            Y[m,n] = RNE_bf16( (sum_k qx[m,k] qw[n,k]) * sx * sw + b[n] )
  *            with qx = quantize(x, 1/sx), qw = quantize(w, 1/sw), w stored
@@ -771,5 +774,28 @@ int orc_fp8_linear_backward(int which, const uint16_t *g, const uint16_t *x, con
     run_rows(fp8lin_row, &c, nrows, nthreads);
     if (amax_g) *amax_g = amax_of(g, m * n);
     free(QG), free(QW), free(QX);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Bias gradient: column sums of dY                                           */
+/* ------------------------------------------------------------------------- */
+
+/* dy: [m, n] of dtype dt; out: [n] of dt; s_out / a_out: exact sum and sum of
+ * absolute values per column (nullable). */
+int orc_bias_grad(int dt, const void *dy, int64_t m, int64_t n, void *out, double *s_out,
+                  double *a_out) {
+    if (dt < ORC_F32 || dt > ORC_F16) return -2;
+    for (int64_t j = 0; j < n; ++j) {
+        double sum = 0.0, ab = 0.0;
+        for (int64_t i = 0; i < m; ++i) {
+            const double v = orc_decode(dt, dy, i * n + j);
+            sum += v;
+            ab += fabs(v);
+        }
+        if (out) store_rounded(dt, out, j, sum);
+        if (s_out) s_out[j] = sum;
+        if (a_out) a_out[j] = ab;
+    }
     return 0;
 }

@@ -58,6 +58,8 @@ MUTANTS = {
     "fp8_linear_dw_wrong_scale": ("c.sa = (double)sg, c.sb = which == 1 ? (double)sw : (double)sx, c.rows = rows;",
                                   "c.sa = (double)sg, c.sb = (double)sw, c.rows = rows;"),
     "fp8_group_of_16": ("if (r % 8 == 7 || r == red - 1)", "if (r % 16 == 15 || r == red - 1)"),
+    "bias_grad_row_stride": ("const double v = orc_decode(dt, dy, i * n + j);",
+                             "const double v = orc_decode(dt, dy, j * m + i);"),
     "f16_overflow_saturates": ("double r = round_mag(fabs(x), 11, -14, 65504.0);\n    uint16_t mag;\n    if (isinf(r)) {\n        mag = 0x7c00;",
                                "double r = round_mag(fabs(x), 11, -14, 65504.0);\n    uint16_t mag;\n    if (isinf(r)) {\n        mag = 0x7bff;"),
 }

@@ -575,3 +575,21 @@ def test_fp8_group_max_statistic_by_hand():
     w = _bf16([[1] * 10])
     f = oracle.fp8_linear_forward(x, w, None, 1.0, 1.0, 1.0, 1.0, 1, 10, 1)
     assert f.g[0, 0] == 18 and f.s[0, 0] == -5
+
+
+@pytest.mark.parametrize("dt", [synth.F32, synth.BF16, synth.F16])
+def test_bias_grad_vs_numpy_column_sum(dt):
+    m, n = 333, 77
+    dy = synth.normal_bits((m, n), 1.0, 8, 4, dt)
+    r = oracle.bias_grad(dt, dy, m, n)
+    v = synth.to_f32(dy, dt).astype(np.float64)
+    # sums of at most a few hundred values of <= 24 significant bits in
+    # double are exact, so numpy's pairwise sum is the same number
+    assert np.array_equal(r.s, v.sum(axis=0))
+    assert np.array_equal(r.a, np.abs(v).sum(axis=0))
+    ref = torch.from_numpy(v.sum(axis=0)).to({synth.F32: torch.float32,
+                                               synth.BF16: torch.bfloat16,
+                                               synth.F16: torch.float16}[dt])
+    bits = ref.view({synth.F32: torch.int32, synth.BF16: torch.int16,
+                     synth.F16: torch.int16}[dt]).numpy()
+    assert np.array_equal(r.out.view(bits.dtype), bits)
