@@ -15,7 +15,8 @@ sample of the same workload.
 Other workloads (--workload): fp8 (e4m3 GEMM 8192x4096x4096), fp8_linear
 (scaled fp8 linear forward + backward with quantisation), grouped (8
 experts, 16384x2048 -> 1408, forward + dinput + dweights), sweep (forward of
-W[4096,4096] at M in {1,3,17,128,1000,8192}).
+W[4096,4096] at M in {1,3,17,128,1000,8192}), bias_grad (column sums of
+dY[4096,3072] and dY[16384,8192], bf16).
 """
 from __future__ import annotations
 
@@ -41,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="linear",
-                    choices=["linear", "fp8", "fp8_linear", "grouped", "sweep", "copy"])
+                    choices=["linear", "fp8", "fp8_linear", "grouped", "sweep", "bias_grad",
+                             "copy"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -415,6 +417,41 @@ def bench_sweep(args, torch, dig, synth):
             "sweep": res}
 
 
+def bench_bias_grad(args, torch, dig, synth):
+    """Bias gradient db = RNE(column sums of dY): the dY of the default linear
+    workload [4096,3072] and a larger [16384,8192], both bf16.  HBM-bound:
+    algorithmic bytes = dY read once + db written once."""
+    bt = synth.BF16
+    shapes = {"db_4096x3072": (4096, 3072), "db_16384x8192": (16384, 8192)}
+    ops, nbytes = [], {}
+    keep = []
+    for name, (m, n) in shapes.items():
+        dy = torch.from_numpy(synth.normal_bits((m, n), 1.0, 2, 4, bt).view(np.int16)).cuda()
+        db = torch.empty(n, dtype=torch.int16, device="cuda")
+        wsb = dig.bi_bias_grad_workspace_bytes(m, n, bt)
+        ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device="cuda")
+        keep += [dy, db, ws]
+        ops.append((name, lambda s, dy=dy, db=db, ws=ws, m=m, n=n, wsb=wsb: dig.check(
+            dig.bi_bias_grad(db, dy, m, n, bt, ws if wsb else None, wsb, s))))
+        nbytes[name] = 2 * (m * n + n)
+    ms, per = timed_steps(torch, ops, args.steps, args.warmup)
+    gbps = {k_: nbytes[k_] / (v * 1e-3) / 1e9 for k_, v in per.items()}
+    main_op = "db_4096x3072"
+    dominant = max(per, key=per.get)
+    return {"metric": "bias gradient GB/s (dY read + db write)", "value": round(gbps[main_op], 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "bf16 bias gradient, dY[4096,3072] (and dY[16384,8192])",
+                       "M": 4096, "N": 3072},
+            "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(gbps[dominant], 1),
+                         "peak": HBM_PEAK, "unit": "GB/s",
+                         "frac": round(gbps[dominant] / HBM_PEAK, 4), "traffic": None,
+                         "algorithmic_bytes": nbytes[dominant]},
+            "ops": {k_: {"us": round(v * 1e3, 2), "GBps": round(gbps[k_], 1)}
+                    for k_, v in per.items()}}
+
+
 def bench_copy(args, torch, dig, synth):
     """Plain device-to-device copy of a 512 MiB buffer: the known-size kernel
     used to calibrate the FETCH_SIZE / WRITE_SIZE counters, and a measured HBM
@@ -450,7 +487,8 @@ def main():
     dig.load()
     fn = {"linear": bench_linear, "fp8": bench_fp8, "fp8_linear": bench_fp8_linear,
           "grouped": bench_grouped,
-          "sweep": bench_sweep, "copy": bench_copy}[args.workload]
+          "sweep": bench_sweep, "bias_grad": bench_bias_grad,
+          "copy": bench_copy}[args.workload]
     out = fn(args, torch, dig, synth)
     print(json.dumps(out), flush=True)
 

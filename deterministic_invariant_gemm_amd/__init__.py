@@ -49,6 +49,10 @@ def load() -> ctypes.CDLL:
     L.bi_backward_dw_workspace_bytes.restype = sz
     L.bi_backward_dw.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, sz, vp, i32]
     L.bi_fp8_mm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i32]
+    L.bi_bias_grad_workspace_bytes.argtypes = [i64, i64, i32]
+    L.bi_bias_grad_workspace_bytes.restype = sz
+    L.bi_bias_grad.argtypes = [vp, vp, i64, i64, i32, vp, sz, vp]
+    L.bi_bias_grad.restype = i32
     L.bi_grouped_nt.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, i32]
     L.bi_grouped_nt_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
                                          vp, i32]
@@ -115,6 +119,15 @@ def bi_backward_dw(dw, x, dy, m, k, n, dtype, workspace, workspace_bytes, stream
                    tc=1) -> int:
     return load().bi_backward_dw(_p(dw), _p(x), _p(dy), m, k, n, dtype, _p(workspace),
                                  workspace_bytes, _s(stream), tc)
+
+
+def bi_bias_grad_workspace_bytes(m, n, dtype) -> int:
+    return load().bi_bias_grad_workspace_bytes(m, n, dtype)
+
+
+def bi_bias_grad(db, dy, m, n, dtype, workspace, workspace_bytes, stream=None) -> int:
+    return load().bi_bias_grad(_p(db), _p(dy), m, n, dtype, _p(workspace), workspace_bytes,
+                               _s(stream))
 
 
 def bi_fp8_mm(y, a, bt, a_dequant, b_dequant, m, k, n, stream=None, tc=1) -> int:

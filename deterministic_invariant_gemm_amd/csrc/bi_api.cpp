@@ -50,6 +50,15 @@ bool mfma_eligible(int op, int dt, int tc, int64_t k, int64_t n) {
     return false;
 }
 
+// tc = 2 asks for the MFMA tier explicitly (rublas grouped_matmul_nt: an
+// explicit tensor-core strategy fails when that path is unavailable instead of
+// falling back); tc = 1 is the automatic choice, tc = 0 the scalar tier.
+constexpr int kTcRequired = 2;
+int tier_check(int op, int dt, int tc, int64_t k, int64_t n) {
+    if (tc == kTcRequired && !mfma_eligible(op, dt, tc, k, n)) return BI_ERR_UNSUPPORTED;
+    return BI_OK;
+}
+
 // Tile per op from the non-M output dims only (the kernel's column count is N
 // for forward / fp8 / grouped forward, K for dX / grouped dinput; dW tiles its
 // [K, N] output).  Every tile issues the same MFMA sequence per element, so
@@ -167,7 +176,7 @@ const char *bi_status_string(int status) {
     case BI_ERR_DTYPE: return "BI_ERR_DTYPE: unsupported dtype";
     case BI_ERR_SHAPE: return "BI_ERR_SHAPE: invalid dimension";
     case BI_ERR_TOO_LARGE: return "BI_ERR_TOO_LARGE: a tensor exceeds 2^40 elements";
-    case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE: dW workspace missing or too small";
+    case BI_ERR_WORKSPACE: return "BI_ERR_WORKSPACE: workspace missing or too small";
     case BI_ERR_HIP: return "BI_ERR_HIP: a HIP launch failed";
     case BI_ERR_UNSUPPORTED: return "BI_ERR_UNSUPPORTED: no tier for this dtype/tc";
     }
@@ -178,6 +187,8 @@ int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows
     if (op < OP_FWD || op > OP_GDW) return BI_ERR_UNSUPPORTED;
     if (op != OP_FP8 && !dtype_ok(dtype)) return BI_ERR_DTYPE;
     if (k < 0 || n < 0) return BI_ERR_SHAPE;
+    const int ts = tier_check(op, op == OP_FP8 ? BI_BF16 : dtype, tc, k, n);
+    if (ts != BI_OK) return ts;
     Plan pl = make_plan(op, op == OP_FP8 ? BI_BF16 : dtype, tc, k, n);
     if (chunk_rows) *chunk_rows = pl.chunk;
     return pl.tile;
@@ -189,6 +200,7 @@ int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t 
     if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
     if (checked_elems(m, k) < 0 || checked_elems(k, n) < 0 || checked_elems(m, n) < 0)
         return BI_ERR_TOO_LARGE;
+    { const int ts = tier_check(OP_FWD, dtype, tc, k, n); if (ts != BI_OK) return ts; }
     if (m == 0 || n == 0) return BI_OK;
     if (!y || (k > 0 && (!x || !w))) return BI_ERR_NULL;
     const Plan pl = make_plan(OP_FWD, dtype, tc, k, n);
@@ -217,6 +229,7 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
     if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
     if (checked_elems(m, k) < 0 || checked_elems(k, n) < 0 || checked_elems(m, n) < 0)
         return BI_ERR_TOO_LARGE;
+    { const int ts = tier_check(OP_DX, dtype, tc, k, n); if (ts != BI_OK) return ts; }
     if (m == 0 || k == 0) return BI_OK;
     if (!dx || (n > 0 && (!dy || !w))) return BI_ERR_NULL;
     const Plan pl = make_plan(OP_DX, dtype, tc, k, n);
@@ -242,6 +255,7 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
 size_t bi_backward_dw_workspace_bytes(int64_t m, int64_t k, int64_t n, int dtype, int tc) {
     if (!dtype_ok(dtype) || m < 0 || k < 0 || n < 0) return 0;
     if (checked_elems(m, k) < 0 || checked_elems(m, n) < 0 || checked_elems(k, n) < 0) return 0;
+    if (tier_check(OP_DW, dtype, tc, k, n) != BI_OK) return 0;
     const Plan pl = make_plan(OP_DW, dtype, tc, k, n);
     const int64_t chunks = dw_chunks(pl, m);
     if (chunks <= 1) return 0;
@@ -255,6 +269,7 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
     if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
     if (checked_elems(m, k) < 0 || checked_elems(k, n) < 0 || checked_elems(m, n) < 0)
         return BI_ERR_TOO_LARGE;
+    { const int ts = tier_check(OP_DW, dtype, tc, k, n); if (ts != BI_OK) return ts; }
     if (k == 0 || n == 0) return BI_OK;
     if (!dw || (m > 0 && (!x || !dy))) return BI_ERR_NULL;
     const Plan pl = make_plan(OP_DW, dtype, tc, k, n);
@@ -289,6 +304,28 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
     return hip_status(e);
 }
 
+size_t bi_bias_grad_workspace_bytes(int64_t m, int64_t n, int dtype) {
+    if (!dtype_ok(dtype) || m < 0 || n < 0 || checked_elems(m, n) < 0) return 0;
+    const int64_t chunks = m <= 0 ? 1 : cdiv(m, BG_CHUNK);
+    return chunks > 1 ? (size_t)chunks * (size_t)n * sizeof(float) : 0;
+}
+
+int bi_bias_grad(void *db, const void *dy, int64_t m, int64_t n, int dtype, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return BI_ERR_DTYPE;
+    if (m < 0 || n < 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, n) < 0) return BI_ERR_TOO_LARGE;
+    if (n == 0) return BI_OK;
+    if (!db || (m > 0 && !dy)) return BI_ERR_NULL;
+    const int64_t chunks = m <= 0 ? 1 : cdiv(m, BG_CHUNK);
+    const size_t need = chunks > 1 ? (size_t)chunks * (size_t)n * sizeof(float) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 3u)))
+        return BI_ERR_WORKSPACE;
+    const bool vec = aligned16(dy) && n % 8 == 0;
+    return hip_status(launch_bias_grad(dy, m, n, chunks, static_cast<float *>(workspace), db,
+                                       dtype, vec, stream));
+}
+
 }  // extern "C"
 
 namespace {
@@ -301,6 +338,7 @@ int fp8_gemm(void *y, const void *a, const void *bt, const float *a_dequant,
     if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
     if (checked_elems(m, k) < 0 || checked_elems(n, k) < 0 || checked_elems(m, n) < 0)
         return BI_ERR_TOO_LARGE;
+    { const int ts = tier_check(OP_FP8, BI_BF16, tc, k, n); if (ts != BI_OK) return ts; }
     if (m == 0 || n == 0) return BI_OK;
     if (!y || !a_dequant || !b_dequant || (k > 0 && (!a || !bt))) return BI_ERR_NULL;
     const Plan pl = make_plan(OP_FP8, BI_BF16, tc, k, n);
@@ -396,6 +434,7 @@ int bi_fp8_linear_forward(void *y, const void *x, const void *w, const void *bia
     if (checked_elems(m, k) < 0 || checked_elems(n, k) < 0 || checked_elems(m, n) < 0 ||
         m > (int64_t)65535 * 64 || n > (int64_t)65535 * 64)
         return BI_ERR_TOO_LARGE;
+    { const int ts = tier_check(OP_FP8, BI_BF16, tc, k, n); if (ts != BI_OK) return ts; }
     if (!sx || !sw || !sx_inv || !sw_inv) return BI_ERR_NULL;
     if ((m > 0 && n > 0 && !y) || (m * k > 0 && !x) || (n * k > 0 && !w)) return BI_ERR_NULL;
     const size_t need = align256(m * k) + align256(n * k);
@@ -420,6 +459,9 @@ int bi_fp8_linear_backward(void *dx, void *dw, const void *g, const void *x, con
     if (checked_elems(m, k) < 0 || checked_elems(n, k) < 0 || checked_elems(m, n) < 0 ||
         m > (int64_t)65535 * 64 || n > (int64_t)65535 * 64)
         return BI_ERR_TOO_LARGE;
+    // dX GEMM: reduction n, columns k; dW GEMM: reduction m, columns k
+    if (dx) { const int ts = tier_check(OP_FP8, BI_BF16, tc, n, k); if (ts != BI_OK) return ts; }
+    if (dw) { const int ts = tier_check(OP_FP8, BI_BF16, tc, m, k); if (ts != BI_OK) return ts; }
     if (!sg || !sw || !sx || !sg_inv || !sw_inv || !sx_inv) return BI_ERR_NULL;
     if ((m * n > 0 && !g) || (dx && n * k > 0 && !w) || (dw && m * k > 0 && !x))
         return BI_ERR_NULL;
@@ -465,6 +507,7 @@ int bi_grouped_nt(void *y, const void *input, const void *weights, const uint32_
                   hipStream_t stream, int tc) {
     int st = grouped_validate(m, k, n, e, dtype);
     if (st != BI_OK) return st;
+    { const int ts = tier_check(OP_GFWD, dtype, tc, k, n); if (ts != BI_OK) return ts; }
     if (m == 0) return BI_OK;
     if (!y || !input || !weights || !row_experts) return BI_ERR_NULL;
     const Plan pl = make_plan(OP_GFWD, dtype, tc, k, n);
@@ -492,6 +535,8 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
                            int dtype, hipStream_t stream, int tc) {
     int st = grouped_validate(m, k, n, e, dtype);
     if (st != BI_OK) return st;
+    { const int ts = tier_check(OP_GDIN, dtype, tc, k, n); if (ts != BI_OK) return ts; }
+    { const int ts = tier_check(OP_GDW, dtype, tc, k, n); if (ts != BI_OK) return ts; }
     if (!dweights || !offsets) return BI_ERR_NULL;
     if (m > 0 && (!dinput || !input || !weights || !grad_out || !row_experts)) return BI_ERR_NULL;
     // dinput (skipped for an empty batch)

@@ -113,6 +113,13 @@ hipError_t launch_quantize(const void *src, const float *scale_inv, void *dst, f
 hipError_t launch_transpose_quantize(const void *src, const float *scale_inv, void *dst,
                                      float *amax, int64_t rows, int64_t cols, int fmt,
                                      hipStream_t s);
+// Bias gradient (bias_grad.hip): out[n] = RNE(column sums of dy [m, n]) in a
+// fixed order; rows in chunks of BG_CHUNK, nchunks = max(1, ceil(m / BG_CHUNK));
+// with more than one chunk ws holds nchunks * n f32 partials.  vec: dy 16-byte
+// aligned and n % 8 == 0.
+constexpr int64_t BG_CHUNK = 256;
+hipError_t launch_bias_grad(const void *dy, int64_t m, int64_t n, int64_t nchunks, float *ws,
+                            void *out, int dt, bool vec, hipStream_t s);
 // *a = *b = *c = +0 (null pointers skipped), one tiny kernel
 hipError_t launch_zero3(float *a, float *b, float *c, hipStream_t s);
 

@@ -113,16 +113,27 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
     }
 }
 
-// Pass 2 of the chunked dW: out = RNE( ((P0 + P1) + P2) + ... ) per element,
-// chunks in ascending order.  Shared by both tiers.
+// Pass 2 of the chunked dW and of the bias gradient: out = RNE( ((P0 + P1) +
+// P2) + ... ) per element, chunks in ascending order.  Loads are issued CS_UN
+// at a time so their latencies overlap; the additions stay in chunk order.
+constexpr int CS_UN = 16;
+
 template <int DT_OUT>
-__global__ __launch_bounds__(256) void chunk_sum_kernel(const float *__restrict__ ws,
+__global__ __launch_bounds__(64) void chunk_sum_kernel(const float *__restrict__ ws,
                                                         void *out, int64_t count,
                                                         int64_t nchunks) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
         float s = ws[i];
-        for (int64_t c = 1; c < nchunks; ++c) s = s + ws[c * count + i];
+        int64_t c = 1;
+        for (; c + CS_UN <= nchunks; c += CS_UN) {
+            float v[CS_UN];
+#pragma unroll
+            for (int u = 0; u < CS_UN; ++u) v[u] = ws[(c + u) * count + i];
+#pragma unroll
+            for (int u = 0; u < CS_UN; ++u) s = s + v[u];
+        }
+        for (; c < nchunks; ++c) s = s + ws[c * count + i];
         store_elem<DT_OUT>(out, i, s);
     }
 }
@@ -215,11 +226,12 @@ hipError_t launch_scalar_gemm(const ScalarGemmArgs &p, int dt_in, int dt_out, in
 hipError_t launch_chunk_sum(const float *ws, void *out, int64_t count, int64_t nchunks,
                             int dt_out, hipStream_t s) {
     if (count <= 0) return hipSuccess;
-    int64_t grid = (count + 255) / 256;
-    if (grid > 65536) grid = 65536;
-    if (dt_out == DT_F32) BI_LAUNCH(chunk_sum_kernel<DT_F32>, grid, 256, s, ws, out, count, nchunks);
-    else if (dt_out == DT_BF16) BI_LAUNCH(chunk_sum_kernel<DT_BF16>, grid, 256, s, ws, out, count, nchunks);
-    else if (dt_out == DT_F16) BI_LAUNCH(chunk_sum_kernel<DT_F16>, grid, 256, s, ws, out, count, nchunks);
+    // one-wave workgroups: short rows of partials still spread over many CUs
+    int64_t grid = (count + 63) / 64;
+    if (grid > (1 << 20)) grid = 1 << 20;
+    if (dt_out == DT_F32) BI_LAUNCH(chunk_sum_kernel<DT_F32>, grid, 64, s, ws, out, count, nchunks);
+    else if (dt_out == DT_BF16) BI_LAUNCH(chunk_sum_kernel<DT_BF16>, grid, 64, s, ws, out, count, nchunks);
+    else if (dt_out == DT_F16) BI_LAUNCH(chunk_sum_kernel<DT_F16>, grid, 64, s, ws, out, count, nchunks);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -6,6 +6,7 @@
  *   bi_forward              Y  = RNE_T(X W + b)
  *   bi_backward_dx          dX = RNE_T(dY W^T)
  *   bi_backward_dw          dW = RNE_T(X^T dY)           (fixed-order two-pass)
+ *   bi_bias_grad            db = RNE_T(sum over rows of dY) (fixed order)
  *   bi_fp8_mm               Y  = RNE_bf16((A B^T) dA dB) (fp8 e4m3fn inputs)
  *   bi_fp8_quantize         q  = FP8(bf16 * scale_inv), amax (e4m3fn / e5m2)
  *   bi_fp8_transpose_quantize   the same into the transposed layout
@@ -43,15 +44,21 @@
  *              output is rounded once, to nearest-even (sgemm-bi PyPI page,
  *              "Determinism contracts").
  *   tc         Tensor-core (MFMA) tier request.  tc = 0 always selects the
- *              scalar FMA tier.  tc = 1 selects the MFMA tier for bf16/f16
- *              (and fp8) unless a non-M output dimension is below 64, in which
- *              case the scalar tier runs (sgemm-bi PyPI page, "Determinism
- *              contracts": shape-only fallback below 64).  f32 operands always
- *              use the scalar tier.  The choice, and the tile shape, depend
- *              only on (op, dtype, tc, the non-M output dims, the reduction
- *              length) -- never on m -- so the forward is batch-invariant:
- *              a row's output bits do not depend on how many other rows are in
- *              the batch.
+ *              scalar FMA tier.  tc = 1 ("auto") selects the MFMA tier for
+ *              bf16/f16 (and fp8) unless a non-M output dimension is below 64,
+ *              in which case the scalar tier runs (sgemm-bi PyPI page,
+ *              "Determinism contracts": shape-only fallback below 64); f32
+ *              operands always use the scalar tier.  tc = 2 requires the MFMA
+ *              tier: where tc = 1 would fall back, the call returns
+ *              BI_ERR_UNSUPPORTED before enqueuing anything (rublas
+ *              tensor_grouped: an explicit tensor-core strategy errors instead
+ *              of falling back silently).  The tier depends only on (op,
+ *              dtype, tc, the non-M output dims, the reduction length) --
+ *              never on m -- so the forward is batch-invariant: a row's
+ *              output bits do not depend on how many other rows are in the
+ *              batch.  The two tiers do not give the same bits (different
+ *              summation); results of either tier are bit-identical run to
+ *              run.
  *
  * Determinism contracts
  *   Every entry point is bit-identical from run to run for the same inputs.
@@ -61,7 +68,8 @@
  *   MFMA tier: one MFMA instruction kind per dtype and a fixed ascending
  *   sequence of 16-deep (bf16/f16) or 64-deep (fp8) reduction steps per output
  *   element in every tile shape, so all tile shapes give identical bits.
- *   No atomics anywhere.
+ *   No atomic accumulation anywhere (the quantisers fold max-abs with one
+ *   integer atomic max per workgroup, which gives the same value in any order).
  */
 #ifndef BI_H
 #define BI_H
@@ -93,7 +101,7 @@ typedef enum {
     BI_ERR_DTYPE = -2,       /* dtype code not supported by this entry point */
     BI_ERR_SHAPE = -3,       /* negative or zero-where-forbidden dimension */
     BI_ERR_TOO_LARGE = -4,   /* a tensor exceeds 2^40 elements */
-    BI_ERR_WORKSPACE = -5,   /* dW workspace missing or too small */
+    BI_ERR_WORKSPACE = -5,   /* workspace missing or too small */
     BI_ERR_HIP = -6,         /* a HIP launch failed (hipGetLastError) */
     BI_ERR_UNSUPPORTED = -7  /* tc/dtype combination has no tier */
 } bi_status;
@@ -130,6 +138,24 @@ size_t bi_backward_dw_workspace_bytes(int64_t m, int64_t k, int64_t n, int dtype
 int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k, int64_t n,
                    int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream,
                    int tc);
+
+/* Workspace bytes bi_bias_grad needs (0 when m <= 256).  Returns 0 for invalid
+ * arguments as well. */
+size_t bi_bias_grad_workspace_bytes(int64_t m, int64_t n, int dtype);
+
+/* Bias gradient (ffma.py, _FFMAAddmm.backward: gb = gy.sum(0) accumulated in
+ * f32 and cast back to the bias dtype; sgemm-bi PyPI page, "Determinism
+ * contracts": the bias gradient is a plain f32 column sum, deterministic for a
+ * fixed shape and outside the batch-invariance contract):
+ *   db[n] = RNE_dtype( sum_m dy[m,n] )
+ * dy: [m,n], db: [n], both of `dtype`.  The order is fixed by m alone: rows in
+ * chunks of 256; inside a chunk 64 interleaved running sums (rows t, t+64,
+ * ...) combined in a fixed tree; chunk partials (f32, in the workspace) added in
+ * ascending chunk order; one rounding.  workspace: 4-byte aligned device memory
+ * of at least bi_bias_grad_workspace_bytes(m, n, dtype) bytes (may be NULL when
+ * that is 0), else BI_ERR_WORKSPACE.  m == 0 writes db = +0. */
+int bi_bias_grad(void *db, const void *dy, int64_t m, int64_t n, int dtype, void *workspace,
+                 size_t workspace_bytes, hipStream_t stream);
 
 /* Per-tensor-scaled fp8 GEMM (AstrAI fp8_mm.cu: fp8_mm takes e4m3fn a[M,K]
  * and b[N,K] and returns bf16 [M,N]; fp8_gemm_into applies the per-tensor f32

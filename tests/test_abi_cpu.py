@@ -129,3 +129,42 @@ def test_fp8_producer_validation(lib):
                                       F, ws) == -1
     assert dig.bi_fp8_linear_backward(F, F, F, F, F, F, F, F, F, F, F, None, m, k, n,
                                       F, 100) == -5
+
+
+def test_tc2_requires_the_mfma_tier(lib):
+    """tc = 2 errors out where tc = 1 would fall back to the scalar tier;
+    checked before any launch (the fake pointers are never touched)."""
+    U = -7
+    # f32 has no MFMA tier; narrow outputs fall back
+    assert dig.bi_forward(F, F, F, None, 4, 128, 128, dig.BI_F32, None, 2) == U
+    assert dig.bi_forward(F, F, F, None, 4, 128, 48, dig.BI_BF16, None, 2) == U
+    assert dig.bi_backward_dx(F, F, F, 4, 48, 128, dig.BI_BF16, None, 2) == U
+    assert dig.bi_backward_dw(F, F, F, 4, 128, 32, dig.BI_F16, None, 0, None, 2) == U
+    assert dig.bi_fp8_mm(F, F, F, F, F, 4, 64, 32, None, 2) == U
+    assert dig.bi_grouped_nt(F, F, F, F, F, 4, 128, 48, 2, dig.BI_BF16, None, 2) == U
+    assert dig.bi_grouped_nt(F, F, F, F, F, 4, 128, 128, 2, dig.BI_F32, None, 2) == U
+    assert dig.bi_grouped_nt_backward(F, F, F, F, F, F, F, 4, 40, 128, 2, dig.BI_BF16,
+                                      None, 2) == U
+    assert dig.bi_plan(0, dig.BI_BF16, 2, 768, 48)[0] == U
+    assert dig.bi_plan(0, dig.BI_BF16, 2, 768, 64)[0] > 0
+    # even an empty batch reports it (validation comes before the no-op)
+    assert dig.bi_forward(F, F, F, None, 0, 128, 48, dig.BI_BF16, None, 2) == U
+    assert dig.bi_backward_dw_workspace_bytes(9000, 128, 32, dig.BI_BF16, 2) == 0
+
+
+def test_bias_grad_validation(lib):
+    m, n = 1000, 300
+    need = dig.bi_bias_grad_workspace_bytes(m, n, dig.BI_BF16)
+    assert need == -(-m // 256) * n * 4
+    assert dig.bi_bias_grad_workspace_bytes(256, n, dig.BI_BF16) == 0
+    assert dig.bi_bias_grad_workspace_bytes(257, n, dig.BI_BF16) == 2 * n * 4
+    assert dig.bi_bias_grad_workspace_bytes(-1, n, dig.BI_BF16) == 0
+    assert dig.bi_bias_grad(F, F, m, n, dig.BI_BF16, None, 0) == -5
+    assert dig.bi_bias_grad(F, F, m, n, dig.BI_BF16, F, need - 1) == -5
+    assert dig.bi_bias_grad(F, F, m, n, dig.BI_BF16, F + 2, need) == -5  # misaligned
+    assert dig.bi_bias_grad(F, F, m, n, 7, F, need) == -2
+    assert dig.bi_bias_grad(F, F, -1, n, dig.BI_BF16, F, need) == -3
+    assert dig.bi_bias_grad(None, F, m, n, dig.BI_BF16, F, need) == -1
+    assert dig.bi_bias_grad(F, None, m, n, dig.BI_BF16, F, need) == -1
+    assert dig.bi_bias_grad(F, F, 1 << 30, 1 << 20, dig.BI_BF16, F, need) == -4
+    assert dig.bi_bias_grad(None, None, 5, 0, dig.BI_BF16, None, 0) == 0  # n == 0: no-op
