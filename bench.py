@@ -16,7 +16,8 @@ Other workloads (--workload): fp8 (e4m3 GEMM 8192x4096x4096), fp8_linear
 (scaled fp8 linear forward + backward with quantisation), grouped (8
 experts, 16384x2048 -> 1408, forward + dinput + dweights), sweep (forward of
 W[4096,4096] at M in {1,3,17,128,1000,8192}), bias_grad (column sums of
-dY[4096,3072] and dY[16384,8192], bf16).
+dY[4096,3072] and dY[16384,8192], bf16), tiles (forward, dX and dW of the
+default workload on each candidate tile, for the tile-choice counters).
 """
 from __future__ import annotations
 
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="linear",
                     choices=["linear", "fp8", "fp8_linear", "grouped", "sweep", "bias_grad",
-                             "copy"])
+                             "tiles", "copy"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -452,6 +453,54 @@ def bench_bias_grad(args, torch, dig, synth):
                     for k_, v in per.items()}}
 
 
+# Candidate MFMA tiles per op of the default workload (tile id 40 + base: direct
+# loads; 100 + base: the same with copies spread between MFMAs).  Shapes:
+# 41 256x256 2x2 waves, 42 256x192 2x2, 44 128x128 2x2, 45 128x96 4x1,
+# 48 96x96 3x1, 50 256x96 4x1, 51 256x192 4x2, 52 256x256 4x2, 55 128x128 2x4,
+# 57 96x96 1x3.  The first id of each list is the default.
+TILE_CANDIDATES = {
+    "fwd": [51, 52, 41, 42, 44, 55, 111, 115],
+    "dX": [45, 105, 115, 55, 44, 50, 51, 42],
+    "dW": [115, 55, 104, 44, 48, 108, 57, 45, 105],
+}
+
+
+def bench_tiles(args, torch, dig, synth):
+    """Forward, dX and dW of the default workload on every candidate tile
+    (forced with tc = 16 + id; every tile gives the same bits).  Used with
+    rocprofv3 counters to compare MFMA busy time, LDS bank conflicts and HBM
+    traffic between tiles."""
+    d = synth.config2(synth.BF16)
+    m, k, n, dt = d["m"], d["k"], d["n"], synth.BF16
+    dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
+    x, w, b, dy = dev(d["x"]), dev(d["w"]), dev(d["b"]), dev(d["dy"])
+    y = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    dx = torch.empty((m, k), dtype=torch.int16, device="cuda")
+    dw = torch.empty((k, n), dtype=torch.int16, device="cuda")
+    calls = {
+        "fwd": lambda s, tc: dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, s, tc)),
+        "dX": lambda s, tc: dig.check(dig.bi_backward_dx(dx, dy, w, m, k, n, dt, s, tc)),
+        "dW": lambda s, tc: dig.check(dig.bi_backward_dw(dw, x, dy, m, k, n, dt, None, 0, s, tc)),
+    }
+    flop = 2.0 * m * k * n
+    res = {}
+    for op, ids in TILE_CANDIDATES.items():
+        ops = [(f"{op}:{t}", lambda s, f=calls[op], t=t: f(s, 16 + t)) for t in ids]
+        _, per = timed_steps(torch, ops, args.steps, args.warmup)
+        res[op] = {str(t): {"us": round(per[f"{op}:{t}"] * 1e3, 2),
+                            "tflops": round(flop / (per[f"{op}:{t}"] * 1e-3) / 1e12, 1)}
+                   for t in ids}
+    default_ms = sum(per_op[str(TILE_CANDIDATES[op][0])]["us"] for op, per_op in res.items()) / 1e3
+    return {"metric": "forward/dX/dW time per candidate tile", "value":
+            round(3 * flop / (default_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(default_ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "bf16 linear 768->3072 at M=4096, each op on each candidate "
+                                   "tile (events per launch)", "M": m, "K": k, "N": n},
+            "roofline": None, "tiles": res}
+
+
 def bench_copy(args, torch, dig, synth):
     """Plain device-to-device copy of a 512 MiB buffer: the known-size kernel
     used to calibrate the FETCH_SIZE / WRITE_SIZE counters, and a measured HBM
@@ -487,7 +536,7 @@ def main():
     dig.load()
     fn = {"linear": bench_linear, "fp8": bench_fp8, "fp8_linear": bench_fp8_linear,
           "grouped": bench_grouped,
-          "sweep": bench_sweep, "bias_grad": bench_bias_grad,
+          "sweep": bench_sweep, "bias_grad": bench_bias_grad, "tiles": bench_tiles,
           "copy": bench_copy}[args.workload]
     out = fn(args, torch, dig, synth)
     print(json.dumps(out), flush=True)

@@ -74,14 +74,20 @@ int pick_tile(int op, int64_t k, int64_t n) {
         if (cols >= 2048) return 112;
         return cols >= 128 ? 115 : 46;
     case OP_FWD:
-        if (cols >= 2048 && cols % 192 == 0 && cols / 192 <= 16) return 51;  // 256x192, 8 waves
-        if (cols >= 2048) return 52;                                           // 256x256, 8 waves
+        // 256x192, 8 waves, copies spread; 256x256, 8 waves
+        if (cols >= 2048 && cols % 192 == 0 && cols / 192 <= 16) return 111;
+        if (cols >= 2048) return 52;
         return cols >= 128 ? 44 : 46;
     case OP_DX:
         if (cols % 96 == 0 && cols <= 1536) return 45;  // 128x96, four waves along M
         return cols >= 128 ? 115 : 46;                  // 128x128, eight waves, spread
     case OP_DW:
+        // 96x96 with three waves (one per SIMD on three SIMDs) while that makes
+        // at most one tile per CU and fills at least half of them; else
         // 128x128, eight waves, copies spread between MFMAs
+        if (k >= 96 && n >= 96 && cdiv(k, 96) * cdiv(n, 96) <= 256 &&
+            cdiv(k, 96) * cdiv(n, 96) >= 128)
+            return 48;
         return (k >= 128 && n >= 128) ? 115 : 46;
     case OP_GFWD: case OP_GDIN:
         // 256x192 / 128x128, eight waves, copies spread
