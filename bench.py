@@ -46,6 +46,9 @@ def parse():
                     choices=["linear", "fp8", "fp8_linear", "grouped", "sweep", "bias_grad",
                              "tiles", "copy"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="untimed run of the step before the warm-up steps, so that the GPU "
+                         "clocks have left their idle state (once per process)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -145,6 +148,26 @@ class HipEvents:
         self.made = []
 
 
+SETTLE_MS = 400.0
+_settled = [False]
+
+
+def settle(torch, ops):
+    """Run the step, untimed, for SETTLE_MS of wall time (first call only).  An
+    idle MI355X takes a few hundred milliseconds of load to reach its working
+    clocks; without this the first few hundred steps run up to 15 % slower."""
+    if _settled[0] or SETTLE_MS <= 0:
+        return
+    s = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for _ in range(20):
+            for _, fn in ops:
+                fn(s)
+        torch.cuda.synchronize()
+    _settled[0] = True
+
+
 def timed_steps(torch, ops, steps, warmup):
     """ops: list of (name, fn(stream)); one step runs every op once, in order,
     through the C ABI.
@@ -155,6 +178,7 @@ def timed_steps(torch, ops, steps, warmup):
     by two timing events recorded on the stream it is launched on (each
     record costs about 2 us of GPU time, so they stay out of the first pass).
     Returns (wall ms per step, {name: mean event ms per call})."""
+    settle(torch, ops)
     s = torch.cuda.current_stream()
     for _ in range(warmup):
         for _, fn in ops:
@@ -250,7 +274,8 @@ def bench_linear(args, torch, dig, synth):
         "config": {"workload": f"{args.dtype} training linear 768->3072 (weight [in,out]) at "
                                "M=4096: forward + dX + dW, MFMA tier",
                    "M": m, "K": k, "N": n, "bias": True},
-        "timing": "value: wall time of the timed steps (no events); kernel times: HIP events "
+        "timing": f"value: wall time of the timed steps (no events), after {SETTLE_MS:.0f} ms of "
+                  "untimed steps (clock ramp) and the warm-up steps; kernel times: HIP events "
                   "around each launch in a second pass of the same steps",
         "roofline": {"bound": "mfma", "kernel": dominant,
                      "achieved": round(achieved, 2), "peak": BF16_PEAK, "unit": "TFLOP/s",
@@ -523,6 +548,8 @@ def bench_copy(args, torch, dig, synth):
 
 def main():
     args = parse()
+    global SETTLE_MS
+    SETTLE_MS = args.settle_ms
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
