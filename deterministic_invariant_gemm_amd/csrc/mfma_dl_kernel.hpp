@@ -270,10 +270,19 @@ struct FragOf<true, R, ESZ> {
     using type = RcFrag<ESZ>;
 };
 
+// Tiles of two to four MFMA waves (burst copies) get one extra wave that
+// issues all the copies: the MFMA waves then only read fragments, multiply and
+// meet at the stage barriers, and the copy wave sits on a SIMD with no or one
+// other wave.  Eight-wave tiles have no register room for a ninth wave.
+constexpr bool dl_producer(int nw, bool spread) { return !spread && nw >= 2 && nw <= 4; }
+constexpr int dl_threads(int nw, bool spread) { return 64 * (nw + (dl_producer(nw, spread) ? 1 : 0)); }
+
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
           bool SPREAD>
-__global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
+__global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD)) void mfma_dl_kernel(MfmaArgs p) {
     constexpr int NW = WGM * WGN;
+    constexpr bool PROD = dl_producer(NW, SPREAD);
+    constexpr int NWC = PROD ? 1 : NW;  // waves that issue the copies
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
@@ -296,7 +305,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
-    const TileInfo ti = decode_tile<MODE, BM, BN, 64 * NW>(p, t);
+    const TileInfo ti = decode_tile<MODE, BM, BN, dl_threads(NW, SPREAD)>(p, t);
+    const bool is_prod = PROD && wave == NW;
+    const int cwave = PROD ? 0 : wave;  // index of this wave among the copying waves
     if (ti.skip) return;
     const int64_t row0 = ti.row0, col0 = ti.col0;
     const float bias_v = fetch_bias<DT, EPI, BN>(p, col0, t);
@@ -304,12 +315,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
 
     const i32x4 rsa = make_rsrc(p.a, p.a_bytes);
     const i32x4 rsb = make_rsrc(static_cast<const uint16_t *>(p.b) + ti.b_off, p.b_bytes - 2 * ti.b_off);
-    using LA = DLoad<BM, A_RC, NW, TY::ESZ>;
-    using LB = DLoad<BN, B_RC, NW, TY::ESZ>;
+    using LA = DLoad<BM, A_RC, NWC, TY::ESZ>;
+    using LB = DLoad<BN, B_RC, NWC, TY::ESZ>;
     LA la;
     LB lb;
-    la.init(p.lda, row0, r_begin, wave, lane);
-    lb.init(p.ldb, col0, r_begin, wave, lane);
+    la.init(p.lda, row0, r_begin, cwave, lane);
+    lb.init(p.ldb, col0, r_begin, cwave, lane);
     typename FragOf<A_RC, BM, TY::ESZ>::type ra;
     typename FragOf<B_RC, BN, TY::ESZ>::type rb;
     ra.init(lane);
@@ -330,11 +341,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
         BI_LDS char *db = da + SA;
         const int64_t rem = red - (int64_t)KPS * s;
         if (rem >= KPS) {
-            la.template issue<false>(rsa, da, s, rem, wave);
-            lb.template issue<false>(rsb, db, s, rem, wave);
+            la.template issue<false>(rsa, da, s, rem, cwave);
+            lb.template issue<false>(rsb, db, s, rem, cwave);
         } else {
-            la.template issue<true>(rsa, da, s, rem, wave);
-            lb.template issue<true>(rsb, db, s, rem, wave);
+            la.template issue<true>(rsa, da, s, rem, cwave);
+            lb.template issue<true>(rsb, db, s, rem, cwave);
         }
     };
     auto frag_a = [&](const BI_LDS char *st, int i, int kk) {
@@ -401,21 +412,37 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
     auto copy_one = [&](int cs, int c) {
         BI_LDS char *da = ring + (cs % NS) * (SA + SB);
         const int64_t rem = red - (int64_t)KPS * cs;
-        if (c < LA::NQ) la.issue_one(rsa, da, cs, rem, wave, c);
-        else lb.issue_one(rsb, da + SA, cs, rem, wave, c - LA::NQ);
+        if (c < LA::NQ) la.issue_one(rsa, da, cs, rem, cwave, c);
+        else lb.issue_one(rsb, da + SA, cs, rem, cwave, c - LA::NQ);
     };
 
+    if (!PROD || is_prod) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-        if (s < nst) issue(s);
+        for (int s = 0; s < NS; ++s)
+            if (s < nst) issue(s);
+    }
     if (nst > 0) {
         // issued: stages 0 .. min(NS-1, nst-1); wait for stage 0
         const int later = nst - 1 < NS - 1 ? nst - 1 : NS - 1;
-        wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
+        if (!PROD || is_prod) wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
         __syncthreads();
+        if (!is_prod) {
 #pragma unroll
-        for (int kk = 0; kk < STEPS - 1; ++kk) read_step(ring, kk, kk);
+            for (int kk = 0; kk < STEPS - 1; ++kk) read_step(ring, kk, kk);
+        }
         __builtin_amdgcn_sched_barrier(0);
+    }
+    if (is_prod) {
+        // the copy wave: one barrier per stage, like the MFMA waves, and the
+        // epilogue's barrier
+        for (int s = 0; s + 1 < nst; ++s) {
+            const int later = nst - 2 - s < NS - 2 ? nst - 2 - s : NS - 2;
+            wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
+            __syncthreads();
+            if (s + NS < nst) issue(s + NS);
+        }
+        __syncthreads();
+        return;
     }
     for (int s = 0; s < nst; ++s) {
         const BI_LDS char *cur = ring + (s % NS) * (SA + SB);
@@ -432,12 +459,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_dl_kernel(MfmaArgs p) {
             // issued so far: stages 0 .. min(s+NS-1, nst-1); stage s+1 has
             // landed once only the copies of the stages after it are pending
             const int later = nst - 2 - s < NS - 2 ? nst - 2 - s : NS - 2;
-            wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
+            if (!PROD) wait_vmcnt_stages<LA::NQ + LB::NQ>(later);
             __syncthreads();
-            if (!SPREAD && s + NS < nst) issue(s + NS);
+            if (!PROD && !SPREAD && s + NS < nst) issue(s + NS);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!SPREAD) {
+        if constexpr (!SPREAD || PROD) {
 #pragma unroll
             for (int kk = BAR + 1; kk < STEPS; ++kk) {
 #pragma unroll
@@ -483,7 +510,7 @@ hipError_t launch_dl_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
     using T = TileOf<ID>;
     hipLaunchKernelGGL(
         (mfma_dl_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE, SPREAD>),
-        dim3(grid), dim3(64 * T::WGM * T::WGN), 0, s, p);
+        dim3(grid), dim3(dl_threads(T::WGM * T::WGN, SPREAD)), 0, s, p);
     return hipGetLastError();
 }
 
