@@ -272,16 +272,24 @@ struct FragOf<true, R, ESZ> {
 
 // Tiles of two to four MFMA waves (burst copies) get one extra wave that
 // issues all the copies: the MFMA waves then only read fragments, multiply and
-// meet at the stage barriers, and the copy wave sits on a SIMD with no or one
-// other wave.  Eight-wave tiles have no register room for a ninth wave.
-constexpr bool dl_producer(int nw, bool spread) { return !spread && nw >= 2 && nw <= 4; }
-constexpr int dl_threads(int nw, bool spread) { return 64 * (nw + (dl_producer(nw, spread) ? 1 : 0)); }
+// meet at the stage barriers.  With two or three MFMA waves the copy wave has a
+// SIMD of its own; with four it shares one, which halves that MFMA wave's
+// register budget, so only wave tiles of at most 96 accumulator registers
+// (e.g. 64x96) qualify.  Eight-wave tiles keep their copies for the same reason.
+constexpr bool dl_producer(int nw, bool spread, int wtm, int wtn) {
+    return !spread && nw >= 2 && nw <= 4 && (nw < 4 || wtm * wtn / 64 <= 96);
+}
+constexpr int dl_threads(int nw, bool spread, int wtm, int wtn) {
+    return 64 * (nw + (dl_producer(nw, spread, wtm, wtn) ? 1 : 0));
+}
 
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
           bool SPREAD>
-__global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD)) void mfma_dl_kernel(MfmaArgs p) {
+__global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) void mfma_dl_kernel(
+    MfmaArgs p) {
     constexpr int NW = WGM * WGN;
-    constexpr bool PROD = dl_producer(NW, SPREAD);
+    constexpr bool PROD = dl_producer(NW, SPREAD, BM / WGM, BN / WGN);
+    constexpr int NTH = dl_threads(NW, SPREAD, BM / WGM, BN / WGN);
     constexpr int NWC = PROD ? 1 : NW;  // waves that issue the copies
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD)) void mfma_dl_kernel(
     const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
-    const TileInfo ti = decode_tile<MODE, BM, BN, dl_threads(NW, SPREAD)>(p, t);
+    const TileInfo ti = decode_tile<MODE, BM, BN, NTH>(p, t);
     const bool is_prod = PROD && wave == NW;
     const int cwave = PROD ? 0 : wave;  // index of this wave among the copying waves
     if (ti.skip) return;
@@ -510,7 +518,7 @@ hipError_t launch_dl_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
     using T = TileOf<ID>;
     hipLaunchKernelGGL(
         (mfma_dl_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE, SPREAD>),
-        dim3(grid), dim3(dl_threads(T::WGM * T::WGN, SPREAD)), 0, s, p);
+        dim3(grid), dim3(dl_threads(T::WGM * T::WGN, SPREAD, T::BM / T::WGM, T::BN / T::WGN)), 0, s, p);
     return hipGetLastError();
 }
 
