@@ -37,7 +37,11 @@ __device__ __forceinline__ uint8_t cvt1(float a) {
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// max over the workgroup, then one atomic max on the bit pattern
+// max over the workgroup, then one atomic max on the bit pattern -- skipped
+// when the value already in *amax is at least as large: the running max only
+// grows, so such an atomic could not change it (a stale read only costs an
+// unneeded atomic).  Thousands of workgroups each issuing an atomic on one
+// address would otherwise serialise at the end of the kernel.
 __device__ __forceinline__ void fold_amax(float mx, float *amax) {
     __shared__ float part[QT / 64];
 #pragma unroll
@@ -48,7 +52,10 @@ __device__ __forceinline__ void fold_amax(float mx, float *amax) {
         float m = part[0];
 #pragma unroll
         for (int w = 1; w < QT / 64; ++w) m = fmaxf(m, part[w]);
-        atomicMax(reinterpret_cast<unsigned int *>(amax), __float_as_uint(m));
+        unsigned int *bits = reinterpret_cast<unsigned int *>(amax);
+        const unsigned int mb = __float_as_uint(m);
+        if (mb > __hip_atomic_load(bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(bits, mb);
     }
 }
 
