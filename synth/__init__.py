@@ -69,6 +69,28 @@ def wide_exponent_bits(shape, dt, seed, idx, emin, emax):
     return to_bits((sign * np.exp2(e) * (1.0 + f)).astype(np.float32), dt)
 
 
+def hashed_ints(rows, cols, lo, hi, seed, idx, xp=np, device=None):
+    """Integers in [lo, hi] at (r, c) for r in ``rows``, c in ``cols`` (index
+    arrays), from a closed-form 32-bit hash of (r, c, seed, idx), as float32 --
+    so any block of a very large tensor can be produced on its own, by numpy
+    (``xp=np``) or by torch on a device (``xp=torch``), with the same values.
+    Every row differs from every other with high probability, so a row or
+    column index off by any amount changes the values read."""
+    if xp is np:
+        r = np.asarray(rows, dtype=np.int64)[:, None]
+        c = np.asarray(cols, dtype=np.int64)[None, :]
+    else:
+        r = torch.as_tensor(rows, dtype=torch.int64, device=device)[:, None]
+        c = torch.as_tensor(cols, dtype=torch.int64, device=device)[None, :]
+    m32 = 0xFFFFFFFF
+    h = (r * 0x9E3779B1 + c * 0x85EBCA77 + (seed * 1000 + idx) * 0xC2B2AE3D) & m32
+    h = h ^ (h >> 15)
+    h = (h * 0x2C1B3C6D) & m32
+    h = h ^ (h >> 12)
+    v = lo + h % (hi - lo + 1)
+    return v.astype(np.float32) if xp is np else v.to(torch.float32)
+
+
 # --------------------------------------------------------------------------
 # linear workloads
 # --------------------------------------------------------------------------

@@ -1,0 +1,93 @@
+"""Operands and outputs beyond 4 GiB.
+
+X [524288, 4608] bf16 is 4.8 GB: the forward and dW read it through the
+register-staged MFMA kernel (the direct-load kernel addresses its operands with
+32-bit buffer offsets and takes operands up to 1 GiB), and dX writes a 4.8 GB
+output.  Inputs are small integers from a closed-form hash (generated on the GPU
+block by block, and on the host for the sampled rows and columns), so every sum
+is exact in f32 and the GPU bits must equal the oracle's exactly.  Sampled rows
+and columns include ones whose byte offsets lie beyond 2^32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_invariant_gemm_amd as dig
+import oracle
+import synth
+from parity import dev, host
+
+pytestmark = pytest.mark.gpu
+
+M, K, N = 524288, 4608, 64
+SEED = 91
+ROWS = np.array([0, 1, 262147, 466034, 500001, M - 2, M - 1], dtype=np.int64)
+COLS = np.array([0, 1, 2305, K - 1], dtype=np.int64)
+
+
+def bf16_bits(v: np.ndarray) -> np.ndarray:
+    return synth.to_bits(v, synth.BF16)
+
+
+@pytest.fixture(scope="module")
+def big():
+    assert 466034 * K * 2 > 2 ** 32  # sampled rows past 4 GiB of X
+    print(f"large operands: generating X [{M}, {K}] on the GPU", flush=True)
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    cols = torch.arange(K, device="cuda")
+    for r0 in range(0, M, 32768):
+        rows = torch.arange(r0, r0 + 32768, device="cuda")
+        x[r0:r0 + 32768] = synth.hashed_ints(rows, cols, -4, 3, SEED, 0, xp=torch,
+                                             device="cuda").to(torch.bfloat16)
+    w = bf16_bits(synth.hashed_ints(np.arange(K), np.arange(N), -4, 3, SEED, 1))
+    dy = bf16_bits(synth.hashed_ints(np.arange(M), np.arange(N), -1, 1, SEED, 2))
+    torch.cuda.synchronize()
+    return {"x": x.view(torch.int16), "w": w, "dy": dy, "w_d": dev(w), "dy_d": dev(dy)}
+
+
+def x_rows(rows):
+    return bf16_bits(synth.hashed_ints(rows, np.arange(K), -4, 3, SEED, 0))
+
+
+def test_forward_beyond_4gib(big):
+    print("large operands: forward", flush=True)
+    y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    dig.check(dig.bi_forward(y, big["x"], big["w_d"], None, M, K, N, dig.BI_BF16,
+                             torch.cuda.current_stream(), 1), "bi_forward")
+    got = host(y[torch.from_numpy(ROWS).cuda()], np.uint16)
+    res = oracle.linear_forward(synth.BF16, x_rows(ROWS), big["w"], None, len(ROWS), K, N)
+    assert np.array_equal(got, res.out)
+    # the generator agrees with itself across backends on these rows
+    assert np.array_equal(host(big["x"][torch.from_numpy(ROWS).cuda()], np.uint16), x_rows(ROWS))
+
+
+def test_dx_output_beyond_4gib(big):
+    print("large operands: dX (4.8 GB output)", flush=True)
+    dx = torch.empty((M, K), dtype=torch.int16, device="cuda")
+    dig.check(dig.bi_backward_dx(dx, big["dy_d"], big["w_d"], M, K, N, dig.BI_BF16,
+                                 torch.cuda.current_stream(), 1), "bi_backward_dx")
+    got = host(dx[torch.from_numpy(ROWS).cuda()], np.uint16)
+    del dx
+    res = oracle.linear_dx(synth.BF16, big["dy"][ROWS], big["w"], len(ROWS), K, N)
+    assert np.array_equal(got, res.out)
+
+
+def test_dw_and_bias_grad_over_half_a_million_rows(big):
+    print("large operands: dW (chunked) and bias gradient", flush=True)
+    s = torch.cuda.current_stream()
+    nb = dig.bi_backward_dw_workspace_bytes(M, K, N, dig.BI_BF16, 1)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dw = torch.empty((K, N), dtype=torch.int16, device="cuda")
+    dig.check(dig.bi_backward_dw(dw, big["x"], big["dy_d"], M, K, N, dig.BI_BF16, ws, nb, s, 1),
+              "bi_backward_dw")
+    got = host(dw[torch.from_numpy(COLS).cuda()], np.uint16)
+    xc = bf16_bits(synth.hashed_ints(np.arange(M), COLS, -4, 3, SEED, 0))
+    res = oracle.linear_dw(synth.BF16, xc, big["dy"], M, len(COLS), N)
+    assert np.array_equal(got, res.out)
+
+    nb = dig.bi_bias_grad_workspace_bytes(M, N, dig.BI_BF16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    db = torch.empty(N, dtype=torch.int16, device="cuda")
+    dig.check(dig.bi_bias_grad(db, big["dy_d"], M, N, dig.BI_BF16, ws, nb, s), "bi_bias_grad")
+    assert np.array_equal(host(db, np.uint16), oracle.bias_grad(synth.BF16, big["dy"], M, N).out)
