@@ -6,7 +6,9 @@ register-staged MFMA kernel (the direct-load kernel addresses its operands with
 output.  Inputs are small integers from a closed-form hash (generated on the GPU
 block by block, and on the host for the sampled rows and columns), so every sum
 is exact in f32 and the GPU bits must equal the oracle's exactly.  Sampled rows
-and columns include ones whose byte offsets lie beyond 2^32.
+and columns include ones whose byte offsets lie beyond 2^32.  The fp8 GEMM is
+checked the same way on A [1048576, 4608] e4m3 (4.8 GB, register-staged fp8
+kernel).
 """
 import numpy as np
 import pytest
@@ -91,3 +93,34 @@ def test_dw_and_bias_grad_over_half_a_million_rows(big):
     db = torch.empty(N, dtype=torch.int16, device="cuda")
     dig.check(dig.bi_bias_grad(db, big["dy_d"], M, N, dig.BI_BF16, ws, nb, s), "bi_bias_grad")
     assert np.array_equal(host(db, np.uint16), oracle.bias_grad(synth.BF16, big["dy"], M, N).out)
+
+
+def e4m3_codes(v: np.ndarray) -> np.ndarray:
+    """Small integers as e4m3fn codes (exact)."""
+    return torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_operand_beyond_4gib():
+    m8, k8, n8 = 1048576, 4608, 64
+    rows = np.array([0, 5, 524289, 1000003, m8 - 1], dtype=np.int64)
+    assert 1000003 * k8 > 2 ** 32
+    print(f"large operands: fp8 A [{m8}, {k8}] generated on the GPU", flush=True)
+    a = torch.empty((m8, k8), dtype=torch.uint8, device="cuda")
+    cols = torch.arange(k8, device="cuda")
+    for r0 in range(0, m8, 32768):
+        r = torch.arange(r0, r0 + 32768, device="cuda")
+        a[r0:r0 + 32768] = synth.hashed_ints(r, cols, -8, 8, SEED, 3, xp=torch, device="cuda").to(
+            torch.float8_e4m3fn).view(torch.uint8)
+    bt = e4m3_codes(synth.hashed_ints(np.arange(n8), np.arange(k8), -8, 8, SEED, 4))
+    da = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+    db = torch.tensor([0.25], dtype=torch.float32, device="cuda")
+    y = torch.empty((m8, n8), dtype=torch.int16, device="cuda")
+    print("large operands: fp8 GEMM", flush=True)
+    dig.check(dig.bi_fp8_mm(y, a, dev(bt), da, db, m8, k8, n8, torch.cuda.current_stream(), 1),
+              "bi_fp8_mm")
+    got = host(y[torch.from_numpy(rows).cuda()], np.uint16)
+    a_rows = e4m3_codes(synth.hashed_ints(rows, np.arange(k8), -8, 8, SEED, 3))
+    assert np.array_equal(host(a[torch.from_numpy(rows).cuda()], np.uint8), a_rows)
+    res = oracle.fp8_mm(a_rows, bt, 0.5, 0.25, len(rows), k8, n8)
+    assert np.array_equal(got, res.out)
