@@ -420,7 +420,7 @@ int bi_fp8_transpose_quantize(void *dst, const void *src, const float *scale_inv
     if (checked_elems(rows, cols) < 0 || rows > (int64_t)65535 * 64) return BI_ERR_TOO_LARGE;
     if (rows == 0 || cols == 0) return BI_OK;
     if (!dst || !src || !scale_inv) return BI_ERR_NULL;
-    return hip_status(launch_transpose_quantize(src, scale_inv, dst, amax, rows, cols, fmt,
+    return hip_status(launch_transpose_quantize(src, scale_inv, dst, nullptr, amax, rows, cols, fmt,
                                                 stream));
 }
 
@@ -477,23 +477,33 @@ int bi_fp8_linear_backward(void *dx, void *dw, const void *g, const void *x, con
     const size_t need = o_amax + 256;
     if (!workspace || workspace_bytes < need) return BI_ERR_WORKSPACE;
     char *ws = static_cast<char *>(workspace);
-    float *scratch = reinterpret_cast<float *>(ws + o_amax);  // amax of the transposed copies
-    if (launch_zero3(amax_g, scratch, nullptr, stream) != hipSuccess) return BI_ERR_HIP;
-    int st = bi_fp8_quantize(ws, g, sg_inv, amax_g, m * n, BI_FP8_E4M3, stream);
-    if (st != BI_OK) return st;
-    if (dx && m > 0 && k > 0) {
+    const bool need_dx = dx && m > 0 && k > 0, need_dw = dw && n > 0 && k > 0;
+    if (launch_zero3(amax_g, nullptr, nullptr, stream) != hipSuccess) return BI_ERR_HIP;
+    // g is read once: with dW wanted, the transposing quantiser writes gt8 and
+    // (when dX is wanted too) g8 from the same read and folds amax_g; the
+    // transposed copies of w and x fold no max-abs (the page keeps theirs in a
+    // scratch value that nothing reads)
+    hipError_t e;
+    if (need_dw)
+        e = launch_transpose_quantize(g, sg_inv, ws + o_gt, need_dx ? ws : nullptr, amax_g, m, n,
+                                      BI_FP8_E4M3, stream);
+    else
+        e = launch_quantize(g, sg_inv, ws, amax_g, m * n, BI_FP8_E4M3, stream);
+    if (e != hipSuccess) return BI_ERR_HIP;
+    int st;
+    if (need_dx) {
         // dX[m,k] = (g8[m,n] . wt8[k,n]^T) * sg * sw
-        st = bi_fp8_transpose_quantize(ws + o_wt, w, sw_inv, scratch, n, k, BI_FP8_E4M3, stream);
-        if (st != BI_OK) return st;
+        e = launch_transpose_quantize(w, sw_inv, ws + o_wt, nullptr, nullptr, n, k, BI_FP8_E4M3,
+                                      stream);
+        if (e != hipSuccess) return BI_ERR_HIP;
         st = fp8_gemm(dx, ws, ws + o_wt, sg, sw, nullptr, m, n, k, stream, tc);
         if (st != BI_OK) return st;
     }
-    if (dw && n > 0 && k > 0) {
+    if (need_dw) {
         // dW[n,k] = (gt8[n,m] . xt8[k,m]^T) * sg * sx
-        st = bi_fp8_transpose_quantize(ws + o_gt, g, sg_inv, scratch, m, n, BI_FP8_E4M3, stream);
-        if (st != BI_OK) return st;
-        st = bi_fp8_transpose_quantize(ws + o_xt, x, sx_inv, scratch, m, k, BI_FP8_E4M3, stream);
-        if (st != BI_OK) return st;
+        e = launch_transpose_quantize(x, sx_inv, ws + o_xt, nullptr, nullptr, m, k, BI_FP8_E4M3,
+                                      stream);
+        if (e != hipSuccess) return BI_ERR_HIP;
         st = fp8_gemm(dw, ws + o_gt, ws + o_xt, sg, sx, nullptr, n, m, k, stream, tc);
         if (st != BI_OK) return st;
     }

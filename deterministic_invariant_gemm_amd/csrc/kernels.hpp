@@ -110,9 +110,10 @@ hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, hipStream_t s);
 // src [rows, cols] -> dst [cols, rows].
 hipError_t launch_quantize(const void *src, const float *scale_inv, void *dst, float *amax,
                            int64_t n, int fmt, hipStream_t s);
+// dst_rows (nullable) also receives the untransposed codes from the same read.
 hipError_t launch_transpose_quantize(const void *src, const float *scale_inv, void *dst,
-                                     float *amax, int64_t rows, int64_t cols, int fmt,
-                                     hipStream_t s);
+                                     void *dst_rows, float *amax, int64_t rows, int64_t cols,
+                                     int fmt, hipStream_t s);
 // Bias gradient (bias_grad.hip): out[n] = RNE(column sums of dy [m, n]) in a
 // fixed order; rows in chunks of BG_CHUNK, nchunks = max(1, ceil(m / BG_CHUNK));
 // with more than one chunk ws holds nchunks * n f32 partials.  vec: dy 16-byte

@@ -122,10 +122,12 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t *src, const
 // 16-byte aligned; vec_out: rows % 16 == 0 and dst 16-byte aligned.
 constexpr int TR = 256;
 
+// dst_rows (nullable): also the untransposed codes, [rows, cols], from the same
+// read of the source; vec_rows: its 16-byte pieces may be stored whole.
 template <int FMT>
 __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
-    const uint16_t *src, const float *scale_inv, uint8_t *dst, float *amax, int64_t rows,
-    int64_t cols, int vec_in, int vec_out) {
+    const uint16_t *src, const float *scale_inv, uint8_t *dst, uint8_t *dst_rows, float *amax,
+    int64_t rows, int64_t cols, int vec_in, int vec_out, int vec_rows) {
     __shared__ uint32_t tile[TR][64 / 4 + 1];  // bytes of source row r at tile[r][..], padded
     const float s = *scale_inv;
     const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * 64;
@@ -149,12 +151,25 @@ __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
                 f[q] = (gr < rows && gc + q < cols) ? bf16_bits_to_f32(src[gr * cols + gc + q])
                                                     : 0.0f;
         }
+        uint32_t code[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             mx = fmaxf(mx, fmaxf(fmaxf(fabsf(f[4 * q]), fabsf(f[4 * q + 1])),
                                  fmaxf(fabsf(f[4 * q + 2]), fabsf(f[4 * q + 3]))));
-            tile[rr][cc / 4 + q] = (uint32_t)cvt2<FMT, true>(
+            code[q] = (uint32_t)cvt2<FMT, true>(
                 f[4 * q + 2] * s, f[4 * q + 3] * s, cvt2<FMT, false>(f[4 * q] * s, f[4 * q + 1] * s, 0));
+            tile[rr][cc / 4 + q] = code[q];
+        }
+        if (dst_rows && gr < rows) {
+            uint8_t *d = dst_rows + gr * cols + gc;
+            if (vec_rows && gc + 16 <= cols) {
+                __builtin_nontemporal_store(u32x4{code[0], code[1], code[2], code[3]},
+                                            reinterpret_cast<u32x4 *>(d));
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (gc + q < cols) d[q] = (uint8_t)((code[q >> 2] >> (8 * (q & 3))) & 0xffu);
+            }
         }
     }
     __syncthreads();
@@ -217,21 +232,23 @@ hipError_t launch_quantize(const void *src, const float *scale_inv, void *dst, f
 }
 
 hipError_t launch_transpose_quantize(const void *src, const float *scale_inv, void *dst,
-                                     float *amax, int64_t rows, int64_t cols, int fmt,
-                                     hipStream_t s) {
+                                     void *dst_rows, float *amax, int64_t rows, int64_t cols,
+                                     int fmt, hipStream_t s) {
     if (rows <= 0 || cols <= 0) return hipSuccess;
     const int64_t gx = (cols + 63) / 64, gy = (rows + TR - 1) / TR;
     if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
     const int vec_in = cols % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0;
     const int vec_out = rows % 16 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+    const int vec_rows = cols % 16 == 0 && (reinterpret_cast<uintptr_t>(dst_rows) & 15) == 0;
     const uint16_t *sp = static_cast<const uint16_t *>(src);
     uint8_t *dp = static_cast<uint8_t *>(dst);
+    uint8_t *rp = static_cast<uint8_t *>(dst_rows);
     if (fmt == DT_E5M2)
         hipLaunchKernelGGL(transpose_quantize_kernel<DT_E5M2>, dim3(gx, gy), dim3(QT), 0, s, sp,
-                           scale_inv, dp, amax, rows, cols, vec_in, vec_out);
+                           scale_inv, dp, rp, amax, rows, cols, vec_in, vec_out, vec_rows);
     else
         hipLaunchKernelGGL(transpose_quantize_kernel<DT_E4M3>, dim3(gx, gy), dim3(QT), 0, s, sp,
-                           scale_inv, dp, amax, rows, cols, vec_in, vec_out);
+                           scale_inv, dp, rp, amax, rows, cols, vec_in, vec_out, vec_rows);
     return hipGetLastError();
 }
 

@@ -218,9 +218,11 @@ int bi_fp8_linear_forward(void *y, const void *x, const void *w, const void *bia
  *   qg = FP8_e4m3(g * sg_inv), qw, qx as in the forward
  * g: [m,n], x: [m,k], w: [n,k] bf16; dx (nullable: skipped) [m,k] and dw
  * (nullable: skipped) [n,k] bf16.  amax_g (nullable) is set to max |g|; the
- * transposed copies' max-abs goes to workspace scratch, never to amax_g.  The
- * bias gradient is not computed here.  workspace: at least
- * bi_fp8_linear_workspace_bytes(m, k, n) bytes. */
+ * transposed copies of w and x record no max-abs (the page keeps theirs in a
+ * scratch value apart from amax_g that nothing reads).  g is read once when dw
+ * is wanted (its row-major and transposed codes come from the same read).  The
+ * bias gradient is not computed here (bi_bias_grad on g gives it).  workspace:
+ * at least bi_fp8_linear_workspace_bytes(m, k, n) bytes. */
 int bi_fp8_linear_backward(void *dx, void *dw, const void *g, const void *x, const void *w,
                            const float *sg, const float *sw, const float *sx,
                            const float *sg_inv, const float *sw_inv, const float *sx_inv,

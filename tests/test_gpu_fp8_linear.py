@@ -145,10 +145,11 @@ def test_fp8_linear_parity(shape, bias, tc):
     check(host(dw, np.uint16), rdw, synth.BF16, f"fp8 linear dW {shape}")
     assert ag == rdx.amax_g
     # one gradient at a time gives the same bits
-    dx1, dw1, _ = L.backward(want_dw=False, tc=tc)
-    dx2, dw2, _ = L.backward(want_dx=False, tc=tc)
+    dx1, dw1, ag1 = L.backward(want_dw=False, tc=tc)
+    dx2, dw2, ag2 = L.backward(want_dx=False, tc=tc)
     assert dw1 is None and dx2 is None
     assert digest(dx1) == digest(dx) and digest(dw2) == digest(dw)
+    assert ag1 == ag2 == rdx.amax_g
 
 
 def test_fp8_linear_integer_bit_exact():
