@@ -50,7 +50,7 @@ def train(seed=0, steps=20, batch=512, d_in=768, d_hidden=3072, d_out=768, dtype
         with torch.no_grad():
             for p in model.parameters():
                 p.sub_(lr * p.grad)
-        losses.append(float(loss))
+        losses.append(float(loss.detach()))
     return model, losses
 
 
