@@ -481,12 +481,12 @@ def bench_bias_grad(args, torch, dig, synth):
 # Candidate MFMA tiles per op of the default workload (tile id 40 + base: direct
 # loads; 100 + base: the same with copies spread between MFMAs).  Shapes:
 # 41 256x256 2x2 waves, 42 256x192 2x2, 44 128x128 2x2, 45 128x96 4x1,
-# 48 96x96 3x1, 50 256x96 4x1, 51 256x192 4x2, 52 256x256 4x2, 55 128x128 2x4,
-# 57 96x96 1x3.  The first id of each list is the default.
+# 48 96x96 3x1, 49 128x192 2x2, 50 256x96 4x1, 51 256x192 4x2, 52 256x256 4x2,
+# 55 128x128 2x4, 57 96x96 1x3.  The first id of each list is the default.
 TILE_CANDIDATES = {
-    "fwd": [51, 52, 41, 42, 44, 55, 111, 115],
-    "dX": [45, 105, 115, 55, 44, 50, 51, 42],
-    "dW": [115, 55, 104, 44, 48, 108, 57, 45, 105],
+    "fwd": [111, 51, 52, 41, 42, 44, 49, 55, 115],
+    "dX": [45, 44, 105, 115, 55, 50, 51, 42],
+    "dW": [57, 48, 44, 45, 115, 55, 104, 108, 105],
 }
 
 

@@ -270,17 +270,20 @@ struct FragOf<true, R, ESZ> {
     using type = RcFrag<ESZ>;
 };
 
-// Tiles of two to four MFMA waves (burst copies) get one extra wave that
-// issues all the copies: the MFMA waves then only read fragments, multiply and
-// meet at the stage barriers.  With two or three MFMA waves the copy wave has a
-// SIMD of its own; with four it shares one, which halves that MFMA wave's
-// register budget, so only wave tiles of at most 96 accumulator registers
-// (e.g. 64x96) qualify.  Eight-wave tiles keep their copies for the same reason.
+// Tiles of two to four MFMA waves (burst copies) get DL_NPW extra waves that
+// issue all the copies: the MFMA waves then only read fragments, multiply and
+// meet at the stage barriers, and the copies of a stage are split over four
+// waves, so four times as many stages can be in flight under each wave's
+// 63-load counter.  A copy wave that shares a SIMD with an MFMA wave halves that
+// wave's register budget, so four-MFMA-wave tiles qualify only with wave tiles
+// of at most 96 accumulator registers (e.g. 64x96); eight-wave tiles keep their
+// copies for the same reason.
 constexpr bool dl_producer(int nw, bool spread, int wtm, int wtn) {
     return !spread && nw >= 2 && nw <= 4 && (nw < 4 || wtm * wtn / 64 <= 96);
 }
+constexpr int DL_NPW = 4;
 constexpr int dl_threads(int nw, bool spread, int wtm, int wtn) {
-    return 64 * (nw + (dl_producer(nw, spread, wtm, wtn) ? 1 : 0));
+    return 64 * (nw + (dl_producer(nw, spread, wtm, wtn) ? DL_NPW : 0));
 }
 
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) 
     constexpr int NW = WGM * WGN;
     constexpr bool PROD = dl_producer(NW, SPREAD, BM / WGM, BN / WGN);
     constexpr int NTH = dl_threads(NW, SPREAD, BM / WGM, BN / WGN);
-    constexpr int NWC = PROD ? 1 : NW;  // waves that issue the copies
+    constexpr int NWC = PROD ? DL_NPW : NW;  // waves that issue the copies
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
@@ -314,8 +317,9 @@ __global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) 
     const int wm = wave / WGN, wn = wave % WGN;
 
     const TileInfo ti = decode_tile<MODE, BM, BN, NTH>(p, t);
-    const bool is_prod = PROD && wave == NW;
-    const int cwave = PROD ? 0 : wave;  // index of this wave among the copying waves
+    const bool is_prod = PROD && wave >= NW;
+    // index of this wave among the copying waves
+    const int cwave = PROD ? (is_prod ? wave - NW : 0) : wave;
     if (ti.skip) return;
     const int64_t row0 = ti.row0, col0 = ti.col0;
     const float bias_v = fetch_bias<DT, EPI, BN>(p, col0, t);
