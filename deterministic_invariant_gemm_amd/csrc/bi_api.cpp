@@ -82,20 +82,21 @@ int pick_tile(int op, int64_t k, int64_t n) {
         if (cols % 96 == 0 && cols <= 1536) return 45;  // 128x96, four waves along M
         return cols >= 128 ? 115 : 46;                  // 128x128, eight waves, spread
     case OP_DW:
-        // 96x96 with three waves side by side along N (one per SIMD on three
-        // SIMDs, plus the copy wave) while that makes at most one tile per CU
-        // and fills at least half of them; else 128x128, eight waves, copies
-        // spread between MFMAs
+        // 96x96 with three MFMA waves side by side along N (one per SIMD on
+        // three SIMDs, plus the copy waves) while that makes at most one tile
+        // per CU and fills at least half of them
         if (k >= 96 && n >= 96 && cdiv(k, 96) * cdiv(n, 96) <= 256 &&
             cdiv(k, 96) * cdiv(n, 96) >= 128)
             return 57;
-        return (k >= 128 && n >= 128) ? 115 : 46;
+        // 128x128, four MFMA waves and four copy waves
+        return (k >= 128 && n >= 128) ? 44 : 46;
     case OP_GFWD: case OP_GDIN:
         // 256x192 / 128x128, eight waves, copies spread
         if (cols >= 1024) return 111;
         return cols >= 128 ? 115 : 46;
     case OP_GDW:
-        return (k >= 128 && n >= 128) ? 115 : 46;
+        // 128x128, four MFMA waves and four copy waves
+        return (k >= 128 && n >= 128) ? 44 : 46;
     }
     return 44;
 }
