@@ -35,9 +35,12 @@ def run_all(fn):
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
-@pytest.mark.parametrize("shape", [(300, 200, 260), (520, 136, 392), (700, 264, 456)],
+@pytest.mark.parametrize("shape", [(300, 200, 260), (520, 136, 392), (700, 264, 456),
+                                   (2500, 200, 264)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_linear_tiles_identical(dt, shape):
+    """The last shape reduces dW over three 1024-row chunks (f32 partials and
+    the ordered chunk sum) in every tile."""
     m, k, n = shape
     d = synth.linear(m, k, n, dt, seed=61 + m, sigma_w=0.05)
     x, w, b, dy = dev(d["x"]), dev(d["w"]), dev(d["b"]), dev(d["dy"])
