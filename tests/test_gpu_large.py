@@ -8,7 +8,8 @@ block by block, and on the host for the sampled rows and columns), so every sum
 is exact in f32 and the GPU bits must equal the oracle's exactly.  Sampled rows
 and columns include ones whose byte offsets lie beyond 2^32.  The fp8 GEMM is
 checked the same way on A [1048576, 4608] e4m3 (4.8 GB, register-staged fp8
-kernel).
+kernel), the grouped forward on X, and the f32 scalar tier on X f32
+[524288, 2304] (4.8 GB).
 """
 import numpy as np
 import pytest
@@ -123,4 +124,41 @@ def test_fp8_operand_beyond_4gib():
     a_rows = e4m3_codes(synth.hashed_ints(rows, np.arange(k8), -8, 8, SEED, 3))
     assert np.array_equal(host(a[torch.from_numpy(rows).cuda()], np.uint8), a_rows)
     res = oracle.fp8_mm(a_rows, bt, 0.5, 0.25, len(rows), k8, n8)
+    assert np.array_equal(got, res.out)
+
+
+def test_grouped_input_beyond_4gib(big):
+    """The bf16 X above as the grouped GEMM's input (4 experts, padding rows
+    at the end): segment-anchored register-staged tiles past 4 GiB."""
+    print("large operands: grouped forward", flush=True)
+    e = 4
+    ids, offsets = synth.route(M, e, SEED, pad_rows=1000, idx=5)
+    wts = bf16_bits(synth.hashed_ints(np.arange(e * N), np.arange(K), -4, 3, SEED, 6))
+    y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    dig.check(dig.bi_grouped_nt(y, big["x"], dev(wts), dev(ids), dev(offsets), M, K, N, e,
+                                dig.BI_BF16, torch.cuda.current_stream(), 1), "bi_grouped_nt")
+    rows = np.concatenate([ROWS, [M - 1001, M - 1000]])  # the last routed row, the first padding row
+    got = host(y[torch.from_numpy(rows).cuda()], np.uint16)
+    res = oracle.grouped_fwd(synth.BF16, x_rows(rows), wts, ids[rows], len(rows), K, N, e)
+    assert np.array_equal(got, res.out)
+    assert not got[-1].any()  # padding row: exact +0
+
+
+def test_f32_scalar_tier_beyond_4gib():
+    """f32 always runs the scalar FMA tier: X f32 [524288, 2304] (4.8 GB)."""
+    m, k, n = M, 2304, 64
+    print(f"large operands: f32 X [{m}, {k}] on the scalar tier", flush=True)
+    x = torch.empty((m, k), dtype=torch.float32, device="cuda")
+    cols = torch.arange(k, device="cuda")
+    for r0 in range(0, m, 32768):
+        r = torch.arange(r0, r0 + 32768, device="cuda")
+        x[r0:r0 + 32768] = synth.hashed_ints(r, cols, -4, 3, SEED, 7, xp=torch, device="cuda")
+    w = synth.hashed_ints(np.arange(k), np.arange(n), -4, 3, SEED, 8).view(np.uint32)
+    y = torch.empty((m, n), dtype=torch.int32, device="cuda")
+    assert dig.bi_plan(dig.OP_FWD, dig.BI_F32, 1, k, n)[0] == 0
+    dig.check(dig.bi_forward(y, x, dev(w), None, m, k, n, dig.BI_F32,
+                             torch.cuda.current_stream(), 1), "bi_forward f32")
+    got = host(y[torch.from_numpy(ROWS).cuda()], np.uint32)
+    xr = synth.hashed_ints(ROWS, np.arange(k), -4, 3, SEED, 7).view(np.uint32)
+    res = oracle.linear_forward(synth.F32, xr, w, None, len(ROWS), k, n)
     assert np.array_equal(got, res.out)
