@@ -61,7 +61,10 @@ __device__ __forceinline__ void fold_amax(float mx, float *amax) {
 
 // vec: src and dst 16-byte aligned.  Each thread converts UN chunks of 16
 // elements per step (all loads issued first, so more bytes are in flight),
-// the remainder element by element.
+// the remainder element by element.  The source is read once (streaming
+// loads); the codes are stored normally, so that the GEMM that reads them next
+// finds them in the caches (streaming stores made the scaled linear 4-5 %
+// slower).
 constexpr int UN = 4;
 
 template <int FMT>
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t *src, const
             }
 #pragma unroll
             for (int u = 0; u < UN; ++u)
-                __builtin_nontemporal_store(convert16<FMT>(a[u], b[u], s, mx), d4 + c + u * stride);
+                d4[c + u * stride] = convert16<FMT>(a[u], b[u], s, mx);
         }
         for (; c < nchunk; c += stride)
             d4[c] = convert16<FMT>(s4[2 * c], s4[2 * c + 1], s, mx);
@@ -163,8 +166,7 @@ __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
         if (dst_rows && gr < rows) {
             uint8_t *d = dst_rows + gr * cols + gc;
             if (vec_rows && gc + 16 <= cols) {
-                __builtin_nontemporal_store(u32x4{code[0], code[1], code[2], code[3]},
-                                            reinterpret_cast<u32x4 *>(d));
+                *reinterpret_cast<u32x4 *>(d) = u32x4{code[0], code[1], code[2], code[3]};
             } else {
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
@@ -191,8 +193,7 @@ __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
         if (go < cols) {
             uint8_t *d = dst + go * rows + gr;
             if (vec_out && gr + 16 <= rows) {
-                __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]},
-                                            reinterpret_cast<u32x4 *>(d));
+                *reinterpret_cast<u32x4 *>(d) = u32x4{w[0], w[1], w[2], w[3]};
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
