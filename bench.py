@@ -3,7 +3,9 @@
 
 Default workload: the bf16 transformer MLP-up linear 768 -> 3072 at M = 4096
 (X[4096,768], W[768,3072] stored [in,out], bias[3072], dY[4096,3072]).  One
-step = forward + dX + dW through the C ABI on the MFMA tier.  Inputs are
+step = forward (bi_forward) + dX and dW (bi_linear_backward, whose dX and dW
+tiles share one launch at this shape) through the C ABI on the MFMA tier; dX
+and dW in launches of their own are timed beside it for reference.  Inputs are
 seeded synthetic data already resident in HBM when timing starts.
 
 Prints ONE JSON line with the whole-step throughput (TFLOP/s, from the wall
@@ -249,19 +251,29 @@ def bench_linear(args, torch, dig, synth):
     dw = torch.empty((k, n), dtype=torch.int16, device="cuda")
     wsb = dig.bi_backward_dw_workspace_bytes(m, k, n, dt, 1)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    # one training step of the layer: the forward, then both gradients from one
+    # call (dX and dW tiles share a launch at this shape)
     ops = [
         ("fwd", lambda s: dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, s, 1))),
+        ("bwd", lambda s: dig.check(dig.bi_linear_backward(dx, dw, dy, x, w, m, k, n, dt,
+                                                           ws if wsb else None, wsb, s, 1))),
+    ]
+    ms, per = timed_steps(torch, ops, args.steps, args.warmup)
+    # the two gradients in launches of their own, for reference (not in the step)
+    alone = [
         ("dX", lambda s: dig.check(dig.bi_backward_dx(dx, dy, w, m, k, n, dt, s, 1))),
         ("dW", lambda s: dig.check(dig.bi_backward_dw(dw, x, dy, m, k, n, dt,
                                                       ws if wsb else None, wsb, s, 1))),
     ]
-    ms, per = timed_steps(torch, ops, args.steps, args.warmup)
+    _, sep = timed_steps(torch, alone, args.steps, args.warmup)
     flop = 2.0 * m * k * n
+    flops = {"fwd": flop, "bwd": 2 * flop, "dX": flop, "dW": flop}
     # algorithmic bytes per launch: each operand read once, the output written once
-    bytes_ = {"fwd": 2 * (m * k + k * n + n + m * n), "dX": 2 * (m * n + k * n + m * k),
-              "dW": 2 * (m * k + m * n + k * n)}
+    # (the shared backward launch reads dY once for both gradients)
+    bytes_ = {"fwd": 2 * (m * k + k * n + n + m * n),
+              "bwd": 2 * (m * n + k * n + m * k) + 2 * (m * k + k * n)}
     dominant = max(per, key=per.get)
-    achieved = flop / (per[dominant] * 1e-3) / 1e12
+    achieved = flops[dominant] / (per[dominant] * 1e-3) / 1e12
     out = {
         "metric": "TFLOP/s and % MFMA peak, bf16 fwd/dX/dW at M=4096, 768->3072; "
                   "bit-exact determinism",
@@ -273,7 +285,8 @@ def bench_linear(args, torch, dig, synth):
         "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": f"{args.dtype} training linear 768->3072 (weight [in,out]) at "
                                "M=4096: forward + dX + dW, MFMA tier",
-                   "M": m, "K": k, "N": n, "bias": True},
+                   "M": m, "K": k, "N": n, "bias": True,
+                   "calls": "bi_forward, bi_linear_backward"},
         "timing": f"value: wall time of the timed steps (no events), after {SETTLE_MS:.0f} ms of "
                   "untimed steps (clock ramp) and the warm-up steps; kernel times: HIP events "
                   "around each launch in a second pass of the same steps",
@@ -283,9 +296,12 @@ def bench_linear(args, torch, dig, synth):
                      "traffic": recorded_traffic("linear_768x3072_m4096_traffic.json", dominant),
                      "algorithmic_bytes": bytes_[dominant]},
         "ops": {name: {"us": round(v * 1e3, 2),
-                       "tflops": round(flop / (v * 1e-3) / 1e12, 2),
-                       "frac_peak": round(flop / (v * 1e-3) / 1e12 / BF16_PEAK, 4)}
+                       "tflops": round(flops[name] / (v * 1e-3) / 1e12, 2),
+                       "frac_peak": round(flops[name] / (v * 1e-3) / 1e12 / BF16_PEAK, 4)}
                 for name, v in per.items()},
+        "separate_launches": {name: {"us": round(v * 1e3, 2),
+                                     "tflops": round(flops[name] / (v * 1e-3) / 1e12, 2)}
+                              for name, v in sep.items()},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_linear(d, args.cpu_seconds)

@@ -49,6 +49,8 @@ def load() -> ctypes.CDLL:
     L.bi_backward_dw_workspace_bytes.restype = sz
     L.bi_backward_dw.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, sz, vp, i32]
     L.bi_fp8_mm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i32]
+    L.bi_linear_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp, i32]
+    L.bi_linear_backward.restype = i32
     L.bi_bias_grad_workspace_bytes.argtypes = [i64, i64, i32]
     L.bi_bias_grad_workspace_bytes.restype = sz
     L.bi_bias_grad.argtypes = [vp, vp, i64, i64, i32, vp, sz, vp]
@@ -119,6 +121,12 @@ def bi_backward_dw(dw, x, dy, m, k, n, dtype, workspace, workspace_bytes, stream
                    tc=1) -> int:
     return load().bi_backward_dw(_p(dw), _p(x), _p(dy), m, k, n, dtype, _p(workspace),
                                  workspace_bytes, _s(stream), tc)
+
+
+def bi_linear_backward(dx, dw, dy, x, w, m, k, n, dtype, workspace, workspace_bytes, stream=None,
+                       tc=1) -> int:
+    return load().bi_linear_backward(_p(dx), _p(dw), _p(dy), _p(x), _p(w), m, k, n, dtype,
+                                     _p(workspace), workspace_bytes, _s(stream), tc)
 
 
 def bi_bias_grad_workspace_bytes(m, n, dtype) -> int:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libbi.so")
 SOURCES = ["bi_api.cpp", "scalar_tier.hip", "mfma_tier.hip", "mfma_fwd.hip", "mfma_dx.hip",
            "mfma_dw.hip", "mfma_grouped.hip", "fp8_tier.hip", "fp8_dl.hip",
-           "quant.hip", "bias_grad.hip"]
+           "quant.hip", "bias_grad.hip", "mfma_bwd.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",

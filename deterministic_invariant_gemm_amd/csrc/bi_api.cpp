@@ -173,6 +173,31 @@ int direct_tile(MfmaArgs &a, int tile, int64_t a_bytes, int64_t b_bytes) {
     return t;
 }
 
+// MFMA-tier arguments of dX = dY W^T ([m,k] from dy [m,n], w [k,n]) and the
+// tile that runs.
+int dx_mfma_args(MfmaArgs &a, void *dx, const void *dy, const void *w, int64_t m, int64_t k,
+                 int64_t n, const Plan &pl, int tc) {
+    a.a = dy; a.lda = n; a.b = w; a.ldb = n; a.c = dx; a.ldc = k;
+    a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
+    a.vec_a = aligned16(dy) && n % 8 == 0;
+    a.vec_b = aligned16(w) && n % 8 == 0;
+    a.vec_c = aligned8(dx) && k % 4 == 0;
+    return direct_tile(a, batch_tile(pl, tc, m, k), 2 * m * n, 2 * k * n);
+}
+
+// MFMA-tier arguments of dW = X^T dY ([k,n] from x [m,k], dy [m,n]; f32 chunk
+// partials into the workspace when chunks > 1) and the tile that runs.
+int dw_mfma_args(MfmaArgs &a, void *dw, const void *x, const void *dy, int64_t m, int64_t k,
+                 int64_t n, const Plan &pl, int64_t chunks, void *workspace) {
+    a.a = x; a.lda = k; a.b = dy; a.ldb = n; a.c = dw; a.ldc = n;
+    a.ws = static_cast<float *>(workspace);
+    a.rows = k; a.cols = n; a.red = m; a.chunk = pl.chunk; a.nchunks = chunks;
+    a.vec_a = aligned16(x) && k % 8 == 0;
+    a.vec_b = aligned16(dy) && n % 8 == 0;
+    a.vec_c = chunks > 1 ? (aligned16(workspace) && n % 4 == 0) : (aligned8(dw) && n % 4 == 0);
+    return direct_tile(a, pl.tile, 2 * m * k, 2 * m * n);
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,12 +276,7 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
         return hip_status(launch_scalar_gemm(a, dtype, dtype, 0, stream));
     }
     MfmaArgs a{};
-    a.a = dy; a.lda = n; a.b = w; a.ldb = n; a.c = dx; a.ldc = k;
-    a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
-    a.vec_a = aligned16(dy) && n % 8 == 0;
-    a.vec_b = aligned16(w) && n % 8 == 0;
-    a.vec_c = aligned8(dx) && k % 4 == 0;
-    const int tile = direct_tile(a, batch_tile(pl, tc, m, k), 2 * m * n, 2 * k * n);
+    const int tile = dx_mfma_args(a, dx, dy, w, m, k, n, pl, tc);
     return hip_status(launch_mfma_gemm(a, tile, dtype, /*both rc*/ 3, 0, stream));
 }
 
@@ -296,13 +316,7 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
         e = launch_scalar_gemm(a, dtype, epi ? BI_F32 : dtype, epi, stream);
     } else {
         MfmaArgs a{};
-        a.a = x; a.lda = k; a.b = dy; a.ldb = n; a.c = dw; a.ldc = n;
-        a.ws = static_cast<float *>(workspace);
-        a.rows = k; a.cols = n; a.red = m; a.chunk = pl.chunk; a.nchunks = chunks;
-        a.vec_a = aligned16(x) && k % 8 == 0;
-        a.vec_b = aligned16(dy) && n % 8 == 0;
-        a.vec_c = epi ? (aligned16(workspace) && n % 4 == 0) : (aligned8(dw) && n % 4 == 0);
-        const int tile = direct_tile(a, pl.tile, 2 * m * k, 2 * m * n);
+        const int tile = dw_mfma_args(a, dw, x, dy, m, k, n, pl, chunks, workspace);
         e = launch_mfma_gemm(a, tile, dtype, /*both strided*/ 0, epi, stream);
     }
     if (e != hipSuccess) return BI_ERR_HIP;
@@ -310,6 +324,36 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
         e = launch_chunk_sum(static_cast<const float *>(workspace), dw, k * n, chunks, dtype,
                              stream);
     return hip_status(e);
+}
+
+int bi_linear_backward(void *dx, void *dw, const void *dy, const void *x, const void *w,
+                       int64_t m, int64_t k, int64_t n, int dtype, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream, int tc) {
+    if (!dx && !dw) return BI_ERR_NULL;
+    if (!dw) return bi_backward_dx(dx, dy, w, m, k, n, dtype, stream, tc);
+    if (!dx) return bi_backward_dw(dw, x, dy, m, k, n, dtype, workspace, workspace_bytes, stream, tc);
+    // every check of the two calls, before anything is enqueued
+    if (!dtype_ok(dtype)) return BI_ERR_DTYPE;
+    if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
+    if (checked_elems(m, k) < 0 || checked_elems(k, n) < 0 || checked_elems(m, n) < 0)
+        return BI_ERR_TOO_LARGE;
+    { const int ts = tier_check(OP_DX, dtype, tc, k, n); if (ts != BI_OK) return ts; }
+    { const int ts = tier_check(OP_DW, dtype, tc, k, n); if (ts != BI_OK) return ts; }
+    if (m > 0 && k > 0 && n > 0 && (!dy || !w || !x)) return BI_ERR_NULL;
+    const Plan px = make_plan(OP_DX, dtype, tc, k, n), pw = make_plan(OP_DW, dtype, tc, k, n);
+    const int64_t chunks = dw_chunks(pw, m);
+    const size_t need = chunks > 1 ? (size_t)chunks * (size_t)k * (size_t)n * sizeof(float) : 0;
+    if (k > 0 && n > 0 && need > 0 && (!workspace || workspace_bytes < need))
+        return BI_ERR_WORKSPACE;
+    if (m > 0 && k > 0 && n > 0 && px.tile != 0 && pw.tile != 0 && chunks == 1) {
+        MfmaArgs ax{}, aw{};
+        const int tx = dx_mfma_args(ax, dx, dy, w, m, k, n, px, tc);
+        const int tw = dw_mfma_args(aw, dw, x, dy, m, k, n, pw, 1, nullptr);
+        if (mfma_backward_pair(tx, tw, dtype)) return hip_status(launch_mfma_backward(ax, tx, aw, tw, dtype, stream));
+    }
+    const int st = bi_backward_dx(dx, dy, w, m, k, n, dtype, stream, tc);
+    if (st != BI_OK) return st;
+    return bi_backward_dw(dw, x, dy, m, k, n, dtype, workspace, workspace_bytes, stream, tc);
 }
 
 size_t bi_bias_grad_workspace_bytes(int64_t m, int64_t n, int dtype) {

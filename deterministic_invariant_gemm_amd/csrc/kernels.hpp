@@ -100,6 +100,14 @@ const TileShape *mfma_tile(int id);  // null for an unknown id
 hipError_t launch_mfma_gemm(const MfmaArgs &p, int tile_id, int dt, int layout, int epi,
                             hipStream_t s);
 
+// dX (px: both operands reduction-contiguous, rounded) and dW (pw: both
+// strided, rounded, one chunk) of one linear layer in one launch, for the
+// direct-load tile pairs mfma_backward_pair() accepts (bf16 / f16); bits equal
+// those of the two launches.  hipErrorNotSupported (nothing launched) otherwise.
+bool mfma_backward_pair(int tile_x, int tile_w, int dt);
+hipError_t launch_mfma_backward(const MfmaArgs &px, int tile_x, const MfmaArgs &pw, int tile_w,
+                                int dt, hipStream_t s);
+
 hipError_t launch_fp8_gemm(const Fp8Args &p, int tile_id, hipStream_t s);
 // fp8 on the direct-load MFMA kernel (tile ids 40 + base, 100 + base):
 // C(i,j) = RNE_bf16((sum_r A(i,r) B(j,r)) * scale_a * scale_b), both operands

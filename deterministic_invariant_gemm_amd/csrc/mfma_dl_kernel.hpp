@@ -286,10 +286,20 @@ constexpr int dl_threads(int nw, bool spread, int wtm, int wtn) {
     return 64 * (nw + (dl_producer(nw, spread, wtm, wtn) ? DL_NPW : 0));
 }
 
+// LDS ring bytes of a BM x BN tile with ns stages (0: dl_stages); the
+// epilogue reuses them
+constexpr int dl_lds_bytes(int bm, int bn, int ns = 0) {
+    return (ns > 0 ? ns : dl_stages(bm, bn)) * 128 * (bm + bn);
+}
+
+// One workgroup's tile: workgroup `blk` of `nblk`, LDS ring `lds_raw`
+// (dl_lds_bytes(BM, BN, NSV)) and bias row `lds_bias` ([BN]) owned by the
+// caller, threadIdx.x below dl_threads(...).  NSV: ring stages (0: as many as
+// fit, dl_stages); fewer leave room for a second workgroup on the CU.
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
-          bool SPREAD>
-__global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) void mfma_dl_kernel(
-    MfmaArgs p) {
+          bool SPREAD, int NSV = 0>
+__device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float *lds_bias,
+                                        int64_t blk, int64_t nblk) {
     constexpr int NW = WGM * WGN;
     constexpr bool PROD = dl_producer(NW, SPREAD, BM / WGM, BN / WGN);
     constexpr int NTH = dl_threads(NW, SPREAD, BM / WGM, BN / WGN);
@@ -298,7 +308,7 @@ __global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) 
     constexpr int FM = WTM / 32, FN = WTN / 32;
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
     constexpr int SA = 128 * BM, SB = 128 * BN;  // bytes of one stage of A / B
-    constexpr int NS = dl_stages(BM, BN);
+    constexpr int NS = NSV > 0 ? NSV : dl_stages(BM, BN);
     static_assert(NS >= 2 && NS <= 8, "two to eight stages");
     using TY = DlType<DT>;
     constexpr int KPS = TY::KPS, STEPS = TY::STEPS;
@@ -308,15 +318,11 @@ __global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) 
     static_assert((EPI != EPI_ROUND && EPI != EPI_SCALE) || BN <= 64 * NW,
                   "one thread per bias column");
 
-    // NS stages of [A | B]; reused by the epilogue
-    __shared__ __align__(1024) char lds_raw[NS * (SA + SB)];
-    __shared__ __align__(16) float lds_bias[BN];
-
     const int t = threadIdx.x;
     const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
-    const TileInfo ti = decode_tile<MODE, BM, BN, NTH>(p, t);
+    const TileInfo ti = decode_tile_at<MODE, BM, BN, NTH>(p, t, blk, nblk);
     const bool is_prod = PROD && wave >= NW;
     // index of this wave among the copying waves
     const int cwave = PROD ? (is_prod ? wave - NW : 0) : wave;
@@ -513,8 +519,19 @@ __global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) 
         }
     }
 
-    write_tile<DT, EPI, WTM, WTN, FM, FN, BN>(p, ti, acc, reinterpret_cast<char *>(lds_raw),
-                                              lds_bias, bias_v, wave, wm, wn, lane);
+    write_tile<DT, EPI, WTM, WTN, FM, FN, BN>(p, ti, acc, lds_raw, lds_bias, bias_v, wave, wm, wn,
+                                              lane);
+}
+
+template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
+          bool SPREAD>
+__global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) void mfma_dl_kernel(
+    MfmaArgs p) {
+    // NS stages of [A | B]; reused by the epilogue
+    __shared__ __align__(1024) char lds_raw[dl_lds_bytes(BM, BN)];
+    __shared__ __align__(16) float lds_bias[BN];
+    dl_body<DT, A_RC, B_RC, BM, BN, WGM, WGN, EPI, MODE, SPREAD>(p, lds_raw, lds_bias, blockIdx.x,
+                                                                 gridDim.x);
 }
 
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID, bool SPREAD>

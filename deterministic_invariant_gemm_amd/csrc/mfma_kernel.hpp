@@ -306,13 +306,16 @@ struct TileInfo {
     bool skip;
 };
 
+// Workgroup `blk` of `nblk` (blockIdx.x and gridDim.x for a launch of its own;
+// an offset index where one launch carries the tiles of two products).
 template <int MODE, int BM, int BN, int NTH = NT>
-__device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
+__device__ __forceinline__ TileInfo decode_tile_at(const MfmaArgs &p, int t, int64_t blk,
+                                                   int64_t nblk) {
     TileInfo ti{};
     ti.skip = false;
     if constexpr (MODE == MODE_PLAIN) {
         const int64_t tiles = p.tiles_i * p.tiles_j;
-        const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
+        const int64_t bid = xcd_remap(blk, nblk);
         ti.chunk = bid / tiles;
         const int64_t tile = bid % tiles;
         // groups of 4 row-tiles, column-major inside a group
@@ -327,8 +330,8 @@ __device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
         ti.r_begin = ti.chunk * p.chunk;
         ti.r_end = ti.r_begin + p.chunk < p.red ? ti.r_begin + p.chunk : p.red;
     } else if constexpr (MODE == MODE_SEGMENTS) {
-        const int64_t tt0 = blockIdx.x / p.tiles_j;
-        ti.col0 = (blockIdx.x % p.tiles_j) * BN;
+        const int64_t tt0 = blk / p.tiles_j;
+        ti.col0 = (blk % p.tiles_j) * BN;
         int64_t tt = tt0;
         int64_t x = 0;
         ti.row0 = -1;
@@ -366,8 +369,8 @@ __device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
         ti.r_end = p.red;
     } else {  // MODE_EXPERT_RED
         const int64_t per_x = p.tiles_i * p.tiles_j;
-        const int64_t x = blockIdx.x / per_x;
-        const int64_t tile = blockIdx.x % per_x;
+        const int64_t x = blk / per_x;
+        const int64_t tile = blk % per_x;
         ti.row0 = (tile / p.tiles_j) * BM;
         ti.col0 = (tile % p.tiles_j) * BN;
         ti.row_end = p.rows;
@@ -378,6 +381,11 @@ __device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
         ti.c_off = x * p.c_expert_stride;
     }
     return ti;
+}
+
+template <int MODE, int BM, int BN, int NTH = NT>
+__device__ __forceinline__ TileInfo decode_tile(const MfmaArgs &p, int t) {
+    return decode_tile_at<MODE, BM, BN, NTH>(p, t, blockIdx.x, gridDim.x);
 }
 
 // The bias of this tile's columns as f32: thread t < BN fetches column t

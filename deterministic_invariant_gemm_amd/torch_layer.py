@@ -5,9 +5,10 @@ The weight is stored ``[in, out]`` (sgemm-bi PyPI page, "Use": the layer keeps
 its weight in the GEMM-natural ``[in, out]`` layout, and ``from_torch`` turns an
 ``nn.Linear`` into one), so ``y = x @ weight + bias`` maps directly onto
 ``bi_forward``.  Backward follows ViperLLM ffma.py, _FFMAAddmm.backward: the
-input gradient ``gy @ weight^T`` (``bi_backward_dx``), the weight gradient
-``x^T @ gy`` returned in the weight dtype (``bi_backward_dw``) and the bias
-gradient as an f32 column sum cast back once (``bi_bias_grad``).
+input gradient ``gy @ weight^T`` and the weight gradient ``x^T @ gy`` returned
+in the weight dtype (both from ``bi_linear_backward``, or ``bi_backward_dx`` /
+``bi_backward_dw`` when only one is needed; same bits) and the bias gradient
+as an f32 column sum cast back once (``bi_bias_grad``).
 
 Torch supplies device memory, the current stream and autograd bookkeeping only.
 Tensors must be CUDA (HIP) tensors of one dtype (float32, bfloat16 or float16);
@@ -20,7 +21,8 @@ import math
 import torch
 
 from . import (BI_BF16, BI_F16, BI_F32, bi_backward_dw, bi_backward_dw_workspace_bytes,
-               bi_backward_dx, bi_bias_grad, bi_bias_grad_workspace_bytes, bi_forward, check)
+               bi_backward_dx, bi_bias_grad, bi_bias_grad_workspace_bytes, bi_forward,
+               bi_linear_backward, check)
 
 _DTYPES = {torch.float32: BI_F32, torch.bfloat16: BI_BF16, torch.float16: BI_F16}
 
@@ -89,14 +91,23 @@ class _LinearFunction(torch.autograd.Function):
             stream = torch.cuda.current_stream()
             if ctx.needs_input_grad[0]:
                 dx = torch.empty((m, k), dtype=w.dtype, device=w.device)
-                check(bi_backward_dx(dx, gy2, w, m, k, n, dt, stream, ctx.tc), "bi_backward_dx")
-                dx = dx.reshape(*ctx.lead, k)
             if ctx.needs_input_grad[1]:
                 dw = torch.empty((k, n), dtype=w.dtype, device=w.device)
+            if dx is not None and dw is not None:
+                # both from one call: the library may run their tiles in one launch
+                nb = bi_backward_dw_workspace_bytes(m, k, n, dt, ctx.tc)
+                ws = _workspace(nb, w.device)
+                check(bi_linear_backward(dx, dw, gy2, x2, w, m, k, n, dt, ws, nb, stream, ctx.tc),
+                      "bi_linear_backward")
+            elif dx is not None:
+                check(bi_backward_dx(dx, gy2, w, m, k, n, dt, stream, ctx.tc), "bi_backward_dx")
+            elif dw is not None:
                 nb = bi_backward_dw_workspace_bytes(m, k, n, dt, ctx.tc)
                 ws = _workspace(nb, w.device)
                 check(bi_backward_dw(dw, x2, gy2, m, k, n, dt, ws, nb, stream, ctx.tc),
                       "bi_backward_dw")
+            if dx is not None:
+                dx = dx.reshape(*ctx.lead, k)
             if ctx.has_bias and ctx.needs_input_grad[2]:
                 db = torch.empty((n,), dtype=w.dtype, device=w.device)
                 nb = bi_bias_grad_workspace_bytes(m, n, dt)

@@ -6,6 +6,7 @@
  *   bi_forward              Y  = RNE_T(X W + b)
  *   bi_backward_dx          dX = RNE_T(dY W^T)
  *   bi_backward_dw          dW = RNE_T(X^T dY)           (fixed-order two-pass)
+ *   bi_linear_backward      dX and dW together (same bits as the two calls)
  *   bi_bias_grad            db = RNE_T(sum over rows of dY) (fixed order)
  *   bi_fp8_mm               Y  = RNE_bf16((A B^T) dA dB) (fp8 e4m3fn inputs)
  *   bi_fp8_quantize         q  = FP8(bf16 * scale_inv), amax (e4m3fn / e5m2)
@@ -138,6 +139,20 @@ size_t bi_backward_dw_workspace_bytes(int64_t m, int64_t k, int64_t n, int dtype
 int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k, int64_t n,
                    int dtype, void *workspace, size_t workspace_bytes, hipStream_t stream,
                    int tc);
+
+/* Both gradients of a linear layer from one dY (ffma.py, _FFMAAddmm.backward:
+ * gx = gy W^T and gW = x^T gy from the same gy).  Each output has exactly the
+ * bits of bi_backward_dx / bi_backward_dw with the same arguments; where both
+ * run the direct-load MFMA kernel (bf16 / f16, aligned rows, dW in one chunk)
+ * their tiles share one launch, so a CU that finishes a dX tile starts a dW
+ * tile while others are still busy; otherwise the two calls run in sequence.
+ * dx or dw may be NULL to skip that gradient (not both: BI_ERR_NULL); the
+ * other arguments, shapes, workspace and errors are those of the two calls,
+ * all checked before anything is enqueued (workspace: see
+ * bi_backward_dw_workspace_bytes). */
+int bi_linear_backward(void *dx, void *dw, const void *dy, const void *x, const void *w,
+                       int64_t m, int64_t k, int64_t n, int dtype, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream, int tc);
 
 /* Workspace bytes bi_bias_grad needs (0 when m <= 256).  Returns 0 for invalid
  * arguments as well. */

@@ -168,3 +168,26 @@ def test_bias_grad_validation(lib):
     assert dig.bi_bias_grad(F, None, m, n, dig.BI_BF16, F, need) == -1
     assert dig.bi_bias_grad(F, F, 1 << 30, 1 << 20, dig.BI_BF16, F, need) == -4
     assert dig.bi_bias_grad(None, None, 5, 0, dig.BI_BF16, None, 0) == 0  # n == 0: no-op
+
+
+def test_linear_backward_validation(lib):
+    """bi_linear_backward checks every argument of both gradients before
+    anything is enqueued."""
+    bf = dig.BI_BF16
+    assert dig.bi_linear_backward(None, None, F, F, F, 4, 8, 8, bf, None, 0) == -1
+    assert dig.bi_linear_backward(F, F, F, F, F, 4, 8, 8, 9, None, 0) == -2
+    assert dig.bi_linear_backward(F, F, F, F, F, 4, -8, 8, bf, None, 0) == -3
+    assert dig.bi_linear_backward(F, F, None, F, F, 4, 128, 128, bf, None, 0) == -1
+    assert dig.bi_linear_backward(F, F, F, None, F, 4, 128, 128, bf, None, 0) == -1
+    assert dig.bi_linear_backward(F, F, F, F, F, 1 << 30, 1 << 20, 4, bf, None, 0) == -4
+    # dW chunked (few output tiles): the workspace is checked before dX runs
+    m, k, n = 4096, 768, 48
+    need = dig.bi_backward_dw_workspace_bytes(m, k, n, bf, 1)
+    assert need > 0
+    assert dig.bi_linear_backward(F, F, F, F, F, m, k, n, bf, None, 0) == -5
+    assert dig.bi_linear_backward(F, F, F, F, F, m, k, n, bf, F, need - 1) == -5
+    # tc = 2 where dX (output dim k = 48) would fall back to the scalar tier
+    assert dig.bi_plan(dig.OP_DX, bf, 1, 48, 768)[0] == 0
+    assert dig.bi_linear_backward(F, F, F, F, F, 64, 48, 768, bf, None, 0, tc=2) == -7
+    # nothing to compute
+    assert dig.bi_linear_backward(F, F, None, None, None, 0, 0, 16, bf, None, 0) == 0
