@@ -127,10 +127,13 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
 
 // Tile for the batch at hand (forward, dX, fp8): the default tile of (k, n)
 // while it gives at least 192 workgroups (three quarters of the CUs), else
-// 128x128 (eight waves) if that does, else the narrow 64x32 tile, which gives
-// the most column tiles to spread the stream of B over.  The tile may follow
-// m because every tile issues the same MFMA sequence per element (the bits do
-// not change); the tier never follows m.  Forced tiles are kept.
+// 128x128 (eight waves) if that does; else the narrow 64x32 tile while one
+// round of it (at most 256 workgroups) covers the batch -- it spreads the
+// stream of B over the most workgroups when M is small -- and beyond that the
+// wider of the two tiles that gives more workgroups (narrow tiles over several
+// rounds re-read B and run 1.5-3x slower).  The tile may follow m because every
+// tile issues the same MFMA sequence per element (the bits do not change); the
+// tier never follows m.  Forced tiles are kept.
 int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols) {
     if (pl.tile < 40 || tc >= kForceBase) return pl.tile;
     auto wgs = [&](int id) {
@@ -139,7 +142,8 @@ int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols) {
     };
     if (wgs(pl.tile) >= 192) return pl.tile;
     if (wgs(115) >= 192) return 115;
-    return 120;
+    if (wgs(120) <= 256) return 120;
+    return wgs(pl.tile) >= wgs(115) ? pl.tile : 115;
 }
 
 int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.chunk); }
@@ -173,16 +177,16 @@ int direct_tile(MfmaArgs &a, int tile, int64_t a_bytes, int64_t b_bytes) {
     return t;
 }
 
-// MFMA-tier arguments of dX = dY W^T ([m,k] from dy [m,n], w [k,n]) and the
-// tile that runs.
+// MFMA-tier arguments of dX = dY W^T ([m,k] from dy [m,n], w [k,n]) on tile
+// `tile` (before the alignment check) and the tile that runs.
 int dx_mfma_args(MfmaArgs &a, void *dx, const void *dy, const void *w, int64_t m, int64_t k,
-                 int64_t n, const Plan &pl, int tc) {
+                 int64_t n, int tile) {
     a.a = dy; a.lda = n; a.b = w; a.ldb = n; a.c = dx; a.ldc = k;
     a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
     a.vec_a = aligned16(dy) && n % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(dx) && k % 4 == 0;
-    return direct_tile(a, batch_tile(pl, tc, m, k), 2 * m * n, 2 * k * n);
+    return direct_tile(a, tile, 2 * m * n, 2 * k * n);
 }
 
 // MFMA-tier arguments of dW = X^T dY ([k,n] from x [m,k], dy [m,n]; f32 chunk
@@ -276,7 +280,7 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
         return hip_status(launch_scalar_gemm(a, dtype, dtype, 0, stream));
     }
     MfmaArgs a{};
-    const int tile = dx_mfma_args(a, dx, dy, w, m, k, n, pl, tc);
+    const int tile = dx_mfma_args(a, dx, dy, w, m, k, n, batch_tile(pl, tc, m, k));
     return hip_status(launch_mfma_gemm(a, tile, dtype, /*both rc*/ 3, 0, stream));
 }
 
@@ -347,9 +351,13 @@ int bi_linear_backward(void *dx, void *dw, const void *dy, const void *x, const 
         return BI_ERR_WORKSPACE;
     if (m > 0 && k > 0 && n > 0 && px.tile != 0 && pw.tile != 0 && chunks == 1) {
         MfmaArgs ax{}, aw{};
-        const int tx = dx_mfma_args(ax, dx, dy, w, m, k, n, px, tc);
+        const int tx = dx_mfma_args(ax, dx, dy, w, m, k, n, batch_tile(px, tc, m, k));
         const int tw = dw_mfma_args(aw, dw, x, dy, m, k, n, pw, 1, nullptr);
-        if (mfma_backward_pair(tx, tw, dtype)) return hip_status(launch_mfma_backward(ax, tx, aw, tw, dtype, stream));
+        // one launch pays off while the dX tiles alone fill most CUs; with fewer,
+        // the dX tiles (on the critical path, with the shorter ring of the
+        // shared launch) are faster in a launch of their own
+        if (mfma_backward_pair(tx, tw, dtype) && ax.tiles_i * ax.tiles_j >= 192)
+            return hip_status(launch_mfma_backward(ax, tx, aw, tw, dtype, stream));
     }
     const int st = bi_backward_dx(dx, dy, w, m, k, n, dtype, stream, tc);
     if (st != BI_OK) return st;

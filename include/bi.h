@@ -143,8 +143,9 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
 /* Both gradients of a linear layer from one dY (ffma.py, _FFMAAddmm.backward:
  * gx = gy W^T and gW = x^T gy from the same gy).  Each output has exactly the
  * bits of bi_backward_dx / bi_backward_dw with the same arguments; where both
- * run the direct-load MFMA kernel (bf16 / f16, aligned rows, dW in one chunk)
- * their tiles share one launch, so a CU that finishes a dX tile starts a dW
+ * run the direct-load MFMA kernel on the 128x96 dX and 96x96 dW tiles (bf16 /
+ * f16, aligned rows, dW in one chunk, at least 192 dX tiles) their tiles share
+ * one launch, so a CU that finishes a dX tile starts a dW
  * tile while others are still busy; otherwise the two calls run in sequence.
  * dx or dw may be NULL to skip that gradient (not both: BI_ERR_NULL); the
  * other arguments, shapes, workspace and errors are those of the two calls,

@@ -1,8 +1,8 @@
 """bi_linear_backward: dX and dW of one linear layer from one call.
 
 Where both gradients run the direct-load MFMA kernel on the 128x96 dX and
-96x96 dW tiles, their tiles share one launch; elsewhere the call runs the two
-products in sequence.  Either way each output must carry exactly the bits of
+96x96 dW tiles (at least 192 dX tiles), their tiles share one launch;
+elsewhere the call runs the two products in sequence.  Either way each output must carry exactly the bits of
 bi_backward_dx / bi_backward_dw on the same arguments, and pass the oracle
 parity rule (sampled rows of dX, sampled K-rows of dW; small-integer operands
 bit-exact against the oracle)."""
@@ -21,8 +21,10 @@ ST = {synth.F32: np.uint32, synth.BF16: np.uint16, synth.F16: np.uint16}
 
 # shared launch: config 2, ragged M (24 x 8 dX tiles), ragged N with K = 7 x 96
 SHARED = [(4096, 768, 3072), (3001, 768, 3072), (4096, 672, 2000)]
-# two launches: small-M dX tile, small shapes, chunked scalar dW, wide K
-SEQUENCE = [(1000, 768, 3072), (300, 200, 260), (4096, 768, 48), (1024, 2048, 512)]
+# two launches: fewer than 192 dX tiles (M = 1000, 2048; and the narrow dX tile
+# at M = 512), small shapes, chunked scalar dW, wide K
+SEQUENCE = [(1000, 768, 3072), (2048, 768, 3072), (512, 768, 3072), (300, 200, 260),
+            (4096, 768, 48), (1024, 2048, 512)]
 
 
 def separate(d, tc=1):
