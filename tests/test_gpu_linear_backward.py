@@ -116,3 +116,38 @@ def test_f32_and_scalar_tier():
         dx0, dw0 = separate(d, tc)
         dx1, dw1 = combined(d, tc)
         assert torch.equal(dx0, dx1) and torch.equal(dw0, dw1), (dt, tc)
+
+
+@pytest.mark.parametrize("mkn", [(4096, 768, 3072), (4096, 768, 48)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_graph_replay_of_the_step(mkn):
+    """bi_forward + bi_linear_backward captured in a HIP graph (the shared
+    launch at config 2; two launches and the chunked dW workspace at N = 48)
+    give the eager bytes on every replay, with the outputs overwritten by
+    eager work between replays."""
+    m, k, n = mkn
+    dt = synth.BF16
+    d = synth.linear(m, k, n, dt, seed=41, sigma_w=0.05)
+    x, w, b, dy = dev(d["x"]), dev(d["w"]), dev(d["b"]), dev(d["dy"])
+    y = empty((m, n), np.uint16)
+    dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, torch.cuda.current_stream(), 1))
+    dx0, dw0 = combined(d)
+    ref = (digest(y), digest(dx0), digest(dw0))
+    dx, dw = empty((m, k), np.uint16), empty((k, n), np.uint16)
+    nb = dig.bi_backward_dw_workspace_bytes(m, k, n, dt, 1)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, cs, 1))
+        dig.check(dig.bi_linear_backward(dx, dw, dy, x, w, m, k, n, dt, ws if nb else None, nb,
+                                         cs, 1))
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in (y, dx, dw, ws):
+            t.fill_(rep + 3)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert (digest(y), digest(dx), digest(dw)) == ref, rep
