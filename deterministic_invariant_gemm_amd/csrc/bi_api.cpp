@@ -333,7 +333,13 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
 int bi_linear_backward(void *dx, void *dw, const void *dy, const void *x, const void *w,
                        int64_t m, int64_t k, int64_t n, int dtype, void *workspace,
                        size_t workspace_bytes, hipStream_t stream, int tc) {
-    if (!dx && !dw) return BI_ERR_NULL;
+    if (!dx && !dw) {
+        // nothing requested: valid only when both outputs, dx [m,k] and dw
+        // [k,n], are empty (callers may pass NULL for an empty tensor)
+        if (!dtype_ok(dtype)) return BI_ERR_DTYPE;
+        if (m < 0 || k < 0 || n < 0) return BI_ERR_SHAPE;
+        return (k == 0 || (m == 0 && n == 0)) ? BI_OK : BI_ERR_NULL;
+    }
     if (!dw) return bi_backward_dx(dx, dy, w, m, k, n, dtype, stream, tc);
     if (!dx) return bi_backward_dw(dw, x, dy, m, k, n, dtype, workspace, workspace_bytes, stream, tc);
     // every check of the two calls, before anything is enqueued

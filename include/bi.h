@@ -147,10 +147,10 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
  * f16, aligned rows, dW in one chunk, at least 192 dX tiles) their tiles share
  * one launch, so a CU that finishes a dX tile starts a dW
  * tile while others are still busy; otherwise the two calls run in sequence.
- * dx or dw may be NULL to skip that gradient (not both: BI_ERR_NULL); the
- * other arguments, shapes, workspace and errors are those of the two calls,
- * all checked before anything is enqueued (workspace: see
- * bi_backward_dw_workspace_bytes). */
+ * dx or dw may be NULL to skip that gradient (not both, unless both outputs
+ * are empty: BI_ERR_NULL); the other arguments, shapes, workspace and errors
+ * are those of the two calls, all checked before anything is enqueued
+ * (workspace: see bi_backward_dw_workspace_bytes). */
 int bi_linear_backward(void *dx, void *dw, const void *dy, const void *x, const void *w,
                        int64_t m, int64_t k, int64_t n, int dtype, void *workspace,
                        size_t workspace_bytes, hipStream_t stream, int tc);

@@ -189,5 +189,8 @@ def test_linear_backward_validation(lib):
     # tc = 2 where dX (output dim k = 48) would fall back to the scalar tier
     assert dig.bi_plan(dig.OP_DX, bf, 1, 48, 768)[0] == 0
     assert dig.bi_linear_backward(F, F, F, F, F, 64, 48, 768, bf, None, 0, tc=2) == -7
-    # nothing to compute
+    # nothing to compute; NULL outputs are fine when both are empty
     assert dig.bi_linear_backward(F, F, None, None, None, 0, 0, 16, bf, None, 0) == 0
+    assert dig.bi_linear_backward(None, None, None, None, None, 64, 0, 128, bf, None, 0) == 0
+    assert dig.bi_linear_backward(None, None, None, None, None, 0, 96, 0, bf, None, 0) == 0
+    assert dig.bi_linear_backward(None, None, F, F, F, 0, 96, 128, bf, None, 0) == -1

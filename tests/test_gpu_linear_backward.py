@@ -151,3 +151,30 @@ def test_graph_replay_of_the_step(mkn):
         g.replay()
         torch.cuda.synchronize()
         assert (digest(y), digest(dx), digest(dw)) == ref, rep
+
+
+@pytest.mark.parametrize("mkn", [(0, 96, 128), (64, 96, 0), (64, 0, 128), (1, 768, 3072)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_empty_and_degenerate_dims(mkn):
+    """Empty reductions and empty outputs give the bytes of the two calls on
+    poisoned buffers: m = 0 writes dW = +0, n = 0 writes dX = +0, k = 0 has
+    no outputs; m = 1 runs the narrow dX tile and two launches."""
+    m, k, n = mkn
+    dt = synth.BF16
+    d = synth.linear(max(m, 1), max(k, 1), max(n, 1), dt, seed=9, sigma_w=0.05)
+    x, w, dy = dev(d["x"]), dev(d["w"]), dev(d["dy"])
+    s = torch.cuda.current_stream()
+    outs = []
+    for call in ("separate", "combined"):
+        dx, dw = empty((m, k), np.uint16), empty((k, n), np.uint16)
+        if call == "separate":
+            dig.check(dig.bi_backward_dx(dx, dy, w, m, k, n, dt, s, 1))
+            dig.check(dig.bi_backward_dw(dw, x, dy, m, k, n, dt, None, 0, s, 1))
+        else:
+            dig.check(dig.bi_linear_backward(dx, dw, dy, x, w, m, k, n, dt, None, 0, s, 1))
+        outs.append((host(dx, np.uint16), host(dw, np.uint16)))
+    assert all(np.array_equal(a, b) for a, b in zip(*outs))
+    if m == 0:
+        assert not outs[1][1].any()
+    if n == 0:
+        assert not outs[1][0].any()
