@@ -242,7 +242,7 @@ def cpu_baseline_linear(d, target_s):
 
 def bench_linear(args, torch, dig, synth):
     dt = synth.BF16 if args.dtype == "bf16" else synth.F16
-    d = synth.config2(dt)
+    d = synth.mlp_up_linear(dt)
     m, k, n = d["m"], d["k"], d["n"]
     dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
     x, w, b, dy = dev(d["x"]), dev(d["w"]), dev(d["b"]), dev(d["dy"])
@@ -309,7 +309,7 @@ def bench_linear(args, torch, dig, synth):
 
 
 def bench_fp8(args, torch, dig, synth):
-    d = synth.config4()
+    d = synth.fp8_8192x4096x4096()
     m, k, n = d["m"], d["k"], d["n"]
     a = torch.from_numpy(d["a8"]).cuda()
     bt = torch.from_numpy(d["bt8"]).cuda()
@@ -398,7 +398,7 @@ def bench_fp8_linear(args, torch, dig, synth):
 
 
 def bench_grouped(args, torch, dig, synth):
-    d = synth.config5()
+    d = synth.grouped_16384x2048x1408_e8()
     m, k, n, e = d["m"], d["k"], d["n"], d["e"]
     dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
     inp, w, dy = dev(d["input"]), dev(d["weights"]), dev(d["dy"])
@@ -432,7 +432,7 @@ def bench_grouped(args, torch, dig, synth):
 
 
 def bench_sweep(args, torch, dig, synth):
-    d = synth.config3()
+    d = synth.square_4096_sweep()
     m, k, n = d["m"], d["k"], d["n"]
     dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
     x, w = dev(d["x"]), dev(d["w"])
@@ -511,7 +511,7 @@ def bench_tiles(args, torch, dig, synth):
     (forced with tc = 16 + id; every tile gives the same bits).  Used with
     rocprofv3 counters to compare MFMA busy time, LDS bank conflicts and HBM
     traffic between tiles."""
-    d = synth.config2(synth.BF16)
+    d = synth.mlp_up_linear(synth.BF16)
     m, k, n, dt = d["m"], d["k"], d["n"], synth.BF16
     dev = lambda a: torch.from_numpy(a.view(np.int16).copy()).cuda()
     x, w, b, dy = dev(d["x"]), dev(d["w"]), dev(d["b"]), dev(d["dy"])

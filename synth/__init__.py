@@ -120,12 +120,12 @@ def linear_integer(m, k, n, dt, seed, lo=-4, hi=4, bias=True):
     }
 
 
-def config1():
+def f32_linear_64x128x256():
     """f32 X[64,128], W[128,256], b[256], dY[64,256], all N(0,1)."""
     return linear(64, 128, 256, F32, seed=1)
 
 
-def config2(dt=BF16, n=3072, seed=2):
+def mlp_up_linear(dt=BF16, n=3072, seed=2):
     """Transformer MLP-up linear 768 -> 3072 at M=4096: X, dY ~ N(0,1);
     W, b ~ N(0,0.02).  dt=F16 gives the f16 rerun from the same f32 draws;
     n=48, seed=22 gives the narrow-output case."""
@@ -133,7 +133,7 @@ def config2(dt=BF16, n=3072, seed=2):
                   sigma_dy=1.0)
 
 
-def config3():
+def square_4096_sweep():
     """Batch-invariance sweep: W[4096,4096] ~ N(0,0.02), X[8192,4096] and
     dY[8192,4096] ~ N(0,1), no bias."""
     return linear(8192, 4096, 4096, BF16, seed=3, sigma_w=0.02, bias=False)
@@ -184,7 +184,7 @@ def fp8_linear(m, k, n, seed, sigma_w=0.02, bias=True):
     return out
 
 
-def config4():
+def fp8_8192x4096x4096():
     """fp8 e4m3: A[8192,4096], B^T[4096,4096] from N(0,1) bf16."""
     return fp8(8192, 4096, 4096, seed=4)
 
@@ -229,7 +229,7 @@ def grouped(m, k, n, e, dt, seed, pad_rows=0, empty=(), sigma_w=0.02):
     }
 
 
-def config5(empty=()):
+def grouped_16384x2048x1408_e8(empty=()):
     """input[16384,2048] ~ N(0,1), weights[8,1408,2048] ~ N(0,0.02), 5 % of
     rows (819) padding, dY[16384,1408] ~ N(0,1)."""
     return grouped(16384, 2048, 1408, 8, BF16, seed=5, pad_rows=round(0.05 * 16384),

@@ -62,20 +62,20 @@ def test_fp8_exact_integer_bits(tc, shape):
     assert np.array_equal(host(Fp8(d).run(tc), np.uint16), r.out)
 
 
-def test_config4_fp8():
+def test_fp8_8192x4096x4096():
     """A[8192,4096], B^T[4096,4096] quantised from N(0,1) bf16 with scale
     448/amax: sampled parity at M = 8192, full parity at M = 16 (the first 16
     rows), 10-run hashes and batch invariance between the two."""
-    d = synth.config4()
+    d = synth.fp8_8192x4096x4096()
     F = Fp8(d)
     m, k, n = F.m, F.k, F.n
     y = host(F.run(1), np.uint16)
     rows = sample_rows(m, 16, 6)
     r = oracle.fp8_mm(d["a8"], d["bt8"], d["da"], d["db"], m, k, n, rows=rows)
-    print("config4 M=8192:", check(y[rows], r, synth.BF16, "config4 M=8192"))
+    print("fp8_8192x4096x4096 M=8192:", check(y[rows], r, synth.BF16, "fp8_8192x4096x4096 M=8192"))
     y16 = host(F.run(1, m=16), np.uint16)
     r16 = oracle.fp8_mm(d["a8"], d["bt8"], d["da"], d["db"], m, k, n, rows=np.arange(16))
-    print("config4 M=16:", check(y16, r16, synth.BF16, "config4 M=16"))
+    print("fp8_8192x4096x4096 M=16:", check(y16, r16, synth.BF16, "fp8_8192x4096x4096 M=16"))
     assert np.array_equal(y16, y[:16])
     assert len({digest(F.run(1)) for _ in range(10)}) == 1
     assert len({digest(F.run(1, m=16)) for _ in range(10)}) == 1

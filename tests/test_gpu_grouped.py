@@ -94,23 +94,23 @@ def test_grouped_exact_integer_bits(tc):
                           oracle.grouped_dweights(dt, d["input"], d["dy"], ids, m, k, n, e).out)
 
 
-def test_config5_grouped():
+def test_grouped_16384x2048x1408_e8():
     """input[16384,2048], weights[8,1408,2048], 819 padding rows: sampled parity
     of forward, dinput and dweights, padding rows +0 bytes, 10-run hashes;
     then the same with expert 5 emptied (its dweights must be zero)."""
-    d = synth.config5()
+    d = synth.grouped_16384x2048x1408_e8()
     G = Grouped(d)
     rows = sample_rows(G.m, 40, 7)
     rows = np.union1d(rows, np.nonzero(d["row_experts"] >= G.e)[0][:8])
     wrows = sample_rows(G.e * G.n, 16, 8)
-    parity(d, 1, "config5", rows=rows, wrows=wrows)
+    parity(d, 1, "grouped_16384x2048x1408_e8", rows=rows, wrows=wrows)
     assert len({digest(G.forward(1)) for _ in range(10)}) == 1
     hs = set()
     for _ in range(10):
         di, dw = G.backward(1)
         hs.add((digest(di), digest(dw)))
     assert len(hs) == 1
-    d2 = synth.config5(empty=(5,))
+    d2 = synth.grouped_16384x2048x1408_e8(empty=(5,))
     G2 = Grouped(d2)
     _, dw2 = G2.backward(1)
     dw2 = host(dw2, np.uint32).reshape(G2.e, G2.n, G2.k)
@@ -118,7 +118,7 @@ def test_config5_grouped():
     wr = np.array([5 * G2.n, 5 * G2.n + 7, 2 * G2.n + 3], dtype=np.int64)
     rw = oracle.grouped_dweights(d2["dt"], d2["input"], d2["dy"], d2["row_experts"], G2.m,
                                  G2.k, G2.n, G2.e, rows=wr)
-    check(dw2.reshape(G2.e * G2.n, G2.k)[wr], rw, synth.F32, "config5 empty-expert dweights")
+    check(dw2.reshape(G2.e * G2.n, G2.k)[wr], rw, synth.F32, "grouped_16384x2048x1408_e8 empty-expert dweights")
 
 
 def test_grouped_tiers_and_explicit_mfma_strategy():

@@ -97,11 +97,11 @@ def test_linear_exact_integer_bits(dt, tc, shape):
     assert np.array_equal(host(L.dw(tc), L.st), rw.out)
 
 
-def test_config1_f32():
+def test_f32_linear_64x128x256():
     """f32 X[64,128] W[128,256] + b, dY[64,256]: parity, 10-run hashes and batch
     invariance at M' in {1, 7, 64}."""
-    d = synth.config1()
-    full_parity(d, 1, "config1")
+    d = synth.f32_linear_64x128x256()
+    full_parity(d, 1, "f32_linear_64x128x256")
     L = Linear(d)
     for op in (lambda: L.forward(1), lambda: L.dx(1), lambda: L.dw(1)):
         assert len({digest(op()) for _ in range(10)}) == 1
@@ -111,26 +111,26 @@ def test_config1_f32():
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
-def test_config2_parity_sampled(dt):
+def test_mlp_up_parity_sampled(dt):
     """X[4096,768] W[768,3072] + b, dY[4096,3072] on the MFMA tier: sampled
     output rows against the oracle (rows for forward and dX, K-rows for dW)."""
-    d = synth.config2(dt)
+    d = synth.mlp_up_linear(dt)
     L = Linear(d)
     m, k, n = L.m, L.k, L.n
     rows = sample_rows(m, 48, 1)
     stats = []
     ry = oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n, rows=rows)
-    stats.append(check(host(L.forward(1), L.st)[rows], ry, dt, "config2 fwd"))
+    stats.append(check(host(L.forward(1), L.st)[rows], ry, dt, "mlp_up_linear fwd"))
     rx = oracle.linear_dx(dt, d["dy"], d["w"], m, k, n, rows=rows)
-    stats.append(check(host(L.dx(1), L.st)[rows], rx, dt, "config2 dX"))
+    stats.append(check(host(L.dx(1), L.st)[rows], rx, dt, "mlp_up_linear dX"))
     krows = sample_rows(k, 24, 2)
     rw = oracle.linear_dw(dt, d["x"], d["dy"], m, k, n, rows=krows)
-    stats.append(check(host(L.dw(1), L.st)[krows], rw, dt, "config2 dW"))
-    print("config2 (max ulp, #A-clause, max rel):", stats)
+    stats.append(check(host(L.dw(1), L.st)[krows], rw, dt, "mlp_up_linear dW"))
+    print("mlp_up_linear (max ulp, #A-clause, max rel):", stats)
 
 
-def test_config2_determinism_and_batch_invariance():
-    d = synth.config2(synth.BF16)
+def test_mlp_up_determinism_and_batch_invariance():
+    d = synth.mlp_up_linear(synth.BF16)
     L = Linear(d)
     for name, op in (("fwd", lambda: L.forward(1)), ("dX", lambda: L.dx(1)),
                      ("dW", lambda: L.dw(1))):
@@ -142,10 +142,10 @@ def test_config2_determinism_and_batch_invariance():
         assert np.array_equal(host(L.dx(1, m=mp), np.uint16), dx[:mp]), mp
 
 
-def test_config2_narrow_n48():
+def test_mlp_up_narrow_n48():
     """N = 48 < 64: forward and dW fall back to the scalar tier, dX (output dim
     K = 768) stays on MFMA; sampled parity and run-to-run hashes."""
-    d = synth.config2(synth.BF16, n=48, seed=22)
+    d = synth.mlp_up_linear(synth.BF16, n=48, seed=22)
     L = Linear(d)
     m, k, n, dt = L.m, L.k, L.n, L.dt
     assert dig.bi_plan(dig.OP_FWD, dt, 1, k, n)[0] == 0
@@ -202,23 +202,23 @@ def test_tile_families_give_identical_bits():
     assert len(tiles) >= 3, tiles
 
 
-def test_config3_batch_invariance_sweep():
+def test_square_4096_batch_invariance_sweep():
     """W[4096,4096], X[8192,4096]: every shared row is bit-identical across
     M in {1, 3, 17, 128, 1000, 8192}; dW at M = 8192 hashed 10 times; sampled
     oracle parity of the forward at M = 8192 and of dW."""
-    d = synth.config3()
+    d = synth.square_4096_sweep()
     L = Linear(d)
     y = host(L.forward(1), np.uint16)
     for mp in (1, 3, 17, 128, 1000, 8192):
         assert np.array_equal(host(L.forward(1, m=mp), np.uint16), y[:mp]), mp
     rows = sample_rows(L.m, 12, 4)
     ry = oracle.linear_forward(L.dt, d["x"], d["w"], None, L.m, L.k, L.n, rows=rows)
-    check(y[rows], ry, L.dt, "config3 fwd")
+    check(y[rows], ry, L.dt, "square_4096_sweep fwd")
     hashes = {digest(L.dw(1)) for _ in range(10)}
     assert len(hashes) == 1
     krows = sample_rows(L.k, 4, 5)
     rw = oracle.linear_dw(L.dt, d["x"], d["dy"], L.m, L.k, L.n, rows=krows)
-    check(host(L.dw(1), np.uint16)[krows], rw, L.dt, "config3 dW")
+    check(host(L.dw(1), np.uint16)[krows], rw, L.dt, "square_4096_sweep dW")
 
 
 @pytest.mark.parametrize("dt,emin,emax", [(synth.BF16, -60, 64), (synth.F16, -12, 8)],

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 ST = {synth.F32: np.uint32, synth.BF16: np.uint16, synth.F16: np.uint16}
 
-# shared launch: config 2, ragged M (24 x 8 dX tiles), ragged N with K = 7 x 96
+# shared launch: 4096x768x3072, ragged M (24 x 8 dX tiles), ragged N with K = 7 x 96
 SHARED = [(4096, 768, 3072), (3001, 768, 3072), (4096, 672, 2000)]
 # two launches: fewer than 192 dX tiles (M = 1000, 2048; and the narrow dX tile
 # at M = 512), small shapes, chunked scalar dW, wide K
@@ -99,7 +99,7 @@ def test_shared_launch_exact_integers():
 
 
 def test_one_gradient_and_determinism():
-    d = synth.config2(synth.BF16)
+    d = synth.mlp_up_linear(synth.BF16)
     dx0, dw0 = separate(d)
     only_dx, none = combined(d, want_dw=False)
     assert none is None and torch.equal(only_dx, dx0)
@@ -122,7 +122,7 @@ def test_f32_and_scalar_tier():
                          ids=lambda s: "x".join(map(str, s)))
 def test_graph_replay_of_the_step(mkn):
     """bi_forward + bi_linear_backward captured in a HIP graph (the shared
-    launch at config 2; two launches and the chunked dW workspace at N = 48)
+    launch at 4096x768x3072; two launches and the chunked dW workspace at N = 48)
     give the eager bytes on every replay, with the outputs overwritten by
     eager work between replays."""
     m, k, n = mkn
