@@ -62,16 +62,22 @@ hipError_t launch_mfma_backward(const MfmaArgs &px, int tile_x, const MfmaArgs &
                                 int dt, hipStream_t s) {
     if (!mfma_backward_pair(tile_x, tile_w, dt) || pw.nchunks != 1 || px.nchunks != 1)
         return hipErrorNotSupported;
-    const int64_t nbx = px.tiles_i * px.tiles_j, nbw = pw.tiles_i * pw.tiles_j;
+    // grids from the tiles this kernel runs
+    MfmaArgs ax = px, aw = pw;
+    ax.tiles_i = (ax.rows + mfma::TX::BM - 1) / mfma::TX::BM;
+    ax.tiles_j = (ax.cols + mfma::TX::BN - 1) / mfma::TX::BN;
+    aw.tiles_i = (aw.rows + mfma::TW::BM - 1) / mfma::TW::BM;
+    aw.tiles_j = (aw.cols + mfma::TW::BN - 1) / mfma::TW::BN;
+    const int64_t nbx = ax.tiles_i * ax.tiles_j, nbw = aw.tiles_i * aw.tiles_j;
     const int64_t offw = (nbx + 7) / 8 * 8;
     if (nbx <= 0 || nbw <= 0) return hipErrorNotSupported;
     if (offw + nbw > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (dt == DT_BF16)
         hipLaunchKernelGGL(mfma::mfma_dl_backward_kernel<DT_BF16>, dim3(offw + nbw),
-                           dim3(mfma::kTh), 0, s, px, pw, nbx, offw, nbw);
+                           dim3(mfma::kTh), 0, s, ax, aw, nbx, offw, nbw);
     else
         hipLaunchKernelGGL(mfma::mfma_dl_backward_kernel<DT_F16>, dim3(offw + nbw),
-                           dim3(mfma::kTh), 0, s, px, pw, nbx, offw, nbw);
+                           dim3(mfma::kTh), 0, s, ax, aw, nbx, offw, nbw);
     return hipGetLastError();
 }
 
