@@ -309,6 +309,9 @@ def bench_linear(args, torch, dig, synth):
 
 
 def bench_fp8(args, torch, dig, synth):
+    """fp8 e4m3 GEMM A[8192,4096] x B^T[4096,4096] and its first 16 rows, on the
+    exact default path (codes widened to bf16, bf16 matrix instruction) and on
+    the opt-in fast path (tc = 3, fp8 matrix instruction)."""
     d = synth.fp8_8192x4096x4096()
     m, k, n = d["m"], d["k"], d["n"]
     a = torch.from_numpy(d["a8"]).cuda()
@@ -317,25 +320,36 @@ def bench_fp8(args, torch, dig, synth):
     db = torch.tensor([float(d["db"])], dtype=torch.float32, device="cuda")
     y = torch.empty((m, n), dtype=torch.int16, device="cuda")
     y16 = torch.empty((16, n), dtype=torch.int16, device="cuda")
+    fast = dig.TC_FP8_FAST
     ops = [("fp8_m8192", lambda s: dig.check(dig.bi_fp8_mm(y, a, bt, da, db, m, k, n, s, 1))),
-           ("fp8_m16", lambda s: dig.check(dig.bi_fp8_mm(y16, a, bt, da, db, 16, k, n, s, 1)))]
+           ("fp8_m16", lambda s: dig.check(dig.bi_fp8_mm(y16, a, bt, da, db, 16, k, n, s, 1))),
+           ("fp8_fast_m8192",
+            lambda s: dig.check(dig.bi_fp8_mm(y, a, bt, da, db, m, k, n, s, fast))),
+           ("fp8_fast_m16",
+            lambda s: dig.check(dig.bi_fp8_mm(y16, a, bt, da, db, 16, k, n, s, fast)))]
     ms, per = timed_steps(torch, ops, args.steps, args.warmup)
     flop = 2.0 * m * k * n
-    ach = flop / (per["fp8_m8192"] * 1e-3) / 1e12
+    ach = {key: flop / (per[key] * 1e-3) / 1e12 for key in ("fp8_m8192", "fp8_fast_m8192")}
     b16 = 16 * k + n * k + 16 * n * 2
+    small = {key: {"us": round(per[key] * 1e3, 2),
+                   "GBps": round(b16 / (per[key] * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(b16 / (per[key] * 1e-3) / 1e9 / HBM_PEAK, 4)}
+             for key in ("fp8_m16", "fp8_fast_m16")}
     return {
-        "metric": "fp8 e4m3 GEMM TFLOP/s", "value": round(ach, 2), "unit": "TFLOP/s",
+        "metric": "fp8 e4m3 GEMM TFLOP/s", "value": round(ach["fp8_m8192"], 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
         "data": "synthetic",
         "config": {"workload": "fp8 e4m3 A[8192,4096] x B^T[4096,4096], per-tensor scales, "
-                               "bf16 out; plus M=16", "M": m, "K": k, "N": n},
-        "roofline": {"bound": "mfma", "kernel": "fp8_m8192", "achieved": round(ach, 2),
-                     "peak": FP8_PEAK, "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK, 4),
-                     "traffic": None},
-        "m16": {"us": round(per["fp8_m16"] * 1e3, 2),
-                "GBps": round(b16 / (per["fp8_m16"] * 1e-3) / 1e9, 1),
-                "frac_hbm": round(b16 / (per["fp8_m16"] * 1e-3) / 1e9 / HBM_PEAK, 4)},
+                               "bf16 out; plus M=16; exact path (value) and fast path",
+                   "M": m, "K": k, "N": n},
+        "roofline": {"bound": "mfma", "kernel": "fp8_m8192", "achieved": round(ach["fp8_m8192"], 2),
+                     "peak": FP8_PEAK, "unit": "TFLOP/s",
+                     "frac": round(ach["fp8_m8192"] / FP8_PEAK, 4), "traffic": None},
+        "fast": {"us": round(per["fp8_fast_m8192"] * 1e3, 2),
+                 "tflops": round(ach["fp8_fast_m8192"], 2),
+                 "frac_peak": round(ach["fp8_fast_m8192"] / FP8_PEAK, 4)},
+        "m16": small,
     }
 
 
@@ -527,7 +541,8 @@ def bench_tiles(args, torch, dig, synth):
     res = {}
     for op, ids in TILE_CANDIDATES.items():
         ops = [(f"{op}:{t}", lambda s, f=calls[op], t=t: f(s, 16 + t)) for t in ids]
-        _, per = timed_steps(torch, ops, args.steps, args.warmup)
+        with dig.testing_build():
+            _, per = timed_steps(torch, ops, args.steps, args.warmup)
         res[op] = {str(t): {"us": round(per[f"{op}:{t}"] * 1e3, 2),
                             "tflops": round(flop / (per[f"{op}:{t}"] * 1e-3) / 1e12, 1)}
                    for t in ids}

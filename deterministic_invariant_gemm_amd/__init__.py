@@ -15,16 +15,21 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbi.so")
+# the same kernels with the tile-forcing values of tc (tc = 16 + tile id, plus
+# 4096 for the fp8 fast path on that tile): tile-identity tests and tile tuning
+LIB_TESTING_PATH = os.path.join(HERE, "libbi_testing.so")
 
 BI_F32, BI_BF16, BI_F16 = 0, 1, 2
 BI_FP8_E4M3, BI_FP8_E5M2 = 3, 4
 BI_OK = 0
+TC_SCALAR, TC_AUTO, TC_MFMA, TC_FP8_FAST = 0, 1, 2, 3
 STATUS = {0: "BI_OK", -1: "BI_ERR_NULL", -2: "BI_ERR_DTYPE", -3: "BI_ERR_SHAPE",
           -4: "BI_ERR_TOO_LARGE", -5: "BI_ERR_WORKSPACE", -6: "BI_ERR_HIP",
           -7: "BI_ERR_UNSUPPORTED"}
 OP_FWD, OP_DX, OP_DW, OP_FP8, OP_GFWD, OP_GDIN, OP_GDW = range(7)
 
 _lib = None
+_lib_testing = None
 
 
 class BIError(RuntimeError):
@@ -36,12 +41,34 @@ class BIError(RuntimeError):
 def load() -> ctypes.CDLL:
     """Load libbi.so (built by ``build.build()``); raise if it is missing."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built: run deterministic_invariant_gemm_amd."
+    if _lib is None:
+        _lib = _bind(LIB_PATH)
+    return _lib
+
+
+class testing_build:
+    """Context manager: the entry points of this module call libbi_testing.so
+    (tile-forcing tc values accepted) instead of libbi.so while it is open."""
+
+    def __enter__(self):
+        global _lib, _lib_testing
+        if _lib_testing is None:
+            _lib_testing = _bind(LIB_TESTING_PATH)
+        self._saved = load()
+        _lib = _lib_testing
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self._saved
+        return False
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run deterministic_invariant_gemm_amd."
                            "build.build() (hipcc, gfx950) first")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.bi_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, i32]
     L.bi_backward_dx.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, i32]
@@ -73,7 +100,6 @@ def load() -> ctypes.CDLL:
     for f in ("bi_forward", "bi_backward_dx", "bi_backward_dw", "bi_fp8_mm", "bi_grouped_nt",
               "bi_grouped_nt_backward", "bi_plan"):
         getattr(L, f).restype = i32
-    _lib = L
     return L
 
 

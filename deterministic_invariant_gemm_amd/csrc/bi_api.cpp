@@ -53,8 +53,36 @@ bool mfma_eligible(int op, int dt, int tc, int64_t k, int64_t n) {
 // tc = 2 asks for the MFMA tier explicitly (rublas grouped_matmul_nt: an
 // explicit tensor-core strategy fails when that path is unavailable instead of
 // falling back); tc = 1 is the automatic choice, tc = 0 the scalar tier.
+// tc = 3 (fp8 GEMMs only) chooses the tier like tc = 1 and multiplies on the
+// MFMA tier with the fp8 matrix instruction instead of the exact widened path.
 constexpr int kTcRequired = 2;
+constexpr int kTcFp8Fast = 3;
+
+// Testing builds only (BI_TESTING, libbi_testing.so): tc = 16 + id forces MFMA
+// tile `id` when the op is on the MFMA tier (plus kFastBit: the fp8 fast path on
+// tile `id`), for the tile-identity tests and tile tuning.  Tiles do not change
+// results.  Production builds reject every other tc with BI_ERR_UNSUPPORTED.
+constexpr int kForceBase = 16;
+constexpr int kFastBit = 4096;
+#ifdef BI_TESTING
+constexpr bool kForceHook = true;
+#else
+constexpr bool kForceHook = false;
+#endif
+
+bool tc_known(int op, int tc) {
+    if (tc >= 0 && tc <= kTcRequired) return true;
+    if (tc == kTcFp8Fast) return op == OP_FP8;
+    if (kForceHook && (tc & ~kFastBit) >= kForceBase && (tc & ~kFastBit) < kFastBit)
+        return op == OP_FP8 || !(tc & kFastBit);
+    return false;
+}
+
+// fp8 GEMMs: the fp8 matrix instruction was asked for
+bool fp8_fast(int tc) { return tc == kTcFp8Fast || (kForceHook && tc >= kForceBase && (tc & kFastBit)); }
+
 int tier_check(int op, int dt, int tc, int64_t k, int64_t n) {
+    if (!tc_known(op, tc)) return BI_ERR_UNSUPPORTED;
     if (tc == kTcRequired && !mfma_eligible(op, dt, tc, k, n)) return BI_ERR_UNSUPPORTED;
     return BI_OK;
 }
@@ -66,12 +94,19 @@ int tier_check(int op, int dt, int tc, int64_t k, int64_t n) {
 // shape i and 100 + i the same with its copies spread between MFMAs (both used
 // when operands are aligned, see direct_tile; fp8 otherwise runs its
 // register-staged kernel on 256x256, 128x128 or 64x64).
-int pick_tile(int op, int64_t k, int64_t n) {
+int pick_tile(int op, int64_t k, int64_t n, bool fast) {
     const int64_t cols = (op == OP_DX || op == OP_GDIN) ? k : n;
     switch (op) {
     case OP_FP8:
-        // 256x256, eight waves, copies spread; 128x128 eight waves below
-        if (cols >= 2048) return 112;
+        if (fast) {
+            // 256x256, eight waves, copies spread; 128x128 eight waves below
+            if (cols >= 2048) return 112;
+            return cols >= 128 ? 115 : 46;
+        }
+        // exact path: 256x256 with four waves of 128x128 (one per SIMD, its
+        // accumulators in the AGPRs); the eight-wave 256x256 tile needs more
+        // registers than two waves per SIMD have once fragments are widened
+        if (cols >= 2048) return 41;
         return cols >= 128 ? 115 : 46;
     case OP_FWD:
         // 256x192, 8 waves, copies spread; 256x256, 8 waves
@@ -101,13 +136,9 @@ int pick_tile(int op, int64_t k, int64_t n) {
     return 44;
 }
 
-// tc >= 16 is a tuning / test hook: tc = 16 + id forces MFMA tile `id` (when the
-// op is on the MFMA tier).  Tiles do not change results.
-constexpr int kForceBase = 16;
-
 Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
     Plan pl{0, kNoSplit};
-    if (mfma_eligible(op, dt, tc, k, n)) pl.tile = pick_tile(op, k, n);
+    if (mfma_eligible(op, dt, tc, k, n)) pl.tile = pick_tile(op, k, n, op == OP_FP8 && fp8_fast(tc));
     if (op == OP_DW) {
         // the chunk length follows from the default tile of (k, n), so a
         // forced tile below never changes the reduction order
@@ -121,7 +152,10 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
             pl.chunk = tiles >= 128 ? kNoSplit : 256;
         }
     }
-    if (pl.tile && tc >= kForceBase && mfma_tile(tc - kForceBase)) pl.tile = tc - kForceBase;
+    if (kForceHook && pl.tile && tc >= kForceBase) {
+        const int id = (tc & ~kFastBit) - kForceBase;
+        if (mfma_tile(id)) pl.tile = id;
+    }
     return pl;
 }
 
@@ -135,7 +169,7 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
 // tile issues the same MFMA sequence per element (the bits do not change); the
 // tier never follows m.  Forced tiles are kept.
 int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols) {
-    if (pl.tile < 40 || tc >= kForceBase) return pl.tile;
+    if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
     auto wgs = [&](int id) {
         const TileShape *ts = mfma_tile(id);
         return cdiv(m, ts->bm) * cdiv(cols, ts->bn);
@@ -150,10 +184,9 @@ int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.ch
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
-// The tile that runs, its operand extents and its grid.  The direct-load (ids
-// 40 + base, 100 + base), direct-A (ids 60 + base) and ping-pong (ids 80 +
-// base) families need 16-byte-aligned rows whose length is a multiple of 8
-// elements and operands below 2^30 bytes; otherwise the register-staged kernel
+// The tile that runs, its operand extents and its grid.  The direct-load family
+// (ids 40 + base, 100 + base) needs 16-byte-aligned rows whose length is a
+// multiple of 8 elements and operands below 2^30 bytes; otherwise the register-staged kernel
 // runs on the tile every op instantiates that is closest in shape: 256x256,
 // 128x128 or 64x64 (same bits either way).  The grid (tiles_i or seg_tiles,
 // and tiles_j, over rows x cols) is set here from the shape that actually runs.
@@ -420,6 +453,7 @@ int fp8_gemm(void *y, const void *a, const void *bt, const float *a_dequant,
         return hip_status(launch_scalar_gemm(s, 3 /*e4m3*/, BI_BF16, 2, stream));
     }
     const bool vec = aligned16(a) && aligned16(bt) && k % 16 == 0;
+    const bool fast = fp8_fast(tc);
     if (pl.tile >= 40 && vec && m * k <= kDirectMaxBytes && n * k <= kDirectMaxBytes) {
         MfmaArgs d{};
         d.a = a; d.lda = k; d.b = bt; d.ldb = k; d.c = y; d.ldc = n;
@@ -429,7 +463,7 @@ int fp8_gemm(void *y, const void *a, const void *bt, const float *a_dequant,
         d.scale_a = a_dequant; d.scale_b = b_dequant;
         d.bias = bias;
         const int tile = direct_tile(d, batch_tile(pl, tc, m, n), m * k, n * k);
-        return hip_status(launch_fp8_dl(d, tile, stream));
+        return hip_status(launch_fp8_dl(d, tile, fast, stream));
     }
     // register-staged fp8 kernel: 256x256, 128x128 or 64x64 tiles
     const TileShape *ts = mfma_tile(pl.tile);
@@ -446,7 +480,7 @@ int fp8_gemm(void *y, const void *a, const void *bt, const float *a_dequant,
     f.tiles_i = cdiv(m, ts->bm); f.tiles_j = cdiv(n, ts->bn);
     f.vec = vec;
     f.vec_c = aligned8(y) && n % 4 == 0;
-    return hip_status(launch_fp8_gemm(f, tile, stream));
+    return hip_status(launch_fp8_gemm(f, tile, fast, stream));
 }
 
 }  // namespace

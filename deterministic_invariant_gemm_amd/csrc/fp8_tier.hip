@@ -5,11 +5,17 @@
 //
 //   y[m,n] = RNE_bf16( ((sum_k a[m,k] * bt[n,k]) * scale_a) * scale_b )
 //
-// MFMA tier: v_mfma_f32_32x32x64_f8f6f4 with both operands in the OCP e4m3
-// format (format code 0), f32 accumulation.  Each output element's accumulator
-// starts at +0 and receives one MFMA per 64-deep reduction step, steps in
-// ascending k; every tile shape issues the same sequence, so tile shape and M
-// never change the bits.  Both operands are k-contiguous, so staging is a
+// MFMA tier, f32 accumulation, each output element's accumulator starting at
+// +0, reduction steps in ascending k:
+//   * default (FAST = false): every e4m3 code is widened exactly to bf16 in
+//     registers and each 16-deep step is one v_mfma_f32_32x32x16_bf16, which
+//     adds the exact products at f32 precision;
+//   * FAST = true (opt-in): each 64-deep step is one
+//     v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in the OCP e4m3
+//     format (format code 0), which aligns the products of each group of 8
+//     reduction indices to the group's largest before adding them.
+// Every tile shape, here and in the direct-load kernel (fp8_dl.hip), issues the
+// same sequence for a path, so tile shape and M never change the bits.  Both operands are k-contiguous, so staging is a
 // straight 16-byte copy into a k-grouped, XOR-swizzled LDS layout (16 fp8
 // values per slot); an operand fragment of one lane is two adjacent slots.
 // Pipeline: two LDS buffers, one slice in registers ahead, one barrier per
@@ -82,7 +88,7 @@ struct Stage8 {
     }
 };
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, bool FAST>
 __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -140,36 +146,64 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
         }
         const u32x4 *la = lds_a[cur];
         const u32x4 *lb = lds_b[cur];
+        if constexpr (FAST) {
 #pragma unroll
-        for (int kk = 0; kk < BK / 64; ++kk) {
-            // this lane's 32 reduction values of the step: groups kg0, kg0 + 1
-            const int kg0 = 4 * kk + 2 * lhalf;
-            i32x8 fa[FM], fb[FN];
+            for (int kk = 0; kk < BK / 64; ++kk) {
+                // this lane's 32 reduction values of the step: groups kg0, kg0 + 1
+                const int kg0 = 4 * kk + 2 * lhalf;
+                i32x8 fa[FM], fb[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * WTM + 32 * i + lrow;
-                const u32x4 lo = la[kg0 * BM + swz(row, kg0)];
-                const u32x4 hi = la[(kg0 + 1) * BM + swz(row, kg0 + 1)];
-                fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                for (int i = 0; i < FM; ++i) {
+                    const int row = wm * WTM + 32 * i + lrow;
+                    const u32x4 lo = la[kg0 * BM + swz(row, kg0)];
+                    const u32x4 hi = la[(kg0 + 1) * BM + swz(row, kg0 + 1)];
+                    fa[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                }
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int row = wn * WTN + 32 * j + lrow;
+                    const u32x4 lo = lb[kg0 * BN + swz(row, kg0)];
+                    const u32x4 hi = lb[(kg0 + 1) * BN + swz(row, kg0 + 1)];
+                    fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        // B fragment first: the lane then holds 4 consecutive output
+                        // columns of one row.  Format codes 0/0: both operands OCP
+                        // fp8 e4m3; no block scales.
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fb[j], fa[i], acc[i][j], 0, 0, 0, 0, 0, 0);
             }
+        } else {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int row = wn * WTN + 32 * j + lrow;
-                const u32x4 lo = lb[kg0 * BN + swz(row, kg0)];
-                const u32x4 hi = lb[(kg0 + 1) * BN + swz(row, kg0 + 1)];
-                fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            for (int kk = 0; kk < BK / 16; ++kk) {
+                // this lane's 8 reduction values of the 16-deep step: half
+                // `lhalf` of group kk, widened exactly to bf16
+                u32x4 fa[FM], fb[FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+                    const int row = wm * WTM + 32 * i + lrow;
+                    const u32x2 g = reinterpret_cast<const u32x2 *>(la + kk * BM + swz(row, kk))[lhalf];
+                    fa[i] = e4m3x8_to_bf16x8(g);
+                }
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int row = wn * WTN + 32 * j + lrow;
+                    const u32x2 g = reinterpret_cast<const u32x2 *>(lb + kk * BN + swz(row, kk))[lhalf];
+                    fb[j] = e4m3x8_to_bf16x8(g);
+                }
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, fb[j]), __builtin_bit_cast(bf16x8, fa[i]),
+                            acc[i][j], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    // B fragment first: the lane then holds 4 consecutive output
-                    // columns of one row.  Format codes 0/0: both operands OCP
-                    // fp8 e4m3; no block scales.
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fb[j], fa[i], acc[i][j], 0, 0, 0, 0, 0, 0);
         }
         __syncthreads();
     }
@@ -209,17 +243,22 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
 
 }  // namespace
 
-hipError_t launch_fp8_gemm(const Fp8Args &p, int tile_id, hipStream_t s) {
-    const int64_t grid = p.tiles_i * p.tiles_j;
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+template <bool FAST>
+hipError_t launch_fp8_tile(const Fp8Args &p, int tile_id, int64_t grid, hipStream_t s) {
     switch (tile_id) {
-    case 1: hipLaunchKernelGGL((fp8_gemm_kernel<256, 256, 2, 2>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((fp8_gemm_kernel<128, 128, 2, 2>), dim3(grid), dim3(NT), 0, s, p); break;
-    case 6: hipLaunchKernelGGL((fp8_gemm_kernel<64, 64, 2, 2>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((fp8_gemm_kernel<256, 256, 2, 2, FAST>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((fp8_gemm_kernel<128, 128, 2, 2, FAST>), dim3(grid), dim3(NT), 0, s, p); break;
+    case 6: hipLaunchKernelGGL((fp8_gemm_kernel<64, 64, 2, 2, FAST>), dim3(grid), dim3(NT), 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const Fp8Args &p, int tile_id, bool fast, hipStream_t s) {
+    const int64_t grid = p.tiles_i * p.tiles_j;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    return fast ? launch_fp8_tile<true>(p, tile_id, grid, s) : launch_fp8_tile<false>(p, tile_id, grid, s);
 }
 
 }  // namespace bi

@@ -108,11 +108,13 @@ bool mfma_backward_pair(int tile_x, int tile_w, int dt);
 hipError_t launch_mfma_backward(const MfmaArgs &px, int tile_x, const MfmaArgs &pw, int tile_w,
                                 int dt, hipStream_t s);
 
-hipError_t launch_fp8_gemm(const Fp8Args &p, int tile_id, hipStream_t s);
-// fp8 on the direct-load MFMA kernel (tile ids 40 + base, 100 + base):
+// fp8 e4m3 GEMM on the register-staged kernel (tile ids 1, 4, 6) and on the
+// direct-load kernel (tile ids 40 + base, 100 + base):
 // C(i,j) = RNE_bf16((sum_r A(i,r) B(j,r)) * scale_a * scale_b), both operands
-// reduction-contiguous e4m3 bytes.
-hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, hipStream_t s);
+// reduction-contiguous e4m3 bytes.  fast = false: codes widened exactly to bf16,
+// one bf16 MFMA per 16-deep step; fast = true: one f8f6f4 MFMA per 64-deep step.
+hipError_t launch_fp8_gemm(const Fp8Args &p, int tile_id, bool fast, hipStream_t s);
+hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, bool fast, hipStream_t s);
 // fp8 quantisation (quant.hip): fmt DT_E4M3 or DT_E5M2; amax (nullable)
 // receives max(*amax, max |src|).  quantize: n elements; transpose_quantize:
 // src [rows, cols] -> dst [cols, rows].

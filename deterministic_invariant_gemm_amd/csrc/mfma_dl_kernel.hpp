@@ -5,7 +5,10 @@
 // receives one v_mfma_f32_32x32x16_{bf16,f16} per 16-deep reduction step, in
 // ascending order from +0 over 64-deep stages starting at the first index of
 // its reduction range, reduction indices past the end contributing exact
-// zeros, and the B fragment is the first MFMA operand.  Every tile shape of
+// zeros, and the B fragment is the first MFMA operand.  fp8 e4m3 operands are
+// staged as bytes (128 per stage row) and, on the exact path, widened to bf16
+// in registers for the same bf16 instruction per 16-deep step; the fast path
+// issues one v_mfma_scale_f32_32x32x64_f8f6f4 per 64-deep step instead.  Every tile shape of
 // this family, and of the other kernel families, therefore gives identical
 // bits (sgemm-bi PyPI page, "Determinism contracts": bit-identical tile
 // families; the forward is batch-invariant because no tile reads M).
@@ -126,29 +129,40 @@ __device__ __forceinline__ int rs_xor(int k) {
 
 // Per data type: bytes per element, reduction values per LDS stage (one
 // 128-byte row segment of a reduction-contiguous tile), MFMA steps per stage
-// and the MFMA fragment of one lane.
+// and the MFMA fragment of one lane as read from LDS.
 template <int DT>
 struct DlType {  // bf16 / f16: v_mfma_f32_32x32x16_{bf16,f16}, 16 values per step
     static constexpr int ESZ = 2, KPS = 64, STEPS = 4;
     using Frag = u32x4;
 };
 template <>
-struct DlType<DT_E4M3> {  // fp8 e4m3: v_mfma_scale_f32_32x32x64_f8f6f4, 64 per step
+struct DlType<DT_E4M3> {  // fp8 e4m3 codes widened exactly to bf16:
+    // v_mfma_f32_32x32x16_bf16, 16 values per step, 8 codes (8 bytes) per lane
+    static constexpr int ESZ = 1, KPS = 128, STEPS = 8;
+    using Frag = u32x2;
+};
+template <>
+struct DlType<DT_E4M3_FAST> {  // fp8 e4m3: v_mfma_scale_f32_32x32x64_f8f6f4, 64 per step
     static constexpr int ESZ = 1, KPS = 128, STEPS = 2;
     using Frag = i32x8;
 };
 
 // One MFMA step, B fragment first (each lane then holds 4 consecutive output
-// columns of one row).
+// columns of one row).  e4m3 fragments of the exact path arrive here already
+// widened to bf16 (u32x4).
 template <int DT>
 __device__ __forceinline__ f32x16 dl_mfma(u32x4 b, u32x4 a, f32x16 c) {
-    return mfma_step<DT>(b, a, c);
+    return mfma_step<DT == DT_E4M3 ? DT_BF16 : DT>(b, a, c);
 }
 template <int DT>
 __device__ __forceinline__ f32x16 dl_mfma(i32x8 b, i32x8 a, f32x16 c) {
     // format codes 0 / 0: both operands OCP fp8 e4m3; no block scales
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
 }
+// fragment as the MFMA takes it: e4m3 codes of the exact path widened to bf16
+__device__ __forceinline__ u32x4 dl_operand(u32x2 f) { return e4m3x8_to_bf16x8(f); }
+__device__ __forceinline__ u32x4 dl_operand(u32x4 f) { return f; }
+__device__ __forceinline__ i32x8 dl_operand(i32x8 f) { return f; }
 
 // Global -> LDS copy of one operand tile per stage (128 bytes of each row or,
 // row-contiguous, 64 reduction rows): R/8 instructions of 1 KB, spread evenly
@@ -205,11 +219,13 @@ struct DLoad {
 
 // MFMA fragment reads from a reduction-contiguous stage ([rows][128 bytes]).
 // 16-bit: lane l takes 16 bytes (8 values) of row l & 31 at value 8 * (l >> 5)
-// of the step; fp8: 32 bytes (two chunks) at value 32 * (l >> 5).
-template <int ESZ = 2>
+// of the 16-deep step; e4m3 (exact path): 8 bytes (8 codes) at value
+// 8 * (l >> 5) of the 16-deep step; e4m3 (fast path): 32 bytes (two chunks)
+// at value 32 * (l >> 5) of the 64-deep step.
+template <int DT>
 struct RcFrag {
-    static constexpr int CH = ESZ == 2 ? 1 : 2;  // 16-byte chunks per lane and step
-    static constexpr int STEPS = 8 / (2 * CH);   // steps per stage
+    static constexpr int CH = DT == DT_E4M3_FAST ? 2 : 1;  // reads per lane and step
+    static constexpr int STEPS = DlType<DT>::STEPS;         // steps per stage
     uint32_t koff[STEPS][CH];  // lane's byte offsets inside a 32-row block
 
     __device__ __forceinline__ void init(int lane) {
@@ -217,13 +233,20 @@ struct RcFrag {
 #pragma unroll
         for (int kk = 0; kk < STEPS; ++kk)
 #pragma unroll
-            for (int c = 0; c < CH; ++c)
-                koff[kk][c] = (uint32_t)(r * 128 + 16 * ((2 * CH * kk + CH * hi + c) ^ rc_xor(r)));
+            for (int c = 0; c < CH; ++c) {
+                if constexpr (DT == DT_E4M3)  // chunk kk holds the step, half hi the lane's
+                    koff[kk][c] = (uint32_t)(r * 128 + 16 * (kk ^ rc_xor(r)) + 8 * hi);
+                else
+                    koff[kk][c] =
+                        (uint32_t)(r * 128 + 16 * ((2 * CH * kk + CH * hi + c) ^ rc_xor(r)));
+            }
     }
     // rows base .. base+31 (base a multiple of 32)
     __device__ __forceinline__ auto read(const BI_LDS char *stage, int base, int kk) const {
         const BI_LDS char *row = stage + base * 128;
-        if constexpr (CH == 1) {
+        if constexpr (DT == DT_E4M3) {
+            return *reinterpret_cast<const BI_LDS u32x2 *>(row + koff[kk][0]);
+        } else if constexpr (CH == 1) {
             return *reinterpret_cast<const BI_LDS u32x4 *>(row + koff[kk][0]);
         } else {
             const u32x4 lo = *reinterpret_cast<const BI_LDS u32x4 *>(row + koff[kk][0]);
@@ -261,13 +284,13 @@ struct RsFrag {
     }
 };
 
-template <bool RC, int R, int ESZ = 2>
+template <bool RC, int R, int DT>
 struct FragOf {
     using type = RsFrag<R>;
 };
-template <int R, int ESZ>
-struct FragOf<true, R, ESZ> {
-    using type = RcFrag<ESZ>;
+template <int R, int DT>
+struct FragOf<true, R, DT> {
+    using type = RcFrag<DT>;
 };
 
 // Tiles of two to four MFMA waves (burst copies) get DL_NPW extra waves that
@@ -313,7 +336,8 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
     using TY = DlType<DT>;
     constexpr int KPS = TY::KPS, STEPS = TY::STEPS;
     using Frag = typename TY::Frag;
-    static_assert(DT != DT_E4M3 || (A_RC && B_RC), "fp8 operands are reduction-contiguous");
+    constexpr bool FP8 = DT == DT_E4M3 || DT == DT_E4M3_FAST;
+    static_assert(!FP8 || (A_RC && B_RC), "fp8 operands are reduction-contiguous");
     static_assert(slab_bytes<EPI, WTN, NW>() <= NS * (SA + SB), "epilogue slabs fit in the stages");
     static_assert((EPI != EPI_ROUND && EPI != EPI_SCALE) || BN <= 64 * NW,
                   "one thread per bias column");
@@ -339,8 +363,8 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
     LB lb;
     la.init(p.lda, row0, r_begin, cwave, lane);
     lb.init(p.ldb, col0, r_begin, cwave, lane);
-    typename FragOf<A_RC, BM, TY::ESZ>::type ra;
-    typename FragOf<B_RC, BN, TY::ESZ>::type rb;
+    typename FragOf<A_RC, BM, DT>::type ra;
+    typename FragOf<B_RC, BN, DT>::type rb;
     ra.init(lane);
     rb.init(lane);
 
@@ -385,13 +409,21 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
 #pragma unroll
         for (int j = 0; j < FN; ++j) fb[set][j] = frag_b(st + SA, j, kk);
     };
+    // every fragment of a set as the MFMA takes it (e4m3 codes of the exact path
+    // are widened once per fragment, not once per MFMA)
+    using Op = decltype(dl_operand(Frag{}));
     auto mfma_step_all = [&](int set) {
+        Op ob[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j) ob[j] = dl_operand(fb[set][j]);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = dl_mfma<DT>(fb[set][j], fa[set][i], acc[i][j]);
+        for (int i = 0; i < FM; ++i) {
+            const Op oa = dl_operand(fa[set][i]);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = dl_mfma<DT>(ob[j], oa, acc[i][j]);
+        }
     };
-    constexpr int RCR = TY::ESZ == 2 ? 1 : 2;  // LDS reads per reduction-contiguous fragment
+    constexpr int RCR = DT == DT_E4M3_FAST ? 2 : 1;  // LDS reads per reduction-contiguous fragment
     constexpr int NREAD = FM * (A_RC ? RCR : 2) + FN * (B_RC ? RCR : 2);  // per step
     constexpr int NMFMA = FM * FN;
     // LDS reads of `sets` steps spread between the MFMAs of one step
@@ -496,6 +528,11 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
 #pragma unroll
             for (int kk = BAR + 1; kk < STEPS; ++kk) {
                 const int x0 = first_set(kk), nx = first_set(kk + 1) - x0;
+                Op oa[FM], ob[FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i) oa[i] = dl_operand(fa[kk][i]);
+#pragma unroll
+                for (int j = 0; j < FN; ++j) ob[j] = dl_operand(fb[kk][j]);
 #pragma unroll
                 for (int q = 0; q < NMFMA; ++q) {
                     // fragments (set x0 + f / (FM+FN), index f % (FM+FN)) with f = q mod NMFMA
@@ -506,7 +543,7 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
                         else fb[x][g - FM] = frag_b(nxt + SA, g - FM, x);
                     }
                     acc[q / FN][q % FN] =
-                        dl_mfma<DT>(fb[kk][q % FN], fa[kk][q / FN], acc[q / FN][q % FN]);
+                        dl_mfma<DT>(ob[q % FN], oa[q / FN], acc[q / FN][q % FN]);
                     if (copies) {
                         const int c0 = ((kk - BAR - 1) * NMFMA + q) * CPS;
 #pragma unroll

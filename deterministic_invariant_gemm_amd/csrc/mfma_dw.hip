@@ -1,5 +1,5 @@
 // Instantiations of the MFMA kernels for dW (both operands row-contiguous), rounded or as f32 chunk partials.
-#include "mfma_pp_kernel.hpp"
+#include "mfma_dl_kernel.hpp"
 
 namespace bi {
 
@@ -10,13 +10,6 @@ hipError_t launch_mfma_dw(const MfmaArgs &p, int tile_id, int dt, int epi, int64
         if (dt == DT_F16 && epi == EPI_ROUND) return launch_dls_among<DT_F16, false, false, EPI_ROUND, MODE_PLAIN, 4, 5, 8, 15>(p, tile_id, grid, s);
         if (dt == DT_BF16 && epi == EPI_PARTIAL) return launch_dls_among<DT_BF16, false, false, EPI_PARTIAL, MODE_PLAIN, 4, 5, 8, 15>(p, tile_id, grid, s);
         if (dt == DT_F16 && epi == EPI_PARTIAL) return launch_dls_among<DT_F16, false, false, EPI_PARTIAL, MODE_PLAIN, 4, 5, 8, 15>(p, tile_id, grid, s);
-        return hipErrorInvalidValue;
-    }
-    if (tile_id >= 80) {
-        if (dt == DT_BF16 && epi == EPI_ROUND) return launch_pp_among<DT_BF16, false, false, EPI_ROUND, MODE_PLAIN, 13, 14, 15>(p, tile_id, grid, s);
-        if (dt == DT_F16 && epi == EPI_ROUND) return launch_pp_among<DT_F16, false, false, EPI_ROUND, MODE_PLAIN, 13, 14, 15>(p, tile_id, grid, s);
-        if (dt == DT_BF16 && epi == EPI_PARTIAL) return launch_pp_among<DT_BF16, false, false, EPI_PARTIAL, MODE_PLAIN, 13, 14, 15>(p, tile_id, grid, s);
-        if (dt == DT_F16 && epi == EPI_PARTIAL) return launch_pp_among<DT_F16, false, false, EPI_PARTIAL, MODE_PLAIN, 13, 14, 15>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
     if (tile_id >= 40) {

@@ -1,7 +1,5 @@
 // Instantiations of the MFMA kernels for dX (both operands reduction-contiguous).
-#include "mfma_ad_kernel.hpp"
-#include "mfma_da_kernel.hpp"
-#include "mfma_pp_kernel.hpp"
+#include "mfma_dl_kernel.hpp"
 
 namespace bi {
 
@@ -18,24 +16,9 @@ hipError_t launch_mfma_dx(const MfmaArgs &p, int tile_id, int dt, int epi, int64
         if (dt == DT_F16) return launch_dls_among<DT_F16, true, true, EPI_ROUND, MODE_PLAIN, 5, 11, 15>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
-    if (tile_id >= 80) {
-        if (dt == DT_BF16) return launch_pp_among<DT_BF16, true, true, EPI_ROUND, MODE_PLAIN, 11, 13, 15>(p, tile_id, grid, s);
-        if (dt == DT_F16) return launch_pp_among<DT_F16, true, true, EPI_ROUND, MODE_PLAIN, 11, 13, 15>(p, tile_id, grid, s);
-        return hipErrorInvalidValue;
-    }
-    if (tile_id >= 60) {
-        if (dt == DT_BF16) return launch_da_among<DT_BF16, true, EPI_ROUND, MODE_PLAIN, 5, 10, 16, 18, 19>(p, tile_id, grid, s);
-        if (dt == DT_F16) return launch_da_among<DT_F16, true, EPI_ROUND, MODE_PLAIN, 5, 10, 16, 18, 19>(p, tile_id, grid, s);
-        return hipErrorInvalidValue;
-    }
     if (tile_id >= 40) {
         if (dt == DT_BF16) return launch_dl_among<DT_BF16, true, true, EPI_ROUND, MODE_PLAIN, 2, 3, 4, 5, 6, 10, 11, 13, 15>(p, tile_id, grid, s);
         if (dt == DT_F16) return launch_dl_among<DT_F16, true, true, EPI_ROUND, MODE_PLAIN, 2, 3, 4, 5, 6, 10, 11, 13, 15>(p, tile_id, grid, s);
-        return hipErrorInvalidValue;
-    }
-    if (tile_id >= 20) {
-        if (dt == DT_BF16) return launch_ad_among<DT_BF16, true, EPI_ROUND, MODE_PLAIN, 2, 3, 4, 5, 7, 9, 10>(p, tile_id, grid, s);
-        if (dt == DT_F16) return launch_ad_among<DT_F16, true, EPI_ROUND, MODE_PLAIN, 2, 3, 4, 5, 7, 9, 10>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
     if (dt == DT_BF16) return launch_among<DT_BF16, true, true, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11, 13, 15>(p, tile_id, grid, s);

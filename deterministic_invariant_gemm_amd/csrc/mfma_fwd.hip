@@ -1,7 +1,5 @@
 // Instantiations of the MFMA kernels for the linear forward (A reduction-contiguous, B = W row-contiguous).
-#include "mfma_ad_kernel.hpp"
-#include "mfma_da_kernel.hpp"
-#include "mfma_pp_kernel.hpp"
+#include "mfma_dl_kernel.hpp"
 
 namespace bi {
 
@@ -18,24 +16,9 @@ hipError_t launch_mfma_fwd(const MfmaArgs &p, int tile_id, int dt, int epi, int6
         if (dt == DT_F16) return launch_dls_among<DT_F16, true, false, EPI_ROUND, MODE_PLAIN, 11, 15>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
-    if (tile_id >= 80) {
-        if (dt == DT_BF16) return launch_pp_among<DT_BF16, true, false, EPI_ROUND, MODE_PLAIN, 11, 12, 13, 14, 15>(p, tile_id, grid, s);
-        if (dt == DT_F16) return launch_pp_among<DT_F16, true, false, EPI_ROUND, MODE_PLAIN, 11, 12, 13, 14, 15>(p, tile_id, grid, s);
-        return hipErrorInvalidValue;
-    }
-    if (tile_id >= 60) {
-        if (dt == DT_BF16) return launch_da_among<DT_BF16, false, EPI_ROUND, MODE_PLAIN, 16, 18, 19>(p, tile_id, grid, s);
-        if (dt == DT_F16) return launch_da_among<DT_F16, false, EPI_ROUND, MODE_PLAIN, 16, 18, 19>(p, tile_id, grid, s);
-        return hipErrorInvalidValue;
-    }
     if (tile_id >= 40) {
         if (dt == DT_BF16) return launch_dl_among<DT_BF16, true, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 6, 7, 9, 11, 12, 13, 14, 15>(p, tile_id, grid, s);
         if (dt == DT_F16) return launch_dl_among<DT_F16, true, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 6, 7, 9, 11, 12, 13, 14, 15>(p, tile_id, grid, s);
-        return hipErrorInvalidValue;
-    }
-    if (tile_id >= 20) {
-        if (dt == DT_BF16) return launch_ad_among<DT_BF16, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 7, 9>(p, tile_id, grid, s);
-        if (dt == DT_F16) return launch_ad_among<DT_F16, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 7, 9>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
     if (dt == DT_BF16) return launch_among<DT_BF16, true, false, EPI_ROUND, MODE_PLAIN, 1, 2, 3, 4, 6, 7, 9, 11, 12, 13, 14>(p, tile_id, grid, s);

@@ -666,10 +666,7 @@ template <> struct TileOf<12> { static constexpr int BM = 256, BN = 256, WGM = 4
 template <> struct TileOf<13> { static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 2; };
 template <> struct TileOf<14> { static constexpr int BM = 128, BN = 256, WGM = 2, WGN = 4; };
 template <> struct TileOf<15> { static constexpr int BM = 128, BN = 128, WGM = 2, WGN = 4; };
-// four waves stacked along M (used by the direct-A kernel)
-template <> struct TileOf<16> { static constexpr int BM = 256, BN = 192, WGM = 4, WGN = 1; };
-template <> struct TileOf<18> { static constexpr int BM = 256, BN = 128, WGM = 4, WGN = 1; };
-template <> struct TileOf<19> { static constexpr int BM = 128, BN = 192, WGM = 4, WGN = 1; };
+// three waves side by side (direct-load kernel only)
 template <> struct TileOf<17> { static constexpr int BM = 96, BN = 96, WGM = 1, WGN = 3; };
 // small-M shapes (direct-load kernel only, tile id 120): many narrow column tiles
 template <> struct TileOf<20> { static constexpr int BM = 64, BN = 32, WGM = 2, WGN = 1; };

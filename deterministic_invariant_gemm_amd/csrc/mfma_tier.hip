@@ -22,11 +22,6 @@ const TileShape *mfma_tile(int id) {
         // eight-wave workgroups
         {11, 256, 192}, {12, 256, 256}, {13, 256, 128}, {14, 128, 256}, {15, 128, 128},
     };
-    // ids 20 + i: the A-direct kernel on base tile i (same shape)
-    static const TileShape ad[] = {
-        {21, 256, 256}, {22, 256, 192}, {23, 256, 128}, {24, 128, 128}, {25, 128, 96},
-        {27, 128, 256}, {29, 128, 192}, {30, 256, 96},
-    };
     // ids 40 + i: the direct-load kernel on base tile i (same shape)
     static const TileShape dl[] = {
         {41, 256, 256}, {42, 256, 192}, {43, 256, 128}, {44, 128, 128}, {45, 128, 96},
@@ -34,27 +29,14 @@ const TileShape *mfma_tile(int id) {
         {52, 256, 256}, {53, 256, 128}, {54, 128, 256}, {55, 128, 128},
         {48, 96, 96},   {57, 96, 96},   {120, 64, 32},
     };
-    // ids 60 + i: the direct-A kernel on base tile i (waves stacked along M)
-    static const TileShape da[] = {
-        {65, 128, 96}, {70, 256, 96}, {76, 256, 192}, {78, 256, 128}, {79, 128, 192},
-    };
-    for (const TileShape &s : da)
-        if (s.id == id) return &s;
     // ids 100 + i: the direct-load kernel with copies spread between MFMAs
     static const TileShape dls[] = {
-        {104, 128, 128}, {105, 128, 96}, {108, 96, 96}, {111, 256, 192}, {112, 256, 256}, {115, 128, 128},
+        {104, 128, 128}, {105, 128, 96}, {108, 96, 96}, {111, 256, 192}, {112, 256, 256},
+        {114, 128, 256}, {115, 128, 128},
     };
     for (const TileShape &s : dls)
         if (s.id == id) return &s;
-    // ids 80 + i: the eight-wave ping-pong kernel on base tile i
-    static const TileShape pp[] = {
-        {91, 256, 192}, {92, 256, 256}, {93, 256, 128}, {94, 128, 256}, {95, 128, 128},
-    };
-    for (const TileShape &s : pp)
-        if (s.id == id) return &s;
     for (const TileShape &s : shapes)
-        if (s.id == id) return &s;
-    for (const TileShape &s : ad)
         if (s.id == id) return &s;
     for (const TileShape &s : dl)
         if (s.id == id) return &s;

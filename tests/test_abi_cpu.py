@@ -194,3 +194,36 @@ def test_linear_backward_validation(lib):
     assert dig.bi_linear_backward(None, None, None, None, None, 64, 0, 128, bf, None, 0) == 0
     assert dig.bi_linear_backward(None, None, None, None, None, 0, 96, 0, bf, None, 0) == 0
     assert dig.bi_linear_backward(None, None, F, F, F, 0, 96, 128, bf, None, 0) == -1
+
+
+def test_tc_values(lib):
+    """tc: 0 scalar, 1 auto, 2 MFMA required, 3 fp8 GEMMs on the fp8 matrix
+    instruction (other ops reject it); every other value is rejected by
+    libbi.so, while libbi_testing.so takes tc = 16 + tile id (plus 4096 for the
+    fp8 fast path) and reports the forced tile in the plan."""
+    U, bf = -7, dig.BI_BF16
+    for tc in (0, 1, 2):
+        assert dig.bi_plan(dig.OP_FWD, bf, tc, 768, 3072)[0] >= 0
+    exact = dig.bi_plan(dig.OP_FP8, bf, 1, 4096, 4096)[0]
+    fast = dig.bi_plan(dig.OP_FP8, bf, dig.TC_FP8_FAST, 4096, 4096)[0]
+    assert exact > 0 and fast > 0
+    assert dig.bi_plan(dig.OP_FWD, bf, dig.TC_FP8_FAST, 768, 3072)[0] == U
+    assert dig.bi_forward(F, F, F, None, 4, 128, 128, bf, None, dig.TC_FP8_FAST) == U
+    assert dig.bi_backward_dx(F, F, F, 4, 128, 128, bf, None, 16 + 44) == U
+    for tc in (4, 15, 16 + 44, 4096 + 16 + 44, -1):
+        assert dig.bi_plan(dig.OP_FWD, bf, tc, 768, 3072)[0] == U, tc
+        assert dig.bi_plan(dig.OP_FP8, bf, tc, 4096, 4096)[0] == U, tc
+    # n < 64: tc = 3 falls back to the scalar tier like tc = 1
+    assert dig.bi_plan(dig.OP_FP8, bf, dig.TC_FP8_FAST, 4096, 48)[0] == 0
+    if not os.path.exists(dig.LIB_TESTING_PATH):
+        pytest.skip("libbi_testing.so not built")
+    with dig.testing_build():
+        assert dig.bi_plan(dig.OP_FWD, bf, 16 + 44, 768, 3072)[0] == 44
+        assert dig.bi_plan(dig.OP_FP8, bf, 16 + 112, 4096, 4096)[0] == 112
+        assert dig.bi_plan(dig.OP_FP8, bf, 4096 + 16 + 54, 4096, 4096)[0] == 54
+        # the fast bit is for fp8 GEMMs only; the dW chunk never follows a forced tile
+        assert dig.bi_plan(dig.OP_FWD, bf, 4096 + 16 + 44, 768, 3072)[0] == U
+        assert (dig.bi_plan(dig.OP_DW, bf, 16 + 46, 768, 3072)[1]
+                == dig.bi_plan(dig.OP_DW, bf, 1, 768, 3072)[1])
+    # back on the production library
+    assert dig.bi_plan(dig.OP_FWD, bf, 16 + 44, 768, 3072)[0] == U

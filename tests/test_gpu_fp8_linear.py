@@ -124,7 +124,7 @@ def oracle_args(d):
     return (d["sx"], d["sw"], d["sx_inv"], d["sw_inv"])
 
 
-@pytest.mark.parametrize("tc", [0, 1])
+@pytest.mark.parametrize("tc", [0, 1, 3])
 @pytest.mark.parametrize("shape,bias", [((300, 256, 260), True), ((129, 200, 96), False),
                                         ((1, 64, 64), True), ((520, 384, 392), True)],
                          ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else str(v))
@@ -134,15 +134,15 @@ def test_fp8_linear_parity(shape, bias, tc):
     L = Fp8Linear(d)
     y, ax, aw = L.forward(tc)
     r = oracle.fp8_linear_forward(d["x"], d["w"], d["b"], *oracle_args(d), m, k, n)
-    check(host(y, np.uint16), r, synth.BF16, f"fp8 linear forward {shape}")
+    check(host(y, np.uint16), r, synth.BF16, f"fp8 linear forward {shape}", groups=tc == 3)
     assert (ax, aw) == (r.amax_x, r.amax_w)
     dx, dw, ag = L.backward(tc=tc)
     args = (d["g"], d["x"], d["w"], d["sg"], d["sw"], d["sx"], d["sg_inv"], d["sw_inv"],
             d["sx_inv"], m, k, n)
     rdx = oracle.fp8_linear_backward("dx", *args)
     rdw = oracle.fp8_linear_backward("dw", *args)
-    check(host(dx, np.uint16), rdx, synth.BF16, f"fp8 linear dX {shape}")
-    check(host(dw, np.uint16), rdw, synth.BF16, f"fp8 linear dW {shape}")
+    check(host(dx, np.uint16), rdx, synth.BF16, f"fp8 linear dX {shape}", groups=tc == 3)
+    check(host(dw, np.uint16), rdw, synth.BF16, f"fp8 linear dW {shape}", groups=tc == 3)
     assert ag == rdx.amax_g
     # one gradient at a time gives the same bits
     dx1, dw1, ag1 = L.backward(want_dw=False, tc=tc)

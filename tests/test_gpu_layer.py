@@ -69,7 +69,8 @@ def test_from_torch_matches_nn_linear():
     x = torch.randn(64, 256, dtype=torch.bfloat16, device="cuda")
     y = lay(x).detach()
     # f32 reference on the CPU, one bf16 rounding apart at most (plus f32 order)
-    y32 = x.float().cpu() @ ref.weight.float().cpu().t() + ref.bias.float().cpu()
+    w32, b32 = ref.weight.detach().float().cpu(), ref.bias.detach().float().cpu()
+    y32 = x.float().cpu() @ w32.t() + b32
     err = (y.float().cpu() - y32).abs()
     assert float((err / (y32.abs() + 1e-2)).max()) < 2 ** -7
 

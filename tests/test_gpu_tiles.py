@@ -1,11 +1,11 @@
-"""Every tile shape of the MFMA tier -- in all five kernel families (operands
-staged through registers into LDS; A read directly into registers; both
-operands copied straight from global memory into LDS; A loaded into registers
-with B copied into LDS; eight waves in two alternating groups) -- must give the
-same bits for
-the same problem: the per-element MFMA sequence does not depend on the tile.
-Tiles are forced with the tuning hook tc = 16 + tile id; ids that an op does
-not instantiate are rejected with BI_ERR_HIP before any launch and skipped."""
+"""Every tile shape of the MFMA tier -- in both kernel families (operands
+staged through registers into LDS; both operands copied straight from global
+memory into LDS, with the copies in bursts or spread between MFMAs) -- must give
+the same bits for the same problem: the per-element MFMA sequence does not
+depend on the tile.  Tiles are forced through libbi_testing.so (the same kernels
+as libbi.so; its C ABI accepts tc = 16 + tile id, plus 4096 for the fp8 fast
+path); ids that an op does not instantiate are rejected with BI_ERR_HIP before
+any launch and skipped."""
 import numpy as np
 import pytest
 import torch
@@ -17,21 +17,32 @@ from parity import check, dev, empty, host
 
 pytestmark = pytest.mark.gpu
 
-TILE_IDS = (list(range(1, 20)) + list(range(21, 31)) + list(range(41, 58))
-            + [65, 70, 76, 78, 79, 91, 92, 93, 94, 95, 104, 105, 108, 111, 112, 115, 120])
+TILE_IDS = (list(range(1, 16)) + list(range(41, 58))
+            + [104, 105, 108, 111, 112, 114, 115, 120])
 
 
-def run_all(fn):
+def run_all(fn, ids=TILE_IDS, base=16):
     """{tile id: output bytes} for every tile the op accepts."""
     out = {}
-    for tid in TILE_IDS:
-        try:
-            r = fn(16 + tid)
-        except dig.BIError as e:
-            assert e.status == -6
-            continue
-        out[tid] = r
+    with dig.testing_build():
+        for tid in ids:
+            try:
+                r = fn(base + tid)
+            except dig.BIError as e:
+                assert e.status == -6
+                continue
+            out[tid] = r
     return out
+
+
+def test_production_library_rejects_forced_tiles():
+    """libbi.so has no tile hook: tc = 16 + id is an unknown request there."""
+    m, k, n = 64, 64, 64
+    z = torch.zeros((m, n), dtype=torch.int16, device="cuda")
+    s = torch.cuda.current_stream()
+    assert dig.bi_forward(z, z, z, None, m, k, n, synth.BF16, s, 16 + 44) == -7
+    with dig.testing_build():
+        dig.check(dig.bi_forward(z, z, z, None, m, k, n, synth.BF16, s, 16 + 44))
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
@@ -105,16 +116,18 @@ def test_grouped_tiles_identical(dt):
         print(name, "tiles", sorted(outs))
 
 
-FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 55, 111, 112, 115, 120]
+FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 54, 55, 111, 112, 114, 115, 120]
 
 
 @pytest.mark.parametrize("shape", [(300, 256, 260), (520, 384, 392), (700, 1008, 456),
                                    (260, 200, 300)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_fp8_tiles_identical(shape):
-    """The register-staged fp8 kernel and every direct-load fp8 tile give the
-    same bits (rows of 16-byte multiples use the direct-load kernel; the last
-    shape's K = 200 sends every tile to the register-staged kernel)."""
+@pytest.mark.parametrize("fast", [False, True], ids=["exact", "fast"])
+def test_fp8_tiles_identical(shape, fast):
+    """For either fp8 path, the register-staged fp8 kernel and every
+    direct-load fp8 tile give the same bits (rows of 16-byte multiples use the
+    direct-load kernel; the last shape's K = 200 sends every tile to the
+    register-staged kernel)."""
     m, k, n = shape
     d = synth.fp8(m, k, n, seed=81 + m)
     a, bt = dev(d["a8"]), dev(d["bt8"])
@@ -127,16 +140,11 @@ def test_fp8_tiles_identical(shape):
         dig.check(dig.bi_fp8_mm(y, a, bt, da, db, m, k, n, s, tc))
         return host(y, np.uint16)
 
-    base = run(1)
+    base = run(dig.TC_FP8_FAST if fast else 1)
     check(base, oracle.fp8_mm(d["a8"], d["bt8"], d["da"], d["db"], m, k, n), synth.BF16,
-          "fp8 default tile")
-    outs = {}
-    for tid in FP8_TILE_IDS:
-        try:
-            outs[tid] = run(16 + tid)
-        except dig.BIError as e:
-            assert e.status == -6
+          "fp8 default tile", groups=fast)
+    outs = run_all(run, FP8_TILE_IDS, 16 + (4096 if fast else 0))
     assert len(outs) >= 3, sorted(outs)
     for tid, o in outs.items():
         assert np.array_equal(o, base), tid
-    print("fp8 tiles", sorted(outs))
+    print("fp8 tiles", "fast" if fast else "exact", sorted(outs))

@@ -31,4 +31,4 @@ def test_linear_stores_weight_in_out_and_from_torch_transposes():
     assert torch.equal(lay.bias, ref.bias)
     fresh = Linear(10, 3, bias=False)
     assert fresh.bias is None and fresh.weight.shape == (10, 3)
-    assert float(fresh.weight.abs().max()) <= 1 / 10 ** 0.5
+    assert float(fresh.weight.detach().abs().max()) <= 1 / 10 ** 0.5
