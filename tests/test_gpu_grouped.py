@@ -95,14 +95,16 @@ def test_grouped_exact_integer_bits(tc):
 
 
 def test_grouped_16384x2048x1408_e8():
-    """input[16384,2048], weights[8,1408,2048], 819 padding rows: sampled parity
-    of forward, dinput and dweights, padding rows +0 bytes, 10-run hashes;
+    """input[16384,2048], weights[8,1408,2048], 819 padding rows: parity of
+    forward and dinput on 267 sampled rows (8 of them padding) and of dweights on
+    259 sampled rows of [E*N, K], padding rows +0 bytes, 10-run hashes;
     then the same with expert 5 emptied (its dweights must be zero)."""
     d = synth.grouped_16384x2048x1408_e8()
     G = Grouped(d)
-    rows = sample_rows(G.m, 40, 7)
+    rows = sample_rows(G.m, 256, 7)
     rows = np.union1d(rows, np.nonzero(d["row_experts"] >= G.e)[0][:8])
-    wrows = sample_rows(G.e * G.n, 16, 8)
+    wrows = sample_rows(G.e * G.n, 256, 8)
+    assert len(rows) >= 256 and len(wrows) >= 256
     parity(d, 1, "grouped_16384x2048x1408_e8", rows=rows, wrows=wrows)
     assert len({digest(G.forward(1)) for _ in range(10)}) == 1
     hs = set()

@@ -110,34 +110,80 @@ def test_f32_linear_64x128x256():
         assert np.array_equal(host(L.forward(1, m=mp), np.uint32), y[:mp])
 
 
+def linear_backward(L, tc=1):
+    """dX and dW from one bi_linear_backward call (its dX and dW tiles share a
+    launch at 4096x768x3072)."""
+    m, k, n, dt = L.m, L.k, L.n, L.dt
+    dx, dw = empty((m, k), L.st), empty((k, n), L.st)
+    nb = dig.bi_backward_dw_workspace_bytes(m, k, n, dt, tc)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    dig.check(dig.bi_linear_backward(dx, dw, L.dy, L.x, L.w, m, k, n, dt, ws if nb else None,
+                                     nb, torch.cuda.current_stream(), tc), "bi_linear_backward")
+    return dx, dw
+
+
 @pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
-def test_mlp_up_parity_sampled(dt):
-    """X[4096,768] W[768,3072] + b, dY[4096,3072] on the MFMA tier: sampled
-    output rows against the oracle (rows for forward and dX, K-rows for dW)."""
+def test_mlp_up_parity_full(dt):
+    """X[4096,768] W[768,3072] + b, dY[4096,3072] on the MFMA tier: every
+    element of the forward, dX and dW against the oracle, from the separate
+    calls and from bi_linear_backward (whose bits must equal the separate
+    calls')."""
     d = synth.mlp_up_linear(dt)
     L = Linear(d)
     m, k, n = L.m, L.k, L.n
-    rows = sample_rows(m, 48, 1)
-    stats = []
-    ry = oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n, rows=rows)
-    stats.append(check(host(L.forward(1), L.st)[rows], ry, dt, "mlp_up_linear fwd"))
-    rx = oracle.linear_dx(dt, d["dy"], d["w"], m, k, n, rows=rows)
-    stats.append(check(host(L.dx(1), L.st)[rows], rx, dt, "mlp_up_linear dX"))
-    krows = sample_rows(k, 24, 2)
-    rw = oracle.linear_dw(dt, d["x"], d["dy"], m, k, n, rows=krows)
-    stats.append(check(host(L.dw(1), L.st)[krows], rw, dt, "mlp_up_linear dW"))
-    print("mlp_up_linear (max ulp, #A-clause, max rel):", stats)
+    stats = {}
+    y = host(L.forward(1), L.st)
+    stats["fwd"] = check(y, oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n), dt,
+                         "mlp_up_linear fwd")
+    dx, dw = host(L.dx(1), L.st), host(L.dw(1), L.st)
+    stats["dX"] = check(dx, oracle.linear_dx(dt, d["dy"], d["w"], m, k, n), dt,
+                        "mlp_up_linear dX")
+    stats["dW"] = check(dw, oracle.linear_dw(dt, d["x"], d["dy"], m, k, n), dt,
+                        "mlp_up_linear dW")
+    bx, bw = linear_backward(L)
+    assert np.array_equal(host(bx, L.st), dx) and np.array_equal(host(bw, L.st), dw)
+    print("mlp_up_linear (max ulp, #beyond 1 ulp, max rel):", stats)
 
 
-def test_mlp_up_determinism_and_batch_invariance():
-    d = synth.mlp_up_linear(synth.BF16)
+@pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
+def test_mlp_up_exact_integer_bits(dt):
+    """4096x768x3072 with integers in [-3, 3]: every partial sum is exact in
+    f32 (|sum| <= 4096 * 9 < 2^24), so the production tiles (the forward's
+    256x192 tile, dX 128x96 and dW 96x96 alone and sharing one launch) must
+    reproduce the oracle bit for bit in every element."""
+    m, k, n = 4096, 768, 3072
+    d = synth.linear_integer(m, k, n, dt, seed=17, lo=-3, hi=3)
+    L = Linear(d)
+    assert np.array_equal(host(L.forward(1), L.st),
+                          oracle.linear_forward(dt, d["x"], d["w"], d["b"], m, k, n).out)
+    rx = oracle.linear_dx(dt, d["dy"], d["w"], m, k, n).out
+    rw = oracle.linear_dw(dt, d["x"], d["dy"], m, k, n).out
+    assert np.array_equal(host(L.dx(1), L.st), rx)
+    assert np.array_equal(host(L.dw(1), L.st), rw)
+    bx, bw = linear_backward(L)
+    assert np.array_equal(host(bx, L.st), rx) and np.array_equal(host(bw, L.st), rw)
+
+
+# M' for the batch-invariance check at K = 768, N = 3072.  The forward runs
+# the 256x192 tile from M' = 2817 (at least 192 workgroups), the 128x128 tile
+# for 897..2816, and the 64x32 tile up to M' = 128 (one round of at most 256
+# workgroups); dX (768 output columns) runs the 64x32 tile up to M' = 640 and
+# the 128x96 tile beyond.  The list covers every one of these tiles.
+MLP_UP_MPRIME = (1, 7, 64, 100, 128, 640, 1000, 2000, 2816, 3000, 4096)
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.F16])
+def test_mlp_up_determinism_and_batch_invariance(dt):
+    d = synth.mlp_up_linear(dt)
     L = Linear(d)
     for name, op in (("fwd", lambda: L.forward(1)), ("dX", lambda: L.dx(1)),
-                     ("dW", lambda: L.dw(1))):
+                     ("dW", lambda: L.dw(1)),
+                     ("bi_linear_backward", lambda: torch.cat([t.flatten() for t in
+                                                               linear_backward(L)]))):
         assert len({digest(op()) for _ in range(10)}) == 1, name
     y = host(L.forward(1), np.uint16)
     dx = host(L.dx(1), np.uint16)
-    for mp in (1, 7, 64, 4096):
+    for mp in MLP_UP_MPRIME:
         assert np.array_equal(host(L.forward(1, m=mp), np.uint16), y[:mp]), mp
         assert np.array_equal(host(L.dx(1, m=mp), np.uint16), dx[:mp]), mp
 
@@ -204,19 +250,21 @@ def test_tile_families_give_identical_bits():
 
 def test_square_4096_batch_invariance_sweep():
     """W[4096,4096], X[8192,4096]: every shared row is bit-identical across
-    M in {1, 3, 17, 128, 1000, 8192}; dW at M = 8192 hashed 10 times; sampled
-    oracle parity of the forward at M = 8192 and of dW."""
+    M in {1, 3, 17, 128, 1000, 8192}; dW at M = 8192 hashed 10 times; oracle
+    parity of the forward at M = 8192 on 259 sampled rows and of dW on 259
+    sampled K-rows."""
     d = synth.square_4096_sweep()
     L = Linear(d)
     y = host(L.forward(1), np.uint16)
     for mp in (1, 3, 17, 128, 1000, 8192):
         assert np.array_equal(host(L.forward(1, m=mp), np.uint16), y[:mp]), mp
-    rows = sample_rows(L.m, 12, 4)
+    rows = sample_rows(L.m, 256, 4)
+    assert len(rows) >= 256
     ry = oracle.linear_forward(L.dt, d["x"], d["w"], None, L.m, L.k, L.n, rows=rows)
     check(y[rows], ry, L.dt, "square_4096_sweep fwd")
     hashes = {digest(L.dw(1)) for _ in range(10)}
     assert len(hashes) == 1
-    krows = sample_rows(L.k, 4, 5)
+    krows = sample_rows(L.k, 256, 5)
     rw = oracle.linear_dw(L.dt, d["x"], d["dy"], L.m, L.k, L.n, rows=krows)
     check(host(L.dw(1), np.uint16)[krows], rw, L.dt, "square_4096_sweep dW")
 

@@ -105,7 +105,7 @@ def test_one_gradient_and_determinism():
     assert none is None and torch.equal(only_dx, dx0)
     none, only_dw = combined(d, want_dx=False)
     assert none is None and torch.equal(only_dw, dw0)
-    digests = {(digest(a), digest(b)) for a, b in (combined(d) for _ in range(8))}
+    digests = {(digest(a), digest(b)) for a, b in (combined(d) for _ in range(10))}
     assert len(digests) == 1
 
 
