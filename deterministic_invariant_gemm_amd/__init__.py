@@ -22,6 +22,7 @@ LIB_TESTING_PATH = os.path.join(HERE, "libbi_testing.so")
 BI_F32, BI_BF16, BI_F16 = 0, 1, 2
 BI_FP8_E4M3, BI_FP8_E5M2 = 3, 4
 BI_OK = 0
+BI_STATIC_SCRATCH_BYTES = 64 << 20
 TC_SCALAR, TC_AUTO, TC_MFMA, TC_FP8_FAST = 0, 1, 2, 3
 STATUS = {0: "BI_OK", -1: "BI_ERR_NULL", -2: "BI_ERR_DTYPE", -3: "BI_ERR_SHAPE",
           -4: "BI_ERR_TOO_LARGE", -5: "BI_ERR_WORKSPACE", -6: "BI_ERR_HIP",
@@ -78,6 +79,8 @@ def _bind(path: str) -> ctypes.CDLL:
     L.bi_fp8_mm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i32]
     L.bi_linear_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp, i32]
     L.bi_linear_backward.restype = i32
+    L.bi_linear_backward_static.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i32]
+    L.bi_linear_backward_static.restype = i32
     L.bi_bias_grad_workspace_bytes.argtypes = [i64, i64, i32]
     L.bi_bias_grad_workspace_bytes.restype = sz
     L.bi_bias_grad.argtypes = [vp, vp, i64, i64, i32, vp, sz, vp]
@@ -153,6 +156,11 @@ def bi_linear_backward(dx, dw, dy, x, w, m, k, n, dtype, workspace, workspace_by
                        tc=1) -> int:
     return load().bi_linear_backward(_p(dx), _p(dw), _p(dy), _p(x), _p(w), m, k, n, dtype,
                                      _p(workspace), workspace_bytes, _s(stream), tc)
+
+
+def bi_linear_backward_static(dx, dw, dy, x, w, m, k, n, dtype, stream=None, tc=1) -> int:
+    return load().bi_linear_backward_static(_p(dx), _p(dw), _p(dy), _p(x), _p(w), m, k, n, dtype,
+                                            _s(stream), tc)
 
 
 def bi_bias_grad_workspace_bytes(m, n, dtype) -> int:

@@ -7,6 +7,7 @@
  *   bi_backward_dx          dX = RNE_T(dY W^T)
  *   bi_backward_dw          dW = RNE_T(X^T dY)           (fixed-order two-pass)
  *   bi_linear_backward      dX and dW together (same bits as the two calls)
+ *   bi_linear_backward_static   the same without a caller workspace
  *   bi_bias_grad            db = RNE_T(sum over rows of dY) (fixed order)
  *   bi_fp8_mm               Y  = RNE_bf16((A B^T) dA dB) (fp8 e4m3fn inputs)
  *   bi_fp8_quantize         q  = FP8(bf16 * scale_inv), amax (e4m3fn / e5m2)
@@ -164,6 +165,28 @@ int bi_backward_dw(void *dw, const void *x, const void *dy, int64_t m, int64_t k
 int bi_linear_backward(void *dx, void *dw, const void *dy, const void *x, const void *w,
                        int64_t m, int64_t k, int64_t n, int dtype, void *workspace,
                        size_t workspace_bytes, hipStream_t stream, int tc);
+
+/* Bytes of the static scratch array behind bi_linear_backward_static: one
+ * copy per GPU the library runs on, held until the process ends. */
+#define BI_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments (without the workspace) and bits as
+ * bi_linear_backward, with dW's f32 chunk partials in a library-owned static
+ * device array of BI_STATIC_SCRATCH_BYTES on the current GPU instead of a
+ * caller workspace.  Nothing here allocates (no hipMalloc, no allocating
+ * library call).  Errors: BI_ERR_WORKSPACE when the partials would need more
+ * than BI_STATIC_SCRATCH_BYTES (bi_backward_dw_workspace_bytes(m, k, n,
+ * dtype, tc) above it), checked before anything is enqueued; otherwise those
+ * of bi_linear_backward, plus BI_ERR_HIP if the array's device address cannot
+ * be looked up (done once per GPU, on the first call there).  All calls on
+ * one GPU share its array and every call overwrites the partials it reads:
+ * calls that overlap on one GPU (on different streams, or from several host
+ * threads without ordering) race. */
+int bi_linear_backward_static(void *dx, void *dw, const void *dy, const void *x, const void *w,
+                              int64_t m, int64_t k, int64_t n, int dtype, hipStream_t stream,
+                              int tc);
 
 /* Workspace bytes bi_bias_grad needs (0 when m <= 256).  Returns 0 for invalid
  * arguments as well. */

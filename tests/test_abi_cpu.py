@@ -227,3 +227,18 @@ def test_tc_values(lib):
                 == dig.bi_plan(dig.OP_DW, bf, 1, 768, 3072)[1])
     # back on the production library
     assert dig.bi_plan(dig.OP_FWD, bf, 16 + 44, 768, 3072)[0] == U
+
+
+def test_static_backward_validation(lib):
+    """bi_linear_backward_static refuses partials beyond its static array and
+    reports bi_linear_backward's validation errors, all before any HIP call."""
+    bf = dig.BI_BF16
+    m, k, n = 65536, 1024, 1024  # 64 chunks of 1024 x 1024 f32 partials: 256 MiB
+    assert dig.bi_backward_dw_workspace_bytes(m, k, n, bf, 1) > dig.BI_STATIC_SCRATCH_BYTES
+    assert dig.bi_linear_backward_static(F, F, F, F, F, m, k, n, bf, None, 1) == -5
+    assert dig.bi_linear_backward_static(F, F, F, F, F, 4, 8, 8, 9, None, 1) == -2
+    assert dig.bi_linear_backward_static(F, F, F, F, F, 4, -8, 8, bf, None, 1) == -3
+    assert dig.bi_linear_backward_static(F, F, None, F, F, 4, 128, 128, bf, None, 1) == -1
+    assert dig.bi_linear_backward_static(F, F, F, F, F, 64, 48, 768, bf, None, 2) == -7
+    assert dig.bi_linear_backward_static(None, None, None, None, None, 0, 96, 0, bf,
+                                         None, 1) == 0
