@@ -19,7 +19,9 @@ Other workloads (--workload): fp8 (e4m3 GEMM 8192x4096x4096), fp8_linear
 experts, 16384x2048 -> 1408, forward + dinput + dweights), sweep (forward of
 W[4096,4096] at M in {1,3,17,128,1000,8192}), bias_grad (column sums of
 dY[4096,3072] and dY[16384,8192], bf16), tiles (forward, dX and dW of the
-default workload on each candidate tile, for the tile-choice counters).
+default workload on each candidate tile, for the tile-choice counters), scalar
+(the scalar FMA tier: bf16 768 -> 48 at M = 4096 and the f32 64x128x256
+linear).
 """
 from __future__ import annotations
 
@@ -37,6 +39,10 @@ sys.path.insert(0, ROOT)
 BF16_PEAK = 2516.6   # TFLOP/s, dense bf16/f16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 FP8_PEAK = 5033.2    # TFLOP/s, dense fp8 MFMA
 HBM_PEAK = 8000.0    # GB/s
+# f32 FMA on the vector ALUs without packed instructions (the library is built
+# without packed f32 math): 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+F32_VALU_PEAK = 78.6  # TFLOP/s
+BF16_FLOP_PER_CLK = 256 * 4096  # dense bf16 MFMA flop per shader clock, whole chip
 
 
 def parse():
@@ -46,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="linear",
                     choices=["linear", "fp8", "fp8_linear", "grouped", "sweep", "bias_grad",
-                             "tiles", "copy"])
+                             "tiles", "copy", "scalar"])
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"])
     ap.add_argument("--settle-ms", type=float, default=400.0,
                     help="untimed run of the step before the warm-up steps, so that the GPU "
@@ -154,19 +160,81 @@ SETTLE_MS = 400.0
 _settled = [False]
 
 
+class ClockSampler:
+    """Shader clock (MHz) of GPU 0 read through amdsmi (gpu metrics,
+    current_gfxclk) every few milliseconds from a host thread while the step
+    runs untimed.  Never active during a timed region."""
+
+    def __init__(self):
+        self.samples, self.error, self._stop, self._th = [], None, False, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            self._read()
+        except Exception as e:  # no SMI access on this host: report why
+            self.error = f"amdsmi unavailable: {e!r}"[:200]
+
+    def _read(self):
+        return float(self._smi.amdsmi_get_gpu_metrics_info(self._h)["current_gfxclk"])
+
+    def _loop(self):
+        while not self._stop:
+            try:
+                self.samples.append(self._read())
+            except Exception as e:
+                self.error = f"amdsmi read failed: {e!r}"[:200]
+                return
+            time.sleep(0.004)
+
+    def start(self):
+        if self.error is None:
+            import threading
+            self._stop = False
+            self._th = threading.Thread(target=self._loop, daemon=True)
+            self._th.start()
+
+    def stop(self):
+        if self._th is not None:
+            self._stop = True
+            self._th.join()
+            self._th = None
+
+    def summary(self):
+        if not self.samples:
+            return {"mhz": None, "source": self.error or "no samples"}
+        a = np.array(self.samples)
+        return {"mhz": float(np.median(a)), "min": float(a.min()), "max": float(a.max()),
+                "samples": int(a.size),
+                "source": "amdsmi gpu metrics current_gfxclk, sampled every ~4 ms while the "
+                          "step ran untimed (second half of the clock-settle phase)"}
+
+
+CLOCK = [None]
+
+
 def settle(torch, ops):
     """Run the step, untimed, for SETTLE_MS of wall time (first call only).  An
     idle MI355X takes a few hundred milliseconds of load to reach its working
-    clocks; without this the first few hundred steps run up to 15 % slower."""
+    clocks; without this the first few hundred steps run up to 15 % slower.
+    The shader clock is sampled during the second half of this phase."""
     if _settled[0] or SETTLE_MS <= 0:
         return
     s = torch.cuda.current_stream()
+    clock = ClockSampler()
     t0 = time.perf_counter()
+    sampling = False
     while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        if not sampling and (time.perf_counter() - t0) * 1e3 >= SETTLE_MS / 2:
+            clock.start()
+            sampling = True
         for _ in range(20):
             for _, fn in ops:
                 fn(s)
         torch.cuda.synchronize()
+    clock.stop()
+    CLOCK[0] = clock.summary()
     _settled[0] = True
 
 
@@ -274,6 +342,17 @@ def bench_linear(args, torch, dig, synth):
               "bwd": 2 * (m * n + k * n + m * k) + 2 * (m * k + k * n)}
     dominant = max(per, key=per.get)
     achieved = flops[dominant] / (per[dominant] * 1e-3) / 1e12
+    clock = CLOCK[0] or {"mhz": None, "source": "no clock-settle phase"}
+    # the dense bf16 MFMA peak at the measured clock, for context beside the
+    # fraction of the 2.4 GHz specification peak
+    peak_at_clock = (BF16_FLOP_PER_CLK * clock["mhz"] * 1e6 / 1e12) if clock["mhz"] else None
+
+    def op_entry(name, v):
+        tf = flops[name] / (v * 1e-3) / 1e12
+        e = {"us": round(v * 1e3, 2), "tflops": round(tf, 2), "frac_peak": round(tf / BF16_PEAK, 4)}
+        if peak_at_clock:
+            e["frac_peak_at_sclk"] = round(tf / peak_at_clock, 4)
+        return e
     out = {
         "metric": "TFLOP/s and % MFMA peak, bf16 fwd/dX/dW at M=4096, 768->3072; "
                   "bit-exact determinism",
@@ -295,13 +374,10 @@ def bench_linear(args, torch, dig, synth):
                      "frac": round(achieved / BF16_PEAK, 4),
                      "traffic": recorded_traffic("linear_768x3072_m4096_traffic.json", dominant),
                      "algorithmic_bytes": bytes_[dominant]},
-        "ops": {name: {"us": round(v * 1e3, 2),
-                       "tflops": round(flops[name] / (v * 1e-3) / 1e12, 2),
-                       "frac_peak": round(flops[name] / (v * 1e-3) / 1e12 / BF16_PEAK, 4)}
-                for name, v in per.items()},
-        "separate_launches": {name: {"us": round(v * 1e3, 2),
-                                     "tflops": round(flops[name] / (v * 1e-3) / 1e12, 2)}
-                              for name, v in sep.items()},
+        "ops": {name: op_entry(name, v) for name, v in per.items()},
+        "separate_launches": {name: op_entry(name, v) for name, v in sep.items()},
+        "sclk": dict(clock, peak_bf16_at_sclk_tflops=round(peak_at_clock, 1)
+                     if peak_at_clock else None),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_linear(d, args.cpu_seconds)
@@ -508,6 +584,55 @@ def bench_bias_grad(args, torch, dig, synth):
                     for k_, v in per.items()}}
 
 
+def bench_scalar(args, torch, dig, synth):
+    """The scalar FMA tier: the bf16 linear 768 -> 48 at M = 4096 (N < 64, so
+    the forward and dW run the scalar tier; dW in 256-row chunks plus the
+    ordered chunk sum) and the f32 linear X[64,128] W[128,256] (forward, dX,
+    dW).  ALU-bound: f32 FMAs on the vector ALUs."""
+    dev = lambda a: torch.from_numpy(a.view(np.int16 if a.dtype == np.uint16 else np.int32)
+                                     .copy()).cuda()
+    keep, ops, flops = [], [], {}
+    for tag, d in (("n48", synth.mlp_up_linear(synth.BF16, n=48, seed=22)),
+                   ("f32", synth.f32_linear_64x128x256())):
+        m, k, n, dt = d["m"], d["k"], d["n"], d["dt"]
+        tdt = torch.int16 if dt != synth.F32 else torch.int32
+        x, w, b, dy = dev(d["x"]), dev(d["w"]), dev(d["b"]), dev(d["dy"])
+        y = torch.empty((m, n), dtype=tdt, device="cuda")
+        dx = torch.empty((m, k), dtype=tdt, device="cuda")
+        dw = torch.empty((k, n), dtype=tdt, device="cuda")
+        wsb = dig.bi_backward_dw_workspace_bytes(m, k, n, dt, 1)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        keep += [x, w, b, dy, y, dx, dw, ws]
+        assert dig.bi_plan(dig.OP_FWD, dt, 1, k, n)[0] == 0  # scalar tier
+        ops.append((f"{tag}_fwd", lambda s, y=y, x=x, w=w, b=b, m=m, k=k, n=n, dt=dt:
+                    dig.check(dig.bi_forward(y, x, w, b, m, k, n, dt, s, 1))))
+        ops.append((f"{tag}_dW", lambda s, dw=dw, x=x, dy=dy, m=m, k=k, n=n, dt=dt, ws=ws, wsb=wsb:
+                    dig.check(dig.bi_backward_dw(dw, x, dy, m, k, n, dt, ws if wsb else None, wsb,
+                                                 s, 1))))
+        if tag == "f32":
+            ops.append((f"{tag}_dX", lambda s, dx=dx, dy=dy, w=w, m=m, k=k, n=n, dt=dt:
+                        dig.check(dig.bi_backward_dx(dx, dy, w, m, k, n, dt, s, 1))))
+        for op in ("fwd", "dW", "dX"):
+            flops[f"{tag}_{op}"] = 2.0 * m * k * n
+    ms, per = timed_steps(torch, ops, args.steps, args.warmup)
+    tf = {name: flops[name] / (v * 1e-3) / 1e12 for name, v in per.items()}
+    main_op = "n48_fwd"
+    return {"metric": "scalar FMA tier TFLOP/s (bf16 linear 768->48 at M=4096, forward)",
+            "value": round(tf[main_op], 3), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "scalar FMA tier: bf16 linear X[4096,768] W[768,48] + b "
+                                   "(forward, chunked dW) and f32 linear X[64,128] W[128,256] + b "
+                                   "(forward, dX, dW)"},
+            "roofline": {"bound": "alu", "kernel": main_op, "achieved": round(tf[main_op], 3),
+                         "peak": F32_VALU_PEAK, "unit": "TFLOP/s",
+                         "frac": round(tf[main_op] / F32_VALU_PEAK, 4), "traffic": None},
+            "ops": {name: {"us": round(v * 1e3, 2), "tflops": round(tf[name], 3),
+                           "frac_alu_peak": round(tf[name] / F32_VALU_PEAK, 4)}
+                    for name, v in per.items()}}
+
+
 # Candidate MFMA tiles per op of the default workload (tile id 40 + base: direct
 # loads; 100 + base: the same with copies spread between MFMAs).  Shapes:
 # 41 256x256 2x2 waves, 42 256x192 2x2, 44 128x128 2x2, 45 128x96 4x1,
@@ -595,7 +720,7 @@ def main():
     fn = {"linear": bench_linear, "fp8": bench_fp8, "fp8_linear": bench_fp8_linear,
           "grouped": bench_grouped,
           "sweep": bench_sweep, "bias_grad": bench_bias_grad, "tiles": bench_tiles,
-          "copy": bench_copy}[args.workload]
+          "copy": bench_copy, "scalar": bench_scalar}[args.workload]
     out = fn(args, torch, dig, synth)
     print(json.dumps(out), flush=True)
 
