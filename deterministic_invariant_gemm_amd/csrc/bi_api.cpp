@@ -163,12 +163,13 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
 // while it gives at least 192 workgroups (three quarters of the CUs), else
 // 128x128 (eight waves) if that does; else the narrow 64x32 tile while one
 // round of it (at most 256 workgroups) covers the batch -- it spreads the
-// stream of B over the most workgroups when M is small -- and beyond that the
-// wider of the two tiles that gives more workgroups (narrow tiles over several
-// rounds re-read B and run 1.5-3x slower).  The tile may follow m because every
-// tile issues the same MFMA sequence per element (the bits do not change); the
-// tier never follows m.  Forced tiles are kept.
-int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols) {
+// stream of B over the most workgroups when M is small; for fp8 up to 32 rows
+// the 32x32 tile with its sixteen-stage ring (more of B in flight) -- and
+// beyond that the wider of the two tiles that gives more workgroups (narrow
+// tiles over several rounds re-read B and run 1.5-3x slower).  The tile may
+// follow m because every tile issues the same MFMA sequence per element (the
+// bits do not change); the tier never follows m.  Forced tiles are kept.
+int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols, bool fp8 = false) {
     if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
     auto wgs = [&](int id) {
         const TileShape *ts = mfma_tile(id);
@@ -176,6 +177,7 @@ int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols) {
     };
     if (wgs(pl.tile) >= 192) return pl.tile;
     if (wgs(115) >= 192) return 115;
+    if (fp8 && m <= 32 && wgs(121) <= 256) return 121;
     if (wgs(120) <= 256) return 120;
     return wgs(pl.tile) >= wgs(115) ? pl.tile : 115;
 }
@@ -462,7 +464,7 @@ int fp8_gemm(void *y, const void *a, const void *bt, const float *a_dequant,
         d.vec_c = aligned8(y) && n % 4 == 0;
         d.scale_a = a_dequant; d.scale_b = b_dequant;
         d.bias = bias;
-        const int tile = direct_tile(d, batch_tile(pl, tc, m, n), m * k, n * k);
+        const int tile = direct_tile(d, batch_tile(pl, tc, m, n, true), m * k, n * k);
         return hip_status(launch_fp8_dl(d, tile, fast, stream));
     }
     // register-staged fp8 kernel: 256x256, 128x128 or 64x64 tiles

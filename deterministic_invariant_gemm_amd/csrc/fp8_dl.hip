@@ -24,7 +24,7 @@ hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, bool fast, hipStream_t 
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (fast) {
         if (tile_id >= 120)
-            return launch_dl_among<DT_E4M3_FAST, true, true, EPI_SCALE, MODE_PLAIN, 20>(p, tile_id, grid, s);
+            return launch_dl_among<DT_E4M3_FAST, true, true, EPI_SCALE, MODE_PLAIN, 20, 21>(p, tile_id, grid, s);
         if (tile_id >= 100)
             return launch_dls_among<DT_E4M3_FAST, true, true, EPI_SCALE, MODE_PLAIN, 11, 12, 15>(
                 p, tile_id, grid, s);
@@ -32,7 +32,7 @@ hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, bool fast, hipStream_t 
             p, tile_id, grid, s);
     }
     if (tile_id >= 120)
-        return launch_dl_among<DT_E4M3, true, true, EPI_SCALE, MODE_PLAIN, 20>(p, tile_id, grid, s);
+        return launch_dl_among<DT_E4M3, true, true, EPI_SCALE, MODE_PLAIN, 20, 21>(p, tile_id, grid, s);
     if (tile_id >= 100)
         return launch_dls_among<DT_E4M3, true, true, EPI_SCALE, MODE_PLAIN, 11, 12, 14, 15>(
             p, tile_id, grid, s);

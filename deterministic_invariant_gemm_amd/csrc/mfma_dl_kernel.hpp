@@ -55,12 +55,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// vmcnt(n * Q) for a run-time n in [0, 7] (a count above 63 is lowered to 63,
+// vmcnt(n * Q) for a run-time n in [0, 15] (a count above 63 is lowered to 63,
 // which only waits longer)
 template <int Q, int I = 0>
 __device__ __forceinline__ void wait_vmcnt_stages(int n) {
     constexpr int C = I * Q < 63 ? I * Q : 63;
-    if constexpr (I >= 7) {
+    if constexpr (I >= 15) {
         wait_vmcnt<C>();
     } else {
         if (n <= I) wait_vmcnt<C>();
@@ -69,12 +69,13 @@ __device__ __forceinline__ void wait_vmcnt_stages(int n) {
 }
 
 // LDS stages (128 bytes of every tile row each) for a BM x BN tile: as many as
-// fit in 160 KB next to the bias row, at most 4 -- at most 8 for small tiles,
-// whose stages are short and which need more of them in flight to keep
-// memory busy (small-M shapes stream the whole of B through a few rows of A)
+// fit in 160 KB next to the bias row, at most 4 -- at most 8 for small tiles
+// and 16 for the 32 x 32 tile, whose stages are short and which need more of
+// them in flight to keep memory busy (small-M shapes stream the whole of B
+// through a few rows of A)
 constexpr int dl_stages(int bm, int bn) {
     const int per = 128 * (bm + bn), avail = 160 * 1024 - 4 * bn;
-    const int cap = bm + bn <= 128 ? 8 : 4;
+    const int cap = bm + bn <= 64 ? 16 : bm + bn <= 128 ? 8 : 4;
     return avail / per >= cap ? cap : avail / per;
 }
 
@@ -293,7 +294,7 @@ struct FragOf<true, R, DT> {
     using type = RcFrag<DT>;
 };
 
-// Tiles of two to four MFMA waves (burst copies) get DL_NPW extra waves that
+// Tiles of one to four MFMA waves (burst copies) get DL_NPW extra waves that
 // issue all the copies: the MFMA waves then only read fragments, multiply and
 // meet at the stage barriers, and the copies of a stage are split over four
 // waves, so four times as many stages can be in flight under each wave's
@@ -302,7 +303,7 @@ struct FragOf<true, R, DT> {
 // of at most 96 accumulator registers (e.g. 64x96); eight-wave tiles keep their
 // copies for the same reason.
 constexpr bool dl_producer(int nw, bool spread, int wtm, int wtn) {
-    return !spread && nw >= 2 && nw <= 4 && (nw < 4 || wtm * wtn / 64 <= 96);
+    return !spread && nw >= 1 && nw <= 4 && (nw < 4 || wtm * wtn / 64 <= 96);
 }
 constexpr int DL_NPW = 4;
 constexpr int dl_threads(int nw, bool spread, int wtm, int wtn) {
@@ -332,7 +333,7 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
     constexpr int SA = 128 * BM, SB = 128 * BN;  // bytes of one stage of A / B
     constexpr int NS = NSV > 0 ? NSV : dl_stages(BM, BN);
-    static_assert(NS >= 2 && NS <= 8, "two to eight stages");
+    static_assert(NS >= 2 && NS <= 16, "two to sixteen stages");
     using TY = DlType<DT>;
     constexpr int KPS = TY::KPS, STEPS = TY::STEPS;
     using Frag = typename TY::Frag;

@@ -668,8 +668,10 @@ template <> struct TileOf<14> { static constexpr int BM = 128, BN = 256, WGM = 2
 template <> struct TileOf<15> { static constexpr int BM = 128, BN = 128, WGM = 2, WGN = 4; };
 // three waves side by side (direct-load kernel only)
 template <> struct TileOf<17> { static constexpr int BM = 96, BN = 96, WGM = 1, WGN = 3; };
-// small-M shapes (direct-load kernel only, tile id 120): many narrow column tiles
+// small-M shapes (direct-load kernel only, tile ids 120 and 121): many narrow
+// column tiles; 121 (one MFMA wave, a sixteen-stage ring) for the fp8 GEMM
 template <> struct TileOf<20> { static constexpr int BM = 64, BN = 32, WGM = 2, WGN = 1; };
+template <> struct TileOf<21> { static constexpr int BM = 32, BN = 32, WGM = 1, WGN = 1; };
 
 template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID>
 hipError_t launch_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {

@@ -27,7 +27,7 @@ const TileShape *mfma_tile(int id) {
         {41, 256, 256}, {42, 256, 192}, {43, 256, 128}, {44, 128, 128}, {45, 128, 96},
         {46, 64, 64},   {47, 128, 256}, {49, 128, 192}, {50, 256, 96},  {51, 256, 192},
         {52, 256, 256}, {53, 256, 128}, {54, 128, 256}, {55, 128, 128},
-        {48, 96, 96},   {57, 96, 96},   {120, 64, 32},
+        {48, 96, 96},   {57, 96, 96},   {120, 64, 32}, {121, 32, 32},
     };
     // ids 100 + i: the direct-load kernel with copies spread between MFMAs
     static const TileShape dls[] = {

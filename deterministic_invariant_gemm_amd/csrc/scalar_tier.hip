@@ -13,8 +13,12 @@
 //
 // Layout: a generic strided formulation C(i,j) = sum_r A(i,r) B(r,j) with
 // A(i,r) = a[i*a_is + r*a_rs] and B(r,j) = b[r*b_rs + j*b_js] covers forward,
-// dX, dW and fp8.  A workgroup of 256 threads computes a 64x64 tile, each thread
-// a 4x4 micro-tile with stride 16, staging 16-deep reduction slices through LDS.
+// dX, dW and fp8.  A workgroup of 256 threads computes a TM x 64 tile (TM = 64,
+// 32 or 16: the tallest that still gives the chip 256 workgroups), each thread
+// a (TM/16) x 4 micro-tile with stride 16, staging 32-deep reduction slices
+// through LDS; the next slice is loaded into registers while the current one is
+// multiplied.  Neither the tile height nor the slice depth changes any
+// element's fmaf chain, so every tile gives the same bits.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -22,14 +26,17 @@ namespace bi {
 
 namespace {
 
-constexpr int ST = 64;  // tile edge
-constexpr int RK = 16;  // reduction slice staged per step
+constexpr int ST = 64;  // tile columns
+constexpr int RK = 32;  // reduction slice staged per step
 
 enum ScalarEpi : int { EPI_ROUND = 0, EPI_PARTIAL = 1, EPI_FP8 = 2 };
 
-template <int DT_IN, int DT_OUT, int EPI>
+template <int DT_IN, int DT_OUT, int EPI, int TM>
 __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
-    __shared__ float As[RK][ST + 1];
+    constexpr int MA = TM / 16;        // output rows per thread
+    constexpr int NA = TM * RK / 256;  // A elements staged per thread per slice
+    constexpr int NB = RK * ST / 256;  // B elements staged per thread per slice
+    __shared__ float As[RK][TM + 1];
     __shared__ float Bs[RK][ST + 1];
 
     const int t = threadIdx.x;
@@ -38,50 +45,74 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
     const int64_t bid = blockIdx.x;
     const int64_t chunk = bid / tiles;
     const int64_t tile = bid % tiles;
-    const int64_t i0 = (tile / p.tiles_j) * ST;
+    const int64_t i0 = (tile / p.tiles_j) * TM;
     const int64_t j0 = (tile % p.tiles_j) * ST;
     const int64_t r_begin = chunk * p.chunk;
     const int64_t r_end = r_begin + p.chunk < p.red ? r_begin + p.chunk : p.red;
 
-    float acc[4][4];
+    float acc[MA][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < MA; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
 
     const bool a_r_contig = p.a_rs == 1;
     const bool b_j_contig = p.b_js == 1;
 
-    for (int64_t rk = r_begin; rk < r_end; rk += RK) {
-        const int valid = (int)(r_end - rk < RK ? r_end - rk : RK);
-        // stage A(i0.., rk..) and B(rk.., j0..) as exact f32
+    // slice at rk into registers (exact f32), zeros outside the matrices and
+    // past the end of the reduction range
+    float ra[NA], rb[NB];
+    auto load = [&](int64_t rk) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < NA; ++q) {
             const int idx = t + 256 * q;
             int row, rr;
-            if (a_r_contig) { row = idx >> 4; rr = idx & 15; }
-            else            { row = idx & 63; rr = idx >> 6; }
+            if (a_r_contig) { row = idx / RK; rr = idx % RK; }
+            else            { row = idx % TM; rr = idx / TM; }
             const int64_t gi = i0 + row, gr = rk + rr;
-            float v = 0.0f;
-            if (gi < p.rows && rr < valid) v = load_elem<DT_IN>(p.a, gi * p.a_is + gr * p.a_rs);
-            As[rr][row] = v;
-            int col;
-            if (b_j_contig) { col = idx & 63; rr = idx >> 6; }
-            else            { col = idx >> 4; rr = idx & 15; }
-            const int64_t gj = j0 + col, gr2 = rk + rr;
-            float w = 0.0f;
-            if (gj < p.cols && rr < valid) w = load_elem<DT_IN>(p.b, gr2 * p.b_rs + gj * p.b_js);
-            Bs[rr][col] = w;
+            ra[q] = (gi < p.rows && gr < r_end) ? load_elem<DT_IN>(p.a, gi * p.a_is + gr * p.a_rs)
+                                                : 0.0f;
         }
-        __syncthreads();
-        for (int rr = 0; rr < valid; ++rr) {
-            float av[4], bv[4];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) av[a] = As[rr][ty + 16 * a];
+        for (int q = 0; q < NB; ++q) {
+            const int idx = t + 256 * q;
+            int col, rr;
+            if (b_j_contig) { col = idx % ST; rr = idx / ST; }
+            else            { col = idx / RK; rr = idx % RK; }
+            const int64_t gj = j0 + col, gr = rk + rr;
+            rb[q] = (gj < p.cols && gr < r_end) ? load_elem<DT_IN>(p.b, gr * p.b_rs + gj * p.b_js)
+                                                : 0.0f;
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int q = 0; q < NA; ++q) {
+            const int idx = t + 256 * q;
+            if (a_r_contig) As[idx % RK][idx / RK] = ra[q];
+            else            As[idx / TM][idx % TM] = ra[q];
+        }
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int idx = t + 256 * q;
+            if (b_j_contig) Bs[idx / ST][idx % ST] = rb[q];
+            else            Bs[idx % RK][idx / RK] = rb[q];
+        }
+    };
+
+    if (r_begin < r_end) load(r_begin);
+    for (int64_t rk = r_begin; rk < r_end; rk += RK) {
+        const int valid = (int)(r_end - rk < RK ? r_end - rk : RK);
+        store();
+        __syncthreads();
+        if (rk + RK < r_end) load(rk + RK);  // in flight while this slice is multiplied
+        for (int rr = 0; rr < valid; ++rr) {
+            float av[MA], bv[4];
+#pragma unroll
+            for (int a = 0; a < MA; ++a) av[a] = As[rr][ty + 16 * a];
 #pragma unroll
             for (int b = 0; b < 4; ++b) bv[b] = Bs[rr][tx + 16 * b];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < MA; ++a)
 #pragma unroll
                 for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(av[a], bv[b], acc[a][b]);
         }
@@ -89,7 +120,7 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
     }
 
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < MA; ++a) {
         const int64_t gi = i0 + ty + 16 * a;
         if (gi >= p.rows) continue;
 #pragma unroll
@@ -205,11 +236,27 @@ __global__ __launch_bounds__(256) void grouped_dweights_scalar_kernel(GroupedSca
 
 hipError_t launch_scalar_gemm(const ScalarGemmArgs &p, int dt_in, int dt_out, int epi,
                               hipStream_t s) {
-    const int64_t grid = p.tiles_i * p.tiles_j * p.nchunks;
+    const int64_t tiles_j = (p.cols + ST - 1) / ST;
+    // the tallest tile that gives at least 256 workgroups (the first that does
+    // not fall below it), 16 rows if none does
+    int tm = 16;
+    for (int cand : {64, 32}) {
+        if ((p.rows + cand - 1) / cand * tiles_j * p.nchunks >= 256) {
+            tm = cand;
+            break;
+        }
+    }
+    ScalarGemmArgs a = p;
+    a.tiles_i = (p.rows + tm - 1) / tm;
+    a.tiles_j = tiles_j;
+    const int64_t grid = a.tiles_i * a.tiles_j * a.nchunks;
     if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
 #define CASE(DI, DO, E)                                                                   \
     if (dt_in == DI && dt_out == DO && epi == E) {                                        \
-        BI_LAUNCH((scalar_gemm_kernel<DI, DO, E>), grid, 256, s, p);                      \
+        if (tm == 64) BI_LAUNCH((scalar_gemm_kernel<DI, DO, E, 64>), grid, 256, s, a);   \
+        else if (tm == 32) BI_LAUNCH((scalar_gemm_kernel<DI, DO, E, 32>), grid, 256, s, a); \
+        else BI_LAUNCH((scalar_gemm_kernel<DI, DO, E, 16>), grid, 256, s, a);            \
         return hipGetLastError();                                                         \
     }
     CASE(DT_F32, DT_F32, EPI_ROUND)

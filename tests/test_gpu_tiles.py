@@ -116,7 +116,7 @@ def test_grouped_tiles_identical(dt):
         print(name, "tiles", sorted(outs))
 
 
-FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 54, 55, 111, 112, 114, 115, 120]
+FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 54, 55, 111, 112, 114, 115, 120, 121]
 
 
 @pytest.mark.parametrize("shape", [(300, 256, 260), (520, 384, 392), (700, 1008, 456),
