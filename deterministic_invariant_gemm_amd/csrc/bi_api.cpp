@@ -60,10 +60,13 @@ constexpr int kTcFp8Fast = 3;
 
 // Testing builds only (BI_TESTING, libbi_testing.so): tc = 16 + id forces MFMA
 // tile `id` when the op is on the MFMA tier (plus kFastBit: the fp8 fast path on
-// tile `id`), for the tile-identity tests and tile tuning.  Tiles do not change
-// results.  Production builds reject every other tc with BI_ERR_UNSUPPORTED.
+// tile `id`; plus (16 + id2) << 16: tile id2 for the dweights of a grouped
+// backward, whose dinput takes `id`), for the tile-identity tests and tile
+// tuning.  Tiles do not change results.  Production builds reject every other
+// tc with BI_ERR_UNSUPPORTED.
 constexpr int kForceBase = 16;
 constexpr int kFastBit = 4096;
+constexpr int kGdwShift = 16;
 #ifdef BI_TESTING
 constexpr bool kForceHook = true;
 #else
@@ -73,9 +76,20 @@ constexpr bool kForceHook = false;
 bool tc_known(int op, int tc) {
     if (tc >= 0 && tc <= kTcRequired) return true;
     if (tc == kTcFp8Fast) return op == OP_FP8;
-    if (kForceHook && (tc & ~kFastBit) >= kForceBase && (tc & ~kFastBit) < kFastBit)
-        return op == OP_FP8 || !(tc & kFastBit);
+    if (kForceHook && tc > 0) {
+        const int lo = tc & (kFastBit - 1), hi = tc >> kGdwShift;
+        const bool hi_ok = hi == 0 || (hi >= kForceBase && (op == OP_GDIN || op == OP_GDW));
+        if (lo >= kForceBase && (tc & ((1 << kGdwShift) - 1) & ~(2 * kFastBit - 1)) == 0 && hi_ok)
+            return op == OP_FP8 || !(tc & kFastBit);
+    }
     return false;
+}
+
+// testing builds: the tile a forcing tc asks for on `op`
+int forced_tile(int op, int tc) {
+    const int hi = tc >> kGdwShift;
+    if (op == OP_GDW && hi) return hi - kForceBase;
+    return (tc & (kFastBit - 1)) - kForceBase;
 }
 
 // fp8 GEMMs: the fp8 matrix instruction was asked for
@@ -115,6 +129,7 @@ int pick_tile(int op, int64_t k, int64_t n, bool fast) {
         return cols >= 128 ? 44 : 46;
     case OP_DX:
         if (cols % 96 == 0 && cols <= 1536) return 45;  // 128x96, four waves along M
+        if (cols >= 2048) return 111;                   // 256x192, eight waves, spread
         return cols >= 128 ? 115 : 46;                  // 128x128, eight waves, spread
     case OP_DW:
         // 96x96 with three MFMA waves side by side along N (one per SIMD on
@@ -126,7 +141,10 @@ int pick_tile(int op, int64_t k, int64_t n, bool fast) {
         // 128x128, four MFMA waves and four copy waves
         return (k >= 128 && n >= 128) ? 44 : 46;
     case OP_GFWD: case OP_GDIN:
-        // 256x192 / 128x128, eight waves, copies spread
+        // dinput over whole 256-column tiles: 256x256, eight waves (its weights
+        // are row-contiguous, read transposed); else 256x192 / 128x128, eight
+        // waves, copies spread
+        if (op == OP_GDIN && cols >= 2048 && cols % 256 == 0) return 52;
         if (cols >= 1024) return 111;
         return cols >= 128 ? 115 : 46;
     case OP_GDW:
@@ -153,7 +171,7 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
         }
     }
     if (kForceHook && pl.tile && tc >= kForceBase) {
-        const int id = (tc & ~kFastBit) - kForceBase;
+        const int id = forced_tile(op, tc);
         if (mfma_tile(id)) pl.tile = id;
     }
     return pl;

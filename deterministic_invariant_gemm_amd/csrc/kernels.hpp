@@ -58,7 +58,7 @@ struct MfmaArgs {
     const uint32_t *offsets;
     int64_t n_experts;
     int64_t b_expert_stride;
-    int64_t seg_tiles;  // tiles_i bound: ceil(rows/BM) + n_experts + 1
+    int64_t seg_tiles;  // tiles_i bound: ceil(rows/BM) + n_experts
     // grouped dweights
     const uint32_t *red_offsets;
     int64_t c_expert_stride;
@@ -69,6 +69,14 @@ struct MfmaArgs {
     // fp8: per-tensor dequantisation scales (device f32 scalars)
     const float *scale_a, *scale_b;
 };
+
+// Row tiles per XCD group of a segment-anchored launch (grouped forward and
+// dinput), and the row tiles its grid covers: seg_tiles rounded up to whole
+// rounds of 8 groups, one group per XCD.
+constexpr int64_t SEG_GROUP = 4;
+__host__ __device__ constexpr int64_t seg_grid_rows(int64_t seg_tiles) {
+    return (seg_tiles + 8 * SEG_GROUP - 1) / (8 * SEG_GROUP) * (8 * SEG_GROUP);
+}
 
 struct Fp8Args {
     const uint8_t *a;   // [m,k]

@@ -330,8 +330,21 @@ __device__ __forceinline__ TileInfo decode_tile_at(const MfmaArgs &p, int t, int
         ti.r_begin = ti.chunk * p.chunk;
         ti.r_end = ti.r_begin + p.chunk < p.red ? ti.r_begin + p.chunk : p.red;
     } else if constexpr (MODE == MODE_SEGMENTS) {
-        const int64_t tt0 = blk / p.tiles_j;
-        ti.col0 = (blk % p.tiles_j) * BN;
+        // Row tiles in groups of SEG_GROUP, each group with all its column
+        // tiles on one XCD (workgroups go to XCD blk % 8), column-major inside
+        // the group, groups dealt to the XCDs in turn: a group's row tiles of
+        // the input are fetched once into that XCD's L2 and shared by its
+        // column tiles, and the tiles past the last segment, whose count only
+        // the device knows, skip evenly on every XCD.  The grid covers
+        // seg_tiles rounded up to whole rounds of 8 groups (seg_grid_rows).
+        const int64_t xcd = blk % 8, j = blk / 8, per = SEG_GROUP * p.tiles_j;
+        const int64_t grp = (j / per) * 8 + xcd, q = j % per;
+        const int64_t tt0 = grp * SEG_GROUP + q % SEG_GROUP;
+        ti.col0 = (q / SEG_GROUP) * BN;
+        if (tt0 >= p.seg_tiles) {
+            ti.skip = true;
+            return ti;
+        }
         int64_t tt = tt0;
         int64_t x = 0;
         ti.row0 = -1;
@@ -368,11 +381,19 @@ __device__ __forceinline__ TileInfo decode_tile_at(const MfmaArgs &p, int t, int
         ti.r_begin = 0;
         ti.r_end = p.red;
     } else {  // MODE_EXPERT_RED
+        // consecutive tiles (one expert's, in groups of 4 row tiles,
+        // column-major inside a group) on one XCD, as for MODE_PLAIN
         const int64_t per_x = p.tiles_i * p.tiles_j;
-        const int64_t x = blk / per_x;
-        const int64_t tile = blk % per_x;
-        ti.row0 = (tile / p.tiles_j) * BM;
-        ti.col0 = (tile % p.tiles_j) * BN;
+        const int64_t bid = xcd_remap(blk, nblk);
+        const int64_t x = bid / per_x;
+        const int64_t tile = bid % per_x;
+        constexpr int64_t GROUP = 4;
+        const int64_t per_group = GROUP * p.tiles_j;
+        const int64_t g = tile / per_group, first = g * GROUP;
+        const int64_t gsz = p.tiles_i - first < GROUP ? p.tiles_i - first : GROUP;
+        const int64_t in_g = tile % per_group;
+        ti.row0 = (first + in_g % gsz) * BM;
+        ti.col0 = (in_g / gsz) * BN;
         ti.row_end = p.rows;
         ti.r_end = p.red_offsets[x + 1];
         ti.r_begin = p.red_offsets[x];

@@ -47,7 +47,7 @@ hipError_t launch_mfma_gemm(const MfmaArgs &p, int tile_id, int dt, int layout, 
                             hipStream_t s) {
     const bool seg = p.offsets != nullptr, red = p.red_offsets != nullptr;
     int64_t grid;
-    if (seg) grid = p.seg_tiles * p.tiles_j;
+    if (seg) grid = seg_grid_rows(p.seg_tiles) * p.tiles_j;
     else if (red) grid = p.n_experts * p.tiles_i * p.tiles_j;
     else grid = p.tiles_i * p.tiles_j * p.nchunks;
     if (grid <= 0) return hipSuccess;
