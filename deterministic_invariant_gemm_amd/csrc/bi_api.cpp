@@ -179,15 +179,17 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
 
 // Tile for the batch at hand (forward, dX, fp8): the default tile of (k, n)
 // while it gives at least 192 workgroups (three quarters of the CUs), else
-// 128x128 (eight waves) if that does; else the narrow 64x32 tile while one
-// round of it (at most 256 workgroups) covers the batch -- it spreads the
-// stream of B over the most workgroups when M is small; for fp8 up to 32 rows
-// the 32x32 tile with its sixteen-stage ring (more of B in flight) -- and
-// beyond that the wider of the two tiles that gives more workgroups (narrow
-// tiles over several rounds re-read B and run 1.5-3x slower).  The tile may
-// follow m because every tile issues the same MFMA sequence per element (the
-// bits do not change); the tier never follows m.  Forced tiles are kept.
-int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols, bool fp8 = false) {
+// 128x128 (eight waves) if that does.  Smaller batches stream B through a few
+// rows of A: one round (at most 256 workgroups) of a narrow tile spreads that
+// stream over the most workgroups, and their time goes mostly to the fixed
+// cost of each LDS stage, so the forward and fp8 take the deep-stage variants
+// (32x32 with 512-byte stage rows while it fits one round, else 64x32 with
+// 256-byte rows) and dX the 64x32 tile; beyond that the wider of the two tiles
+// that gives more workgroups (narrow tiles over several rounds re-read B and
+// run 1.5-3x slower).  The tile may follow m because every tile issues the same
+// MFMA sequence per element (the bits do not change); the tier never follows
+// m.  Forced tiles are kept.
+int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols, bool deep) {
     if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
     auto wgs = [&](int id) {
         const TileShape *ts = mfma_tile(id);
@@ -195,7 +197,8 @@ int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols, bool fp8 = false
     };
     if (wgs(pl.tile) >= 192) return pl.tile;
     if (wgs(115) >= 192) return 115;
-    if (fp8 && m <= 32 && wgs(121) <= 256) return 121;
+    if (deep && wgs(321) <= 256) return 321;
+    if (deep && wgs(220) <= 256) return 220;
     if (wgs(120) <= 256) return 120;
     return wgs(pl.tile) >= wgs(115) ? pl.tile : 115;
 }
@@ -205,7 +208,7 @@ int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.ch
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
 // The tile that runs, its operand extents and its grid.  The direct-load family
-// (ids 40 + base, 100 + base) needs 16-byte-aligned rows whose length is a
+// (ids 40, 100, 200 and 300 + base) needs 16-byte-aligned rows whose length is a
 // multiple of 8 elements and operands below 2^30 bytes; otherwise the register-staged kernel
 // runs on the tile every op instantiates that is closest in shape: 256x256,
 // 128x128 or 64x64 (same bits either way).  The grid (tiles_i or seg_tiles,
@@ -309,7 +312,7 @@ int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t 
     a.vec_a = aligned16(x) && k % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(y) && n % 4 == 0;
-    const int tile = direct_tile(a, batch_tile(pl, tc, m, n), 2 * m * k, 2 * k * n);
+    const int tile = direct_tile(a, batch_tile(pl, tc, m, n, true), 2 * m * k, 2 * k * n);
     return hip_status(launch_mfma_gemm(a, tile, dtype, /*layout A rc, B strided*/ 1, 0, stream));
 }
 
@@ -333,7 +336,7 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
         return hip_status(launch_scalar_gemm(a, dtype, dtype, 0, stream));
     }
     MfmaArgs a{};
-    const int tile = dx_mfma_args(a, dx, dy, w, m, k, n, batch_tile(pl, tc, m, k));
+    const int tile = dx_mfma_args(a, dx, dy, w, m, k, n, batch_tile(pl, tc, m, k, false));
     return hip_status(launch_mfma_gemm(a, tile, dtype, /*both rc*/ 3, 0, stream));
 }
 
@@ -410,7 +413,7 @@ int bi_linear_backward(void *dx, void *dw, const void *dy, const void *x, const 
         return BI_ERR_WORKSPACE;
     if (m > 0 && k > 0 && n > 0 && px.tile != 0 && pw.tile != 0 && chunks == 1) {
         MfmaArgs ax{}, aw{};
-        const int tx = dx_mfma_args(ax, dx, dy, w, m, k, n, batch_tile(px, tc, m, k));
+        const int tx = dx_mfma_args(ax, dx, dy, w, m, k, n, batch_tile(px, tc, m, k, false));
         const int tw = dw_mfma_args(aw, dw, x, dy, m, k, n, pw, 1, nullptr);
         // one launch pays off while the dX tiles alone fill most CUs; with fewer,
         // the dX tiles (on the critical path, with the shorter ring of the

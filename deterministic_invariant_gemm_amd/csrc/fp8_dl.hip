@@ -23,6 +23,10 @@ hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, bool fast, hipStream_t 
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (fast) {
+        if (tile_id >= 300)
+            return launch_dld_among<DT_E4M3_FAST, true, true, EPI_SCALE, MODE_PLAIN, 512, 21>(p, tile_id, grid, s);
+        if (tile_id >= 200)
+            return launch_dld_among<DT_E4M3_FAST, true, true, EPI_SCALE, MODE_PLAIN, 256, 20>(p, tile_id, grid, s);
         if (tile_id >= 120)
             return launch_dl_among<DT_E4M3_FAST, true, true, EPI_SCALE, MODE_PLAIN, 20, 21>(p, tile_id, grid, s);
         if (tile_id >= 100)
@@ -31,6 +35,10 @@ hipError_t launch_fp8_dl(const MfmaArgs &p, int tile_id, bool fast, hipStream_t 
         return launch_dl_among<DT_E4M3_FAST, true, true, EPI_SCALE, MODE_PLAIN, 1, 4, 6, 11, 12, 15>(
             p, tile_id, grid, s);
     }
+    if (tile_id >= 300)
+        return launch_dld_among<DT_E4M3, true, true, EPI_SCALE, MODE_PLAIN, 512, 21>(p, tile_id, grid, s);
+    if (tile_id >= 200)
+        return launch_dld_among<DT_E4M3, true, true, EPI_SCALE, MODE_PLAIN, 256, 20>(p, tile_id, grid, s);
     if (tile_id >= 120)
         return launch_dl_among<DT_E4M3, true, true, EPI_SCALE, MODE_PLAIN, 20, 21>(p, tile_id, grid, s);
     if (tile_id >= 100)

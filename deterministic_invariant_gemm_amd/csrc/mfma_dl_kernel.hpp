@@ -68,13 +68,14 @@ __device__ __forceinline__ void wait_vmcnt_stages(int n) {
     }
 }
 
-// LDS stages (128 bytes of every tile row each) for a BM x BN tile: as many as
-// fit in 160 KB next to the bias row, at most 4 -- at most 8 for small tiles
-// and 16 for the 32 x 32 tile, whose stages are short and which need more of
-// them in flight to keep memory busy (small-M shapes stream the whole of B
-// through a few rows of A)
-constexpr int dl_stages(int bm, int bn) {
-    const int per = 128 * (bm + bn), avail = 160 * 1024 - 4 * bn;
+// LDS stages (sr = 128 bytes of every tile row each, or 256 for the
+// double-depth variants of small tiles) for a BM x BN tile: as many as fit in
+// 160 KB next to the bias row, at most 4 -- at most 8 for small tiles and 16
+// for the 32 x 32 tile, whose stages are short and which need more of them in
+// flight to keep memory busy (small-M shapes stream the whole of B through a
+// few rows of A)
+constexpr int dl_stages(int bm, int bn, int sr = 128) {
+    const int per = sr * (bm + bn), avail = 160 * 1024 - 4 * bn;
     const int cap = bm + bn <= 64 ? 16 : bm + bn <= 128 ? 8 : 4;
     return avail / per >= cap ? cap : avail / per;
 }
@@ -104,11 +105,17 @@ __device__ __forceinline__ void lds_dma16(i32x4 rs, uint32_t voff, uint32_t lds_
 }
 #pragma clang diagnostic pop
 
-// XOR of the 16-byte chunk index inside a row of a reduction-contiguous tile.
-// A fragment read takes one chunk from each of 32 consecutive rows; any 8 (and
-// any 16) of those rows that the LDS serves together land on distinct banks.
-// Depends on row & 15 only, so it is a per-lane constant for fragment reads.
-__device__ __forceinline__ int rc_xor(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+// XOR of the 16-byte chunk index inside a row of a reduction-contiguous tile
+// (SR bytes per stage row).  A fragment read takes one chunk from each of 32
+// consecutive rows; any 8 (and any 16) of those rows that the LDS serves
+// together land on distinct banks (256-byte rows all start on bank 0, so the
+// chunk turns with every row).  Depends on row & 15 only, so it is a per-lane
+// constant for fragment reads.
+template <int SR = 128>
+__device__ __forceinline__ int rc_xor(int row) {
+    if constexpr (SR >= 256) return row & 15;
+    else return (row ^ ((row >> 3) & 1)) & 7;
+}
 
 // XOR of the 16-byte chunk index inside reduction row k of a row-contiguous
 // tile of R columns.  A transposed fragment read takes 32 bytes (16 lanes) or
@@ -128,23 +135,24 @@ __device__ __forceinline__ int rs_xor(int k) {
     else return 0;
 }
 
-// Per data type: bytes per element, reduction values per LDS stage (one
-// 128-byte row segment of a reduction-contiguous tile), MFMA steps per stage
-// and the MFMA fragment of one lane as read from LDS.
+// Per data type: bytes per element, reduction values per MFMA step and the
+// MFMA fragment of one lane as read from LDS; a stage row of SR bytes (a
+// reduction-contiguous tile row; SR / 2 reduction rows of a row-contiguous one)
+// holds KPS = SR / ESZ reduction values, STEPS = KPS / STEPK steps.
 template <int DT>
 struct DlType {  // bf16 / f16: v_mfma_f32_32x32x16_{bf16,f16}, 16 values per step
-    static constexpr int ESZ = 2, KPS = 64, STEPS = 4;
+    static constexpr int ESZ = 2, STEPK = 16;
     using Frag = u32x4;
 };
 template <>
 struct DlType<DT_E4M3> {  // fp8 e4m3 codes widened exactly to bf16:
     // v_mfma_f32_32x32x16_bf16, 16 values per step, 8 codes (8 bytes) per lane
-    static constexpr int ESZ = 1, KPS = 128, STEPS = 8;
+    static constexpr int ESZ = 1, STEPK = 16;
     using Frag = u32x2;
 };
 template <>
 struct DlType<DT_E4M3_FAST> {  // fp8 e4m3: v_mfma_scale_f32_32x32x64_f8f6f4, 64 per step
-    static constexpr int ESZ = 1, KPS = 128, STEPS = 2;
+    static constexpr int ESZ = 1, STEPK = 64;
     using Frag = i32x8;
 };
 
@@ -165,13 +173,14 @@ __device__ __forceinline__ u32x4 dl_operand(u32x2 f) { return e4m3x8_to_bf16x8(f
 __device__ __forceinline__ u32x4 dl_operand(u32x4 f) { return f; }
 __device__ __forceinline__ i32x8 dl_operand(i32x8 f) { return f; }
 
-// Global -> LDS copy of one operand tile per stage (128 bytes of each row or,
-// row-contiguous, 64 reduction rows): R/8 instructions of 1 KB, spread evenly
-// over the NW waves.  ESZ: bytes per element.
-template <int R, bool RC, int NW, int ESZ = 2>
+// Global -> LDS copy of one operand tile per stage (SR bytes of each row or,
+// row-contiguous, SR / 2 reduction rows): R * SR / 1024 instructions of 1 KB,
+// spread evenly over the NW waves.  ESZ: bytes per element.
+template <int R, bool RC, int NW, int ESZ = 2, int SR = 128>
 struct DLoad {
-    static constexpr int NQ = R / 8 / NW;
-    static_assert(NQ >= 1 && NQ * 8 * NW == R, "tile rows must spread evenly over the waves");
+    static constexpr int NQ = R * SR / 1024 / NW;
+    static constexpr int CPR = SR / 16;  // 16-byte chunks per reduction-contiguous row
+    static_assert(NQ >= 1 && NQ * 1024 * NW == R * SR, "tile rows must spread evenly over the waves");
     uint32_t off[NQ];  // byte offset of this lane's chunk in stage 0
     int kin[NQ];       // reduction index of the chunk within its stage
     uint32_t sstride;  // bytes between consecutive stages
@@ -183,7 +192,7 @@ struct DLoad {
         for (int p = 0; p < NQ; ++p) {
             const int s = 64 * (wave + NW * p) + lane;  // chunk slot within the stage
             if constexpr (RC) {
-                const int row = s >> 3, kg = (s & 7) ^ rc_xor(row);
+                const int row = s / CPR, kg = (s % CPR) ^ rc_xor<SR>(row);
                 off[p] = (uint32_t)(((o0 + row) * ld + r_begin) * ESZ + 16 * kg);
                 kin[p] = (16 / ESZ) * kg;
             } else {
@@ -193,7 +202,7 @@ struct DLoad {
                 kin[p] = k;
             }
         }
-        sstride = RC ? 128u : (uint32_t)(64 * ld * 2);
+        sstride = RC ? (uint32_t)SR : (uint32_t)(SR / 2 * ld * 2);
     }
 
     // copy stage s into `stage`; with MASK, chunks at reduction index >= rem
@@ -218,15 +227,15 @@ struct DLoad {
     }
 };
 
-// MFMA fragment reads from a reduction-contiguous stage ([rows][128 bytes]).
+// MFMA fragment reads from a reduction-contiguous stage ([rows][SR bytes]).
 // 16-bit: lane l takes 16 bytes (8 values) of row l & 31 at value 8 * (l >> 5)
 // of the 16-deep step; e4m3 (exact path): 8 bytes (8 codes) at value
 // 8 * (l >> 5) of the 16-deep step; e4m3 (fast path): 32 bytes (two chunks)
 // at value 32 * (l >> 5) of the 64-deep step.
-template <int DT>
+template <int DT, int SR = 128>
 struct RcFrag {
     static constexpr int CH = DT == DT_E4M3_FAST ? 2 : 1;  // reads per lane and step
-    static constexpr int STEPS = DlType<DT>::STEPS;         // steps per stage
+    static constexpr int STEPS = SR / DlType<DT>::ESZ / DlType<DT>::STEPK;  // steps per stage
     uint32_t koff[STEPS][CH];  // lane's byte offsets inside a 32-row block
 
     __device__ __forceinline__ void init(int lane) {
@@ -236,15 +245,15 @@ struct RcFrag {
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 if constexpr (DT == DT_E4M3)  // chunk kk holds the step, half hi the lane's
-                    koff[kk][c] = (uint32_t)(r * 128 + 16 * (kk ^ rc_xor(r)) + 8 * hi);
+                    koff[kk][c] = (uint32_t)(r * SR + 16 * (kk ^ rc_xor<SR>(r)) + 8 * hi);
                 else
                     koff[kk][c] =
-                        (uint32_t)(r * 128 + 16 * ((2 * CH * kk + CH * hi + c) ^ rc_xor(r)));
+                        (uint32_t)(r * SR + 16 * ((2 * CH * kk + CH * hi + c) ^ rc_xor<SR>(r)));
             }
     }
     // rows base .. base+31 (base a multiple of 32)
     __device__ __forceinline__ auto read(const BI_LDS char *stage, int base, int kk) const {
-        const BI_LDS char *row = stage + base * 128;
+        const BI_LDS char *row = stage + base * SR;
         if constexpr (DT == DT_E4M3) {
             return *reinterpret_cast<const BI_LDS u32x2 *>(row + koff[kk][0]);
         } else if constexpr (CH == 1) {
@@ -285,13 +294,13 @@ struct RsFrag {
     }
 };
 
-template <bool RC, int R, int DT>
+template <bool RC, int R, int DT, int SR>
 struct FragOf {
     using type = RsFrag<R>;
 };
-template <int R, int DT>
-struct FragOf<true, R, DT> {
-    using type = RcFrag<DT>;
+template <int R, int DT, int SR>
+struct FragOf<true, R, DT, SR> {
+    using type = RcFrag<DT, SR>;
 };
 
 // Tiles of one to four MFMA waves (burst copies) get DL_NPW extra waves that
@@ -310,10 +319,10 @@ constexpr int dl_threads(int nw, bool spread, int wtm, int wtn) {
     return 64 * (nw + (dl_producer(nw, spread, wtm, wtn) ? DL_NPW : 0));
 }
 
-// LDS ring bytes of a BM x BN tile with ns stages (0: dl_stages); the
-// epilogue reuses them
-constexpr int dl_lds_bytes(int bm, int bn, int ns = 0) {
-    return (ns > 0 ? ns : dl_stages(bm, bn)) * 128 * (bm + bn);
+// LDS ring bytes of a BM x BN tile with ns stages (0: dl_stages) of sr-byte
+// rows; the epilogue reuses them
+constexpr int dl_lds_bytes(int bm, int bn, int ns = 0, int sr = 128) {
+    return (ns > 0 ? ns : dl_stages(bm, bn, sr)) * sr * (bm + bn);
 }
 
 // One workgroup's tile: workgroup `blk` of `nblk`, LDS ring `lds_raw`
@@ -321,7 +330,7 @@ constexpr int dl_lds_bytes(int bm, int bn, int ns = 0) {
 // caller, threadIdx.x below dl_threads(...).  NSV: ring stages (0: as many as
 // fit, dl_stages); fewer leave room for a second workgroup on the CU.
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
-          bool SPREAD, int NSV = 0>
+          bool SPREAD, int NSV = 0, int SR = 128>
 __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float *lds_bias,
                                         int64_t blk, int64_t nblk) {
     constexpr int NW = WGM * WGN;
@@ -331,11 +340,13 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     static_assert(FM * 32 == WTM && FN * 32 == WTN, "wave tile must be a multiple of 32");
-    constexpr int SA = 128 * BM, SB = 128 * BN;  // bytes of one stage of A / B
-    constexpr int NS = NSV > 0 ? NSV : dl_stages(BM, BN);
+    constexpr int SA = SR * BM, SB = SR * BN;  // bytes of one stage of A / B
+    constexpr int NS = NSV > 0 ? NSV : dl_stages(BM, BN, SR);
     static_assert(NS >= 2 && NS <= 16, "two to sixteen stages");
     using TY = DlType<DT>;
-    constexpr int KPS = TY::KPS, STEPS = TY::STEPS;
+    constexpr int KPS = SR / TY::ESZ, STEPS = KPS / TY::STEPK;
+    static_assert(SR == 128 || SR == 256 || SR == 512, "stage rows of 128, 256 or 512 bytes");
+    static_assert(STEPS >= 2, "two or more MFMA steps per stage");
     using Frag = typename TY::Frag;
     constexpr bool FP8 = DT == DT_E4M3 || DT == DT_E4M3_FAST;
     static_assert(!FP8 || (A_RC && B_RC), "fp8 operands are reduction-contiguous");
@@ -358,14 +369,14 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
 
     const i32x4 rsa = make_rsrc(p.a, p.a_bytes);
     const i32x4 rsb = make_rsrc(static_cast<const uint16_t *>(p.b) + ti.b_off, p.b_bytes - 2 * ti.b_off);
-    using LA = DLoad<BM, A_RC, NWC, TY::ESZ>;
-    using LB = DLoad<BN, B_RC, NWC, TY::ESZ>;
+    using LA = DLoad<BM, A_RC, NWC, TY::ESZ, SR>;
+    using LB = DLoad<BN, B_RC, NWC, TY::ESZ, SR>;
     LA la;
     LB lb;
     la.init(p.lda, row0, r_begin, cwave, lane);
     lb.init(p.ldb, col0, r_begin, cwave, lane);
-    typename FragOf<A_RC, BM, DT>::type ra;
-    typename FragOf<B_RC, BN, DT>::type rb;
+    typename FragOf<A_RC, BM, DT, SR>::type ra;
+    typename FragOf<B_RC, BN, DT, SR>::type rb;
     ra.init(lane);
     rb.init(lane);
 
@@ -562,21 +573,21 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
 }
 
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
-          bool SPREAD>
+          bool SPREAD, int SR = 128>
 __global__ __launch_bounds__(dl_threads(WGM * WGN, SPREAD, BM / WGM, BN / WGN)) void mfma_dl_kernel(
     MfmaArgs p) {
     // NS stages of [A | B]; reused by the epilogue
-    __shared__ __align__(1024) char lds_raw[dl_lds_bytes(BM, BN)];
+    __shared__ __align__(1024) char lds_raw[dl_lds_bytes(BM, BN, 0, SR)];
     __shared__ __align__(16) float lds_bias[BN];
-    dl_body<DT, A_RC, B_RC, BM, BN, WGM, WGN, EPI, MODE, SPREAD>(p, lds_raw, lds_bias, blockIdx.x,
-                                                                 gridDim.x);
+    dl_body<DT, A_RC, B_RC, BM, BN, WGM, WGN, EPI, MODE, SPREAD, 0, SR>(p, lds_raw, lds_bias,
+                                                                         blockIdx.x, gridDim.x);
 }
 
-template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID, bool SPREAD>
+template <int DT, bool ARC, bool BRC, int EPI, int MODE, int ID, bool SPREAD, int SR = 128>
 hipError_t launch_dl_tile(const MfmaArgs &p, int64_t grid, hipStream_t s) {
     using T = TileOf<ID>;
     hipLaunchKernelGGL(
-        (mfma_dl_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE, SPREAD>),
+        (mfma_dl_kernel<DT, ARC, BRC, T::BM, T::BN, T::WGM, T::WGN, EPI, MODE, SPREAD, SR>),
         dim3(grid), dim3(dl_threads(T::WGM * T::WGN, SPREAD, T::BM / T::WGM, T::BN / T::WGN)), 0, s, p);
     return hipGetLastError();
 }
@@ -604,6 +615,24 @@ hipError_t launch_dls_among(const MfmaArgs &p, int tile_id, int64_t grid, hipStr
     hipError_t r = hipErrorInvalidValue;
     ((tile_id == 100 + IDS
           ? (void)(r = launch_dl_tile<DT, ARC, BRC, EPI, MODE, IDS, true>(p, grid, s))
+          : (void)0),
+     ...);
+    return r;
+}
+
+// tile ids 200 + base id (SR = 256) and 300 + base id (SR = 512), bases
+// 20..39: the direct-load kernel with double- and quadruple-depth stages (256-
+// and 512-byte stage rows), a half and a quarter as many stage barriers per
+// reduction -- for the small tiles of small batches, whose time per stage is
+// mostly fixed cost
+template <int DT, bool ARC, bool BRC, int EPI, int MODE, int SR, int... IDS>
+hipError_t launch_dld_among(const MfmaArgs &p, int tile_id, int64_t grid, hipStream_t s) {
+    static_assert(((IDS >= 20) && ...), "deep-stage variants exist for bases 20..39");
+    static_assert(SR == 256 || SR == 512, "double- or quadruple-depth stages");
+    constexpr int OFF = SR == 256 ? 200 : 300;
+    hipError_t r = hipErrorInvalidValue;
+    ((tile_id == OFF + IDS
+          ? (void)(r = launch_dl_tile<DT, ARC, BRC, EPI, MODE, IDS, false, SR>(p, grid, s))
           : (void)0),
      ...);
     return r;

@@ -6,6 +6,16 @@ namespace bi {
 hipError_t launch_mfma_fwd(const MfmaArgs &p, int tile_id, int dt, int epi, int64_t grid, hipStream_t s) {
     using namespace mfma;
     (void)epi;
+    if (tile_id >= 300) {
+        if (dt == DT_BF16) return launch_dld_among<DT_BF16, true, false, EPI_ROUND, MODE_PLAIN, 512, 21>(p, tile_id, grid, s);
+        if (dt == DT_F16) return launch_dld_among<DT_F16, true, false, EPI_ROUND, MODE_PLAIN, 512, 21>(p, tile_id, grid, s);
+        return hipErrorInvalidValue;
+    }
+    if (tile_id >= 200) {
+        if (dt == DT_BF16) return launch_dld_among<DT_BF16, true, false, EPI_ROUND, MODE_PLAIN, 256, 20>(p, tile_id, grid, s);
+        if (dt == DT_F16) return launch_dld_among<DT_F16, true, false, EPI_ROUND, MODE_PLAIN, 256, 20>(p, tile_id, grid, s);
+        return hipErrorInvalidValue;
+    }
     if (tile_id >= 120) {
         if (dt == DT_BF16) return launch_dl_among<DT_BF16, true, false, EPI_ROUND, MODE_PLAIN, 20>(p, tile_id, grid, s);
         if (dt == DT_F16) return launch_dl_among<DT_F16, true, false, EPI_ROUND, MODE_PLAIN, 20>(p, tile_id, grid, s);

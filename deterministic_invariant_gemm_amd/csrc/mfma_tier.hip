@@ -34,6 +34,10 @@ const TileShape *mfma_tile(int id) {
         {104, 128, 128}, {105, 128, 96}, {108, 96, 96}, {111, 256, 192}, {112, 256, 256},
         {114, 128, 256}, {115, 128, 128},
     };
+    // ids 200 + i / 300 + i: the direct-load kernel with double- / quadruple-depth stages
+    static const TileShape dld[] = {{220, 64, 32}, {321, 32, 32}};
+    for (const TileShape &s : dld)
+        if (s.id == id) return &s;
     for (const TileShape &s : dls)
         if (s.id == id) return &s;
     for (const TileShape &s : shapes)

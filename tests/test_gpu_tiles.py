@@ -18,7 +18,7 @@ from parity import check, dev, empty, host
 pytestmark = pytest.mark.gpu
 
 TILE_IDS = (list(range(1, 16)) + list(range(41, 58))
-            + [104, 105, 108, 111, 112, 114, 115, 120])
+            + [104, 105, 108, 111, 112, 114, 115, 120, 220, 321])
 
 
 def run_all(fn, ids=TILE_IDS, base=16):
@@ -116,7 +116,7 @@ def test_grouped_tiles_identical(dt):
         print(name, "tiles", sorted(outs))
 
 
-FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 54, 55, 111, 112, 114, 115, 120, 121]
+FP8_TILE_IDS = [1, 4, 6, 41, 44, 46, 51, 52, 54, 55, 111, 112, 114, 115, 120, 121, 220, 321]
 
 
 @pytest.mark.parametrize("shape", [(300, 256, 260), (520, 384, 392), (700, 1008, 456),
