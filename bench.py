@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--traffic-record", nargs=4, metavar=("RD", "WR", "COPY_RD", "COPY_WR"),
+                    help="no GPU: write the HBM traffic record of the default workload from "
+                         "four rocprofv3 --pmc output folders (read and write request "
+                         "counters of the default workload and of --workload copy)")
     return ap.parse_args()
 
 
@@ -77,8 +81,8 @@ def kernel_source_hash() -> str:
 
 def recorded_traffic(record: str, op: str):
     """HBM bytes per launch of `op` from the committed rocprofv3 counter record
-    (FETCH_SIZE and WRITE_SIZE, calibrated against a copy of known size), or
-    None if the record is missing or the kernels changed since it was taken."""
+    (memory-side read and write requests counted by size), or None if the
+    record is missing or the kernels changed since it was taken."""
     path = os.path.join(ROOT, "profiles", record)
     try:
         with open(path) as f:
@@ -88,6 +92,118 @@ def recorded_traffic(record: str, op: str):
     if rec.get("source_hash") != kernel_source_hash() or op not in rec.get("kernels", {}):
         return None
     return int(rec["kernels"][op]["traffic_bytes"])
+
+
+TRAFFIC_RECORD = "linear_768x3072_m4096_traffic"
+# kernels of the default workload, by name: the step's forward and shared
+# backward, and dX and dW in launches of their own
+LINEAR_KERNELS = {"fwd": "mfma_dl_kernel<1, true, false,", "bwd": "mfma_dl_backward_kernel",
+                  "dX": "mfma_dl_kernel<1, true, true,", "dW": "mfma_dl_kernel<1, false, false,"}
+COPY_BYTES = 512 << 20  # --workload copy
+
+
+def counter_means(folder: str) -> dict:
+    """{kernel name: {counter: mean per dispatch, "dispatches": n}} from the
+    csv files a rocprofv3 --pmc run wrote under `folder` (each counter summed
+    over its hardware instances within a dispatch)."""
+    import csv
+    import glob
+    disp = {}
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"),
+                              recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                d = disp.setdefault((f, r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    per = {}
+    for d in disp.values():
+        acc = per.setdefault(d.pop("kernel"), {})
+        for c, v in d.items():
+            acc.setdefault(c, []).append(v)
+    return {k: dict({c: sum(v) / len(v) for c, v in cs.items()},
+                    dispatches=max(len(v) for v in cs.values()))
+            for k, cs in per.items()}
+
+
+def request_bytes(rd: dict, wr: dict):
+    """HBM bytes (read, written) of one dispatch from the memory-side request
+    counters: each read request moves 32, 64 or 128 bytes as its counter says;
+    a write request moves 64 bytes (TCC_EA0_WRREQ_64B) or 32 bytes (the rest
+    of TCC_EA0_WRREQ)."""
+    read = (32 * rd.get("TCC_EA0_RDREQ_32B", 0.0) + 64 * rd.get("TCC_EA0_RDREQ_64B", 0.0)
+            + 128 * rd.get("TCC_EA0_RDREQ_128B", 0.0))
+    w64 = wr.get("TCC_EA0_WRREQ_64B", 0.0)
+    write = 64 * w64 + 32 * (wr.get("TCC_EA0_WRREQ", w64) - w64)
+    return read, write
+
+
+def write_traffic_record(rd_dir: str, wr_dir: str, copy_rd_dir: str, copy_wr_dir: str):
+    """Traffic record of the default workload (profiles/<TRAFFIC_RECORD>.json,
+    read back by recorded_traffic, and a markdown summary beside it) from the
+    four counter runs; the copy of COPY_BYTES checks the byte accounting."""
+    rd, wr = counter_means(rd_dir), counter_means(wr_dir)
+    crd, cwr = counter_means(copy_rd_dir), counter_means(copy_wr_dir)
+    copy = [k for k in crd if "copyBuffer" in k]
+    if len(copy) != 1 or copy[0] not in cwr:
+        raise SystemExit("the copy runs hold no single copy kernel")
+    c_read, c_write = request_bytes(crd[copy[0]], cwr[copy[0]])
+    m, k, n = 4096, 768, 3072
+    alg = {"fwd": (2 * (m * k + k * n + n), 2 * m * n),
+           "bwd": (2 * (m * n + k * n + m * k), 2 * (m * k + k * n)),
+           "dX": (2 * (m * n + k * n), 2 * m * k), "dW": (2 * (m * k + m * n), 2 * k * n)}
+    kernels = {}
+    for op, pat in LINEAR_KERNELS.items():
+        names = [kn for kn in rd if pat in kn]
+        if len(names) != 1 or names[0] not in wr:
+            raise SystemExit(f"{op}: expected one kernel matching {pat!r}, found {names}")
+        r, w = request_bytes(rd[names[0]], wr[names[0]])
+        short = names[0].replace("(anonymous namespace)::", "").split("(")[0]
+        short = short.replace("void bi::mfma::", "").replace("void bi::", "")
+        kernels[op] = {"kernel": short, "read_bytes": r, "write_bytes": w, "traffic_bytes": r + w,
+                       "algorithmic_read": alg[op][0], "algorithmic_write": alg[op][1],
+                       "dispatches": rd[names[0]]["dispatches"]}
+    rec = {"source_hash": kernel_source_hash(),
+           "method": "HBM bytes per dispatch = 32, 64, 128 x TCC_EA0_RDREQ_{32B,64B,128B} "
+                     "read + 64 x TCC_EA0_WRREQ_64B + 32 x (TCC_EA0_WRREQ - "
+                     "TCC_EA0_WRREQ_64B) written, each counter summed over its instances",
+           "copy_check": {"bytes": COPY_BYTES, "read_bytes": c_read, "write_bytes": c_write},
+           "kernels": kernels}
+    base = os.path.join(ROOT, "profiles", TRAFFIC_RECORD)
+    with open(base + ".json", "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- "
+           "python3 bench.py{w} --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline")
+    rdc, wrc = "TCC_EA0_RDREQ_32B TCC_EA0_RDREQ_64B TCC_EA0_RDREQ_128B", \
+        "TCC_EA0_WRREQ TCC_EA0_WRREQ_64B"
+    lines = ["# HBM traffic: bf16 linear 768->3072 at M=4096", "",
+             "Commands (repository root, one MI355X; one counter set per run):", "", "```",
+             cmd.format(c=rdc, d=rd_dir, w=""), cmd.format(c=wrc, d=wr_dir, w=""),
+             cmd.format(c=rdc, d=copy_rd_dir, w=" --workload copy"),
+             cmd.format(c=wrc, d=copy_wr_dir, w=" --workload copy"),
+             f"python3 bench.py --traffic-record {rd_dir} {wr_dir} {copy_rd_dir} {copy_wr_dir}",
+             "```", "",
+             "Bytes per dispatch from the memory-side request counters, each counted at its "
+             "size: read = 32 x RDREQ_32B + 64 x RDREQ_64B + 128 x RDREQ_128B, write = "
+             "64 x WRREQ_64B + 32 x (WRREQ - WRREQ_64B) (TCC_EA0_ counters summed over the "
+             "channels).  No calibration factor: the 512 MiB device copy counts "
+             f"{c_read / 2**20:.1f} MiB read and {c_write / 2**20:.1f} MiB written.", "",
+             "| op | kernel | HBM read (MB) | algorithmic read (MB) | read / algorithmic | "
+             "HBM write (MB) | algorithmic write (MB) |", "|---|---|---|---|---|---|---|"]
+    for op, e in kernels.items():
+        lines.append(f"| {op} | `{e['kernel']}` | {e['read_bytes'] / 1e6:.1f} | "
+                     f"{e['algorithmic_read'] / 1e6:.1f} | "
+                     f"{e['read_bytes'] / e['algorithmic_read']:.2f} | "
+                     f"{e['write_bytes'] / 1e6:.1f} | {e['algorithmic_write'] / 1e6:.1f} |")
+    lines += ["", "fwd and bwd (dX and dW tiles in one launch, bi_linear_backward) make the "
+              "step; dX and dW are the same products in launches of their own.  Algorithmic "
+              "bytes: every operand read once and the output written once (bwd reads dY once "
+              "for both products).", "",
+              f"Kernel sources hash at measurement: `{rec['source_hash']}` (bench.py reports "
+              "this traffic only while the sources hash the same)."]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def host_threads() -> int:
@@ -342,10 +458,18 @@ def bench_linear(args, torch, dig, synth):
               "bwd": 2 * (m * n + k * n + m * k) + 2 * (m * k + k * n)}
     dominant = max(per, key=per.get)
     achieved = flops[dominant] / (per[dominant] * 1e-3) / 1e12
-    clock = CLOCK[0] or {"mhz": None, "source": "no clock-settle phase"}
+    clock = dict(CLOCK[0] or {"mhz": None, "source": "no clock-settle phase"})
     # the dense bf16 MFMA peak at the measured clock, for context beside the
     # fraction of the 2.4 GHz specification peak
     peak_at_clock = (BF16_FLOP_PER_CLK * clock["mhz"] * 1e6 / 1e12) if clock["mhz"] else None
+    fastest = max(flops[name] / (v * 1e-3) / 1e12 for name, v in list(per.items()) + list(sep.items()))
+    if peak_at_clock is not None and fastest > peak_at_clock:
+        # a stale metrics table (seen under a profiler) reads far below the
+        # clock the kernels must have run at: report no clock rather than it
+        clock = {"mhz": None, "rejected_mhz": clock["mhz"],
+                 "source": clock["source"] + "; reading rejected: the peak at that clock is "
+                           "below the measured throughput"}
+        peak_at_clock = None
 
     def op_entry(name, v):
         tf = flops[name] / (v * 1e-3) / 1e12
@@ -704,6 +828,9 @@ def bench_copy(args, torch, dig, synth):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        write_traffic_record(*args.traffic_record)
+        return
     global SETTLE_MS
     SETTLE_MS = args.settle_ms
     if args.gpus != 1:
