@@ -15,10 +15,16 @@
 // A(i,r) = a[i*a_is + r*a_rs] and B(r,j) = b[r*b_rs + j*b_js] covers forward,
 // dX, dW and fp8.  A workgroup of 256 threads computes a TM x 64 tile (TM = 64,
 // 32 or 16: the tallest that still gives the chip 256 workgroups), each thread
-// a (TM/16) x 4 micro-tile with stride 16, staging 32-deep reduction slices
-// through LDS; the next slice is loaded into registers while the current one is
-// multiplied.  Neither the tile height nor the slice depth changes any
-// element's fmaf chain, so every tile gives the same bits.
+// TM/16 rows (stride 16) by 4 adjacent columns, staging 32-deep reduction
+// slices through LDS; the next slice is loaded into registers while the
+// current one is multiplied.  A is staged row by row ([TM][RK]) and B one
+// reduction index per row ([RK][64]), so one 16-byte LDS read gives a thread
+// four reduction values of a row of A, or its four columns of B at one
+// reduction index; full slices run unrolled on those reads, the last partial
+// slice one reduction index at a time up to the end of the range (an fmaf on
+// padding zeros could turn a chain's -0, reached by underflow, into +0).
+// Neither the tile height nor the slice depth changes any element's fmaf
+// chain, so every tile gives the same bits.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -27,17 +33,18 @@ namespace bi {
 namespace {
 
 constexpr int ST = 64;  // tile columns
-constexpr int RK = 32;  // reduction slice staged per step
 
 enum ScalarEpi : int { EPI_ROUND = 0, EPI_PARTIAL = 1, EPI_FP8 = 2 };
 
 template <int DT_IN, int DT_OUT, int EPI, int TM>
 __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
+    constexpr int RK = 32;             // reduction slice staged per step
     constexpr int MA = TM / 16;        // output rows per thread
     constexpr int NA = TM * RK / 256;  // A elements staged per thread per slice
     constexpr int NB = RK * ST / 256;  // B elements staged per thread per slice
-    __shared__ float As[RK][TM + 1];
-    __shared__ float Bs[RK][ST + 1];
+    // rows padded by 4 floats: 16-byte aligned, and rows of A four banks apart
+    __shared__ __align__(16) float As[TM][RK + 4];
+    __shared__ __align__(16) float Bs[RK][ST + 4];
 
     const int t = threadIdx.x;
     const int tx = t & 15, ty = t >> 4;
@@ -88,8 +95,8 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
 #pragma unroll
         for (int q = 0; q < NA; ++q) {
             const int idx = t + 256 * q;
-            if (a_r_contig) As[idx % RK][idx / RK] = ra[q];
-            else            As[idx / TM][idx % TM] = ra[q];
+            if (a_r_contig) As[idx / RK][idx % RK] = ra[q];
+            else            As[idx % TM][idx / TM] = ra[q];
         }
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
@@ -101,20 +108,39 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
 
     if (r_begin < r_end) load(r_begin);
     for (int64_t rk = r_begin; rk < r_end; rk += RK) {
-        const int valid = (int)(r_end - rk < RK ? r_end - rk : RK);
         store();
         __syncthreads();
         if (rk + RK < r_end) load(rk + RK);  // in flight while this slice is multiplied
-        for (int rr = 0; rr < valid; ++rr) {
-            float av[MA], bv[4];
+        if (r_end - rk >= RK) {
 #pragma unroll
-            for (int a = 0; a < MA; ++a) av[a] = As[rr][ty + 16 * a];
+            for (int r4 = 0; r4 < RK; r4 += 4) {
+                f32x4 av[MA], bv[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) bv[b] = Bs[rr][tx + 16 * b];
+                for (int a = 0; a < MA; ++a)
+                    av[a] = *reinterpret_cast<const f32x4 *>(&As[ty + 16 * a][r4]);
 #pragma unroll
-            for (int a = 0; a < MA; ++a)
+                for (int q = 0; q < 4; ++q)
+                    bv[q] = *reinterpret_cast<const f32x4 *>(&Bs[r4 + q][4 * tx]);
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(av[a], bv[b], acc[a][b]);
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int a = 0; a < MA; ++a)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            acc[a][b] = __builtin_fmaf(av[a][q], bv[q][b], acc[a][b]);
+            }
+        } else {
+            const int valid = (int)(r_end - rk);
+            for (int rr = 0; rr < valid; ++rr) {
+                float av[MA];
+#pragma unroll
+                for (int a = 0; a < MA; ++a) av[a] = As[ty + 16 * a][rr];
+                const f32x4 bv = *reinterpret_cast<const f32x4 *>(&Bs[rr][4 * tx]);
+#pragma unroll
+                for (int a = 0; a < MA; ++a)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(av[a], bv[b], acc[a][b]);
+            }
         }
         __syncthreads();
     }
@@ -125,7 +151,7 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
         if (gi >= p.rows) continue;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const int64_t gj = j0 + tx + 16 * b;
+            const int64_t gj = j0 + 4 * tx + b;
             if (gj >= p.cols) continue;
             float v = acc[a][b];
             if constexpr (EPI == EPI_PARTIAL) {
