@@ -148,7 +148,10 @@ int pick_tile(int op, int64_t k, int64_t n, bool fast) {
         if (cols >= 1024) return 111;
         return cols >= 128 ? 115 : 46;
     case OP_GDW:
+        // large expert weights: 192x256, eight waves of 96x64, copies spread
+        // (config 5: 8 x 8 tiles per expert, two rounds of the CUs); else
         // 128x128, four MFMA waves and four copy waves
+        if (n >= 768 && k >= 1024) return 116;
         return (k >= 128 && n >= 128) ? 44 : 46;
     }
     return 44;

@@ -11,8 +11,8 @@ hipError_t launch_mfma_grouped(const MfmaArgs &p, int tile_id, int dt, int epi, 
         if (dt == DT_F16 && epi == 0) return launch_dls_among<DT_F16, true, true, EPI_ROUND, MODE_SEGMENTS, 11, 12, 15>(p, tile_id, grid, s);
         if (dt == DT_BF16 && epi == 1) return launch_dls_among<DT_BF16, true, false, EPI_ROUND, MODE_SEGMENTS, 11, 12, 15>(p, tile_id, grid, s);
         if (dt == DT_F16 && epi == 1) return launch_dls_among<DT_F16, true, false, EPI_ROUND, MODE_SEGMENTS, 11, 12, 15>(p, tile_id, grid, s);
-        if (dt == DT_BF16 && epi == 2) return launch_dls_among<DT_BF16, false, false, EPI_F32, MODE_EXPERT_RED, 11, 15>(p, tile_id, grid, s);
-        if (dt == DT_F16 && epi == 2) return launch_dls_among<DT_F16, false, false, EPI_F32, MODE_EXPERT_RED, 11, 15>(p, tile_id, grid, s);
+        if (dt == DT_BF16 && epi == 2) return launch_dls_among<DT_BF16, false, false, EPI_F32, MODE_EXPERT_RED, 11, 15, 16>(p, tile_id, grid, s);
+        if (dt == DT_F16 && epi == 2) return launch_dls_among<DT_F16, false, false, EPI_F32, MODE_EXPERT_RED, 11, 15, 16>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
     if (tile_id >= 40) {
@@ -20,8 +20,8 @@ hipError_t launch_mfma_grouped(const MfmaArgs &p, int tile_id, int dt, int epi, 
         if (dt == DT_F16 && epi == 0) return launch_dl_among<DT_F16, true, true, EPI_ROUND, MODE_SEGMENTS, 1, 4, 6, 11, 12, 15>(p, tile_id, grid, s);
         if (dt == DT_BF16 && epi == 1) return launch_dl_among<DT_BF16, true, false, EPI_ROUND, MODE_SEGMENTS, 1, 4, 6, 11, 12, 15>(p, tile_id, grid, s);
         if (dt == DT_F16 && epi == 1) return launch_dl_among<DT_F16, true, false, EPI_ROUND, MODE_SEGMENTS, 1, 4, 6, 11, 12, 15>(p, tile_id, grid, s);
-        if (dt == DT_BF16 && epi == 2) return launch_dl_among<DT_BF16, false, false, EPI_F32, MODE_EXPERT_RED, 1, 4, 6, 11, 15>(p, tile_id, grid, s);
-        if (dt == DT_F16 && epi == 2) return launch_dl_among<DT_F16, false, false, EPI_F32, MODE_EXPERT_RED, 1, 4, 6, 11, 15>(p, tile_id, grid, s);
+        if (dt == DT_BF16 && epi == 2) return launch_dl_among<DT_BF16, false, false, EPI_F32, MODE_EXPERT_RED, 1, 4, 6, 11, 15, 16>(p, tile_id, grid, s);
+        if (dt == DT_F16 && epi == 2) return launch_dl_among<DT_F16, false, false, EPI_F32, MODE_EXPERT_RED, 1, 4, 6, 11, 15, 16>(p, tile_id, grid, s);
         return hipErrorInvalidValue;
     }
     if (dt == DT_BF16 && epi == 0) return launch_among<DT_BF16, true, true, EPI_ROUND, MODE_SEGMENTS, 1, 4, 6>(p, tile_id, grid, s);

@@ -688,6 +688,8 @@ template <> struct TileOf<13> { static constexpr int BM = 256, BN = 128, WGM = 4
 template <> struct TileOf<14> { static constexpr int BM = 128, BN = 256, WGM = 2, WGN = 4; };
 template <> struct TileOf<15> { static constexpr int BM = 128, BN = 128, WGM = 2, WGN = 4; };
 // three waves side by side (direct-load kernel only)
+// eight waves of 96x64: 2 x 4 tiles of 1408 x 2048 per expert (grouped dweights)
+template <> struct TileOf<16> { static constexpr int BM = 192, BN = 256, WGM = 2, WGN = 4; };
 template <> struct TileOf<17> { static constexpr int BM = 96, BN = 96, WGM = 1, WGN = 3; };
 // small-M shapes (direct-load kernel only, tile ids 120 and 121): many narrow
 // column tiles; 121 (one MFMA wave, a sixteen-stage ring) for the fp8 GEMM

@@ -27,12 +27,12 @@ const TileShape *mfma_tile(int id) {
         {41, 256, 256}, {42, 256, 192}, {43, 256, 128}, {44, 128, 128}, {45, 128, 96},
         {46, 64, 64},   {47, 128, 256}, {49, 128, 192}, {50, 256, 96},  {51, 256, 192},
         {52, 256, 256}, {53, 256, 128}, {54, 128, 256}, {55, 128, 128},
-        {48, 96, 96},   {57, 96, 96},   {120, 64, 32}, {121, 32, 32},
+        {48, 96, 96},   {56, 192, 256}, {57, 96, 96},  {120, 64, 32}, {121, 32, 32},
     };
     // ids 100 + i: the direct-load kernel with copies spread between MFMAs
     static const TileShape dls[] = {
         {104, 128, 128}, {105, 128, 96}, {108, 96, 96}, {111, 256, 192}, {112, 256, 256},
-        {114, 128, 256}, {115, 128, 128},
+        {114, 128, 256}, {115, 128, 128}, {116, 192, 256},
     };
     // ids 200 + i / 300 + i: the direct-load kernel with double- / quadruple-depth stages
     static const TileShape dld[] = {{220, 64, 32}, {321, 32, 32}};

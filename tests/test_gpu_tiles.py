@@ -18,7 +18,7 @@ from parity import check, dev, empty, host
 pytestmark = pytest.mark.gpu
 
 TILE_IDS = (list(range(1, 16)) + list(range(41, 58))
-            + [104, 105, 108, 111, 112, 114, 115, 120, 220, 321])
+            + [104, 105, 108, 111, 112, 114, 115, 116, 120, 220, 321])
 
 
 def run_all(fn, ids=TILE_IDS, base=16):
