@@ -25,6 +25,8 @@
 // padding zeros could turn a chain's -0, reached by underflow, into +0).
 // Neither the tile height nor the slice depth changes any element's fmaf
 // chain, so every tile gives the same bits.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -170,6 +172,170 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
     }
 }
 
+// Narrow outputs (at most 64 columns, such as a 48-wide layer).  The tiled
+// kernel above would leave the columns past the output's width idle in every
+// 64-column tile and make few tiles; here a lane owns ONE row and CW adjacent
+// columns (CW = 4, or 2 when that gives too few workgroups), a workgroup 256
+// consecutive rows (one per lane of its four waves) of the same columns.  The
+// B values of a reduction index are the same for every lane: they are staged
+// per slice into LDS and read back as one broadcast LDS read per reduction
+// index; each lane's A values come straight from memory into
+// registers, 16 bytes at a time along the reduction when rows are contiguous
+// and aligned (VEC), one value per reduction index otherwise (coalesced across
+// lanes when A is contiguous along its rows, as in dW).  The next slice's A and
+// B are loaded while the current one is multiplied; a partial last slice loads
+// each value as it multiplies it.  Each output is the same chain as in the
+// tiled kernel: fmaf over the reduction indices of its range in ascending
+// order from +0, nothing past the range.
+
+template <int DT>
+__device__ __forceinline__ float vec_elem(const u32x4 &v, int q) {
+    if constexpr (DT == DT_F32) {
+        return __uint_as_float(v[q]);
+    } else if constexpr (DT == DT_BF16 || DT == DT_F16) {
+        const uint32_t h = (v[q >> 1] >> (16 * (q & 1))) & 0xffffu;
+        return DT == DT_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+    } else {
+        return e4m3_bits_to_f32((v[q >> 2] >> (8 * (q & 3))) & 0xffu);
+    }
+}
+
+template <int DT_IN, int DT_OUT, int EPI, int CW, bool VEC>
+__global__ __launch_bounds__(256) void scalar_narrow_kernel(ScalarGemmArgs p) {
+    constexpr int ESZ = DT_IN == DT_F32 ? 4 : DT_IN == DT_E4M3 ? 1 : 2;
+    // reduction indices per staged slice: 256 bytes of each lane's A row when
+    // it is loaded 16 bytes at a time, 64 values otherwise
+    constexpr int NR_SL = VEC ? 256 / ESZ : 64;
+    constexpr int NBS = (NR_SL * CW + 255) / 256;  // B values staged per thread
+    constexpr int AV = 16 / ESZ;      // A values per 16-byte load
+    constexpr int NV = NR_SL / AV;    // 16-byte loads per lane and slice
+    constexpr int NA = VEC ? 1 : NR_SL;
+    using BV = typename std::conditional<CW == 4, f32x4, f32x2>::type;
+    __shared__ __align__(16) float Bs[2][NR_SL][CW];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t rgroups = (p.rows + 255) / 256, cgroups = (p.cols + CW - 1) / CW;
+    const int64_t per_chunk = rgroups * cgroups;
+    const int64_t bid = blockIdx.x;
+    const int64_t chunk = bid / per_chunk, rem = bid % per_chunk;
+    const int64_t cg = rem / rgroups, rg = rem % rgroups;
+    const int64_t i = rg * 256 + wave * 64 + lane;
+    const int64_t j0 = cg * CW;
+    const int64_t r_begin = chunk * p.chunk;
+    const int64_t r_end = r_begin + p.chunk < p.red ? r_begin + p.chunk : p.red;
+    // rows past the end load the last row (their outputs are not stored)
+    const int64_t ic = i < p.rows ? i : p.rows - 1;
+
+    float acc[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[c] = 0.0f;
+
+    // thread t stages B(rs + e / CW, j0 + e % CW) for e = t + 256 u < NR_SL * CW;
+    // +0 outside
+    float b_next[NBS];
+    auto load_b = [&](int64_t rs) {
+#pragma unroll
+        for (int u = 0; u < NBS; ++u) {
+            const int e = t + 256 * u;
+            if (e < NR_SL * CW) {
+                const int64_t r = rs + e / CW, j = j0 + e % CW;
+                b_next[u] = (r < r_end && j < p.cols)
+                                ? load_elem<DT_IN>(p.b, r * p.b_rs + j * p.b_js)
+                                : 0.0f;
+            }
+        }
+    };
+    // this lane's A values of a whole slice
+    u32x4 av_next[VEC ? NV : 1], av_cur[VEC ? NV : 1];
+    float as_next[NA], as_cur[NA];
+    auto load_a = [&](int64_t rs) {
+        if constexpr (VEC) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                static_cast<const char *>(p.a) + (ic * p.a_is + rs) * ESZ);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) av_next[v] = src[v];
+        } else {
+#pragma unroll
+            for (int q = 0; q < NR_SL; ++q)
+                as_next[q] = load_elem<DT_IN>(p.a, ic * p.a_is + (rs + q) * p.a_rs);
+        }
+    };
+
+    if (r_begin < r_end) {
+        load_b(r_begin);
+        if (r_begin + NR_SL <= r_end) load_a(r_begin);
+    }
+    int buf = 0;
+    for (int64_t rs = r_begin; rs < r_end; rs += NR_SL, buf ^= 1) {
+#pragma unroll
+        for (int u = 0; u < NBS; ++u) {
+            const int e = t + 256 * u;
+            if (e < NR_SL * CW) Bs[buf][e / CW][e % CW] = b_next[u];
+        }
+        const bool full = rs + NR_SL <= r_end;
+        if (full) {
+            if constexpr (VEC) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) av_cur[v] = av_next[v];
+            } else {
+#pragma unroll
+                for (int q = 0; q < NR_SL; ++q) as_cur[q] = as_next[q];
+            }
+        }
+        __syncthreads();
+        if (rs + NR_SL < r_end) {  // in flight while this slice is multiplied
+            load_b(rs + NR_SL);
+            if (rs + 2 * NR_SL <= r_end) load_a(rs + NR_SL);
+        }
+        if (full) {
+            // 16 bytes of B per LDS read: one reduction index of four columns or
+            // two of two
+            constexpr int RPR = 4 / CW;
+#pragma unroll
+            for (int r0 = 0; r0 < NR_SL; r0 += RPR) {
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(&Bs[buf][r0][0]);
+#pragma unroll
+                for (int u = 0; u < RPR; ++u) {
+                    const int rr = r0 + u;
+                    float a;
+                    if constexpr (VEC) a = vec_elem<DT_IN>(av_cur[rr / AV], rr % AV);
+                    else a = as_cur[rr];
+#pragma unroll
+                    for (int c = 0; c < CW; ++c) acc[c] = __builtin_fmaf(a, b[u * CW + c], acc[c]);
+                }
+            }
+        } else {
+            const int n = (int)(r_end - rs);
+            for (int rr = 0; rr < n; ++rr) {
+                const float a = load_elem<DT_IN>(p.a, ic * p.a_is + (rs + rr) * p.a_rs);
+                const BV b = *reinterpret_cast<const BV *>(&Bs[buf][rr][0]);
+#pragma unroll
+                for (int c = 0; c < CW; ++c) acc[c] = __builtin_fmaf(a, b[c], acc[c]);
+            }
+        }
+    }
+
+    if (i >= p.rows) return;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+        const int64_t j = j0 + c;
+        if (j >= p.cols) continue;
+        float v = acc[c];
+        if constexpr (EPI == EPI_PARTIAL) {
+            p.ws[(chunk * p.rows + i) * p.cols + j] = v;
+        } else {
+            if constexpr (EPI == EPI_FP8) {
+                v = v * p.scale_a[0];
+                v = v * p.scale_b[0];
+                if (p.bias) v = v + load_elem<DT_OUT>(p.bias, j);  // bf16 bias
+            } else {
+                if (p.bias) v = v + load_elem<DT_IN>(p.bias, j);
+            }
+            store_elem<DT_OUT>(p.c, i * p.ldc + j, v);
+        }
+    }
+}
+
 // Pass 2 of the chunked dW and of the bias gradient: out = RNE( ((P0 + P1) +
 // P2) + ... ) per element, chunks in ascending order.  Loads are issued CS_UN
 // at a time so their latencies overlap; the additions stay in chunk order.
@@ -260,8 +426,48 @@ __global__ __launch_bounds__(256) void grouped_dweights_scalar_kernel(GroupedSca
         hipLaunchKernelGGL(kern, dim3(grid), dim3(block), 0, stream, __VA_ARGS__);   \
     } while (0)
 
+// narrow outputs (at most 64 columns): one row per lane
+static hipError_t launch_scalar_narrow(const ScalarGemmArgs &p, int dt_in, int dt_out,
+                                       int epi, hipStream_t s) {
+    const int64_t rgroups = (p.rows + 255) / 256;
+    // four columns per lane while that gives the chip 256 workgroups, else two
+    const int cw = rgroups * ((p.cols + 3) / 4) * p.nchunks >= 256 ? 4 : 2;
+    const int64_t grid = rgroups * ((p.cols + cw - 1) / cw) * p.nchunks;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int esz = dt_in == DT_F32 ? 4 : dt_in == DT_E4M3 ? 1 : 2;
+    // 16-byte loads of A along the reduction: contiguous, aligned rows and
+    // chunk starts
+    const bool vec = p.a_rs == 1 && reinterpret_cast<uintptr_t>(p.a) % 16 == 0 &&
+                     (p.a_is * esz) % 16 == 0 && (p.nchunks == 1 || (p.chunk * esz) % 16 == 0);
+#define NCASE(DI, DO, E)                                                                    \
+    if (dt_in == DI && dt_out == DO && epi == E) {                                          \
+        if (cw == 4 && vec) BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 4, true>), grid, 256, s, p);  \
+        else if (cw == 4) BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 4, false>), grid, 256, s, p);   \
+        else if (vec) BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 2, true>), grid, 256, s, p);        \
+        else BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 2, false>), grid, 256, s, p);                \
+        return hipGetLastError();                                                           \
+    }
+    NCASE(DT_F32, DT_F32, EPI_ROUND)
+    NCASE(DT_BF16, DT_BF16, EPI_ROUND)
+    NCASE(DT_F16, DT_F16, EPI_ROUND)
+    NCASE(DT_F32, DT_F32, EPI_PARTIAL)
+    NCASE(DT_BF16, DT_F32, EPI_PARTIAL)
+    NCASE(DT_F16, DT_F32, EPI_PARTIAL)
+#undef NCASE
+    // e4m3 codes one at a time (16-byte loads of 16 codes cost registers the
+    // conversions need)
+    if (dt_in == DT_E4M3 && dt_out == DT_BF16 && epi == EPI_FP8) {
+        if (cw == 4) BI_LAUNCH((scalar_narrow_kernel<DT_E4M3, DT_BF16, EPI_FP8, 4, false>), grid, 256, s, p);
+        else BI_LAUNCH((scalar_narrow_kernel<DT_E4M3, DT_BF16, EPI_FP8, 2, false>), grid, 256, s, p);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_scalar_gemm(const ScalarGemmArgs &p, int dt_in, int dt_out, int epi,
                               hipStream_t s) {
+    if (p.cols <= 64) return launch_scalar_narrow(p, dt_in, dt_out, epi, s);
     const int64_t tiles_j = (p.cols + ST - 1) / ST;
     // the tallest tile that gives at least 256 workgroups (the first that does
     // not fall below it), 16 rows if none does
