@@ -77,6 +77,22 @@ def test_linear_parity_small(dt, tc, shape):
     full_parity(d, tc, f"dt{dt} tc{tc} {shape}")
 
 
+# outputs of at most 64 columns run the scalar tier's one-row-per-lane kernel:
+# whole and partial reduction slices, 16-byte and one-value loads of A (odd K),
+# one column, a dW reduced over three 256-row chunks (M = 700)
+NARROW = [(300, 1000, 48), (257, 256, 1), (65, 520, 63), (1, 384, 17), (700, 136, 40),
+          (130, 301, 48)]
+
+
+@pytest.mark.parametrize("dt", [synth.F32, synth.BF16, synth.F16])
+@pytest.mark.parametrize("shape", NARROW, ids=lambda s: "x".join(map(str, s)))
+def test_linear_parity_narrow(dt, shape):
+    m, k, n = shape
+    d = synth.linear(m, k, n, dt, seed=300 + m + k + n, sigma_w=0.05)
+    print(f"narrow linear parity dt={dt} shape={shape}", flush=True)
+    full_parity(d, 0, f"narrow dt{dt} {shape}")
+
+
 @pytest.mark.parametrize("dt", [synth.BF16, synth.F16, synth.F32])
 @pytest.mark.parametrize("tc", [0, 1])
 @pytest.mark.parametrize("shape", [(300, 200, 260), (257, 1000, 130), (4100, 96, 72),
@@ -214,8 +230,9 @@ def test_mlp_up_narrow_n48():
 def test_scalar_tier_bf16_is_rne_of_f32_on_upcast():
     """Scalar-tier contract: the bf16 (and f16) result equals the f32 tier run on
     the exactly upcast inputs, then rounded once to nearest-even."""
-    for dt in (synth.BF16, synth.F16):
-        d = synth.linear(130, 300, 70, dt, seed=31, sigma_w=0.05)
+    for dt, (m, k, n) in ((synth.BF16, (130, 300, 70)), (synth.F16, (130, 300, 70)),
+                          (synth.BF16, (700, 520, 40)), (synth.F16, (700, 520, 40))):
+        d = synth.linear(m, k, n, dt, seed=31, sigma_w=0.05)
         up = dict(d)
         for t in ("x", "w", "b", "dy"):
             up[t] = synth.to_bits(synth.to_f32(d[t], dt), synth.F32)
@@ -224,7 +241,7 @@ def test_scalar_tier_bf16_is_rne_of_f32_on_upcast():
         for name in ("forward", "dx", "dw"):
             low = host(getattr(Lb, name)(0), np.uint16)
             f32 = host(getattr(Lf, name)(0), np.uint32).view(np.float32)
-            assert np.array_equal(low, synth.to_bits(f32, dt)), (dt, name)
+            assert np.array_equal(low, synth.to_bits(f32, dt)), (dt, (m, k, n), name)
 
 
 def test_tile_families_give_identical_bits():
