@@ -43,6 +43,7 @@ HBM_PEAK = 8000.0    # GB/s
 # without packed f32 math): 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
 F32_VALU_PEAK = 78.6  # TFLOP/s
 BF16_FLOP_PER_CLK = 256 * 4096  # dense bf16 MFMA flop per shader clock, whole chip
+TARGET_FRAC = 0.60   # stated target for the default workload: forward, dX, dW each
 
 
 def parse():
@@ -277,9 +278,10 @@ _settled = [False]
 
 
 class ClockSampler:
-    """Shader clock (MHz) of GPU 0 read through amdsmi (gpu metrics,
-    current_gfxclk) every few milliseconds from a host thread while the step
-    runs untimed.  Never active during a timed region."""
+    """Shader clock (MHz) of GPU 0 read through amdsmi every few milliseconds
+    from a host thread while the step runs untimed: the current entry of the
+    GFX clock table (amdsmi_get_clk_freq), else the gpu-metrics current_gfxclk
+    (which some boards leave stale).  Never active during a timed region."""
 
     def __init__(self):
         self.samples, self.error, self._stop, self._th = [], None, False, None
@@ -293,7 +295,12 @@ class ClockSampler:
             self.error = f"amdsmi unavailable: {e!r}"[:200]
 
     def _read(self):
-        return float(self._smi.amdsmi_get_gpu_metrics_info(self._h)["current_gfxclk"])
+        smi = self._smi
+        try:
+            f = smi.amdsmi_get_clk_freq(self._h, smi.AmdSmiClkType.GFX)
+            return float(f["frequency"][f["current"]]) / 1e6
+        except Exception:
+            return float(smi.amdsmi_get_gpu_metrics_info(self._h)["current_gfxclk"])
 
     def _loop(self):
         while not self._stop:
@@ -323,8 +330,9 @@ class ClockSampler:
         a = np.array(self.samples)
         return {"mhz": float(np.median(a)), "min": float(a.min()), "max": float(a.max()),
                 "samples": int(a.size),
-                "source": "amdsmi gpu metrics current_gfxclk, sampled every ~4 ms while the "
-                          "step ran untimed (second half of the clock-settle phase)"}
+                "source": "amdsmi GFX clock (current entry of the clock table), sampled every "
+                          "~4 ms while the step ran untimed (second half of the clock-settle "
+                          "phase)"}
 
 
 CLOCK = [None]
@@ -503,6 +511,13 @@ def bench_linear(args, torch, dig, synth):
         "sclk": dict(clock, peak_bf16_at_sclk_tflops=round(peak_at_clock, 1)
                      if peak_at_clock else None),
     }
+    # the stated target for this workload: each of forward, dX and dW at 60 % or
+    # more of the dense bf16 peak; the gap per op, beside the result
+    fracs = {name: e["frac_peak"] for name, e in out["ops"].items()}
+    fracs.update({name: e["frac_peak"] for name, e in out["separate_launches"].items()})
+    out["target"] = {"frac_peak": TARGET_FRAC, "met": all(f >= TARGET_FRAC for f in fracs.values()),
+                     "gap": {name: round(TARGET_FRAC - f, 4) for name, f in fracs.items()},
+                     "us_per_op_at_target": round(flop / (TARGET_FRAC * BF16_PEAK * 1e12) * 1e6, 2)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_linear(d, args.cpu_seconds)
     return out
