@@ -63,7 +63,13 @@ def parity(d, tc, what, rows=None, wrows=None):
 @pytest.mark.parametrize("dt", [synth.BF16, synth.F16, synth.F32])
 @pytest.mark.parametrize("tc", [0, 1])
 @pytest.mark.parametrize("case", [(300, 136, 200, 5, 17, (2,)), (129, 64, 64, 3, 0, ()),
-                                  (520, 72, 260, 8, 40, (0, 7)), (7, 8, 5, 2, 2, ())],
+                                  (520, 72, 260, 8, 40, (0, 7)), (7, 8, 5, 2, 2, ()),
+                                  # more row-tile groups than one round over the eight XCDs
+                                  (2600, 136, 264, 37, 100, (5, 20)),
+                                  # expert weights large enough for the 192x256 dweights tile
+                                  (1200, 1024, 768, 3, 50, ()),
+                                  # every row is padding
+                                  (64, 64, 64, 4, 64, ())],
                          ids=lambda c: "m{}k{}n{}e{}".format(*c[:4]))
 def test_grouped_parity_small(dt, tc, case):
     m, k, n, e, pad, empty_experts = case
