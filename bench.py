@@ -10,9 +10,9 @@ seeded synthetic data already resident in HBM when timing starts.
 
 Prints ONE JSON line with the whole-step throughput (TFLOP/s, from the wall
 time of the timed steps), a per-kernel roofline entry for the dominant kernel
-(average launch duration from HIP events recorded on the launch stream in a
-second pass over the same steps), and the CPU oracle's throughput on a bounded
-sample of the same workload.
+(time per launch from batches of back-to-back launches of that kernel, each
+batch bracketed by HIP events recorded on the launch stream), and the CPU
+oracle's throughput on a bounded sample of the same workload.
 
 Other workloads (--workload): fp8 (e4m3 GEMM 8192x4096x4096), fp8_linear
 (scaled fp8 linear forward + backward with quantisation), grouped (8
@@ -274,6 +274,11 @@ class HipEvents:
 
 
 SETTLE_MS = 400.0
+SETTLE_CHUNK = 100  # steps queued between synchronisations
+TIMING = ("value: wall time of the timed steps (no events), after the clock-settle phase "
+          "(untimed steps) and the warm-up steps; time per launch of each op: median of "
+          "5 batches of 100 back-to-back launches of that op, each batch bracketed by HIP "
+          "events on its stream, divided by 100")
 _settled = [False]
 
 
@@ -331,35 +336,49 @@ class ClockSampler:
         return {"mhz": float(np.median(a)), "min": float(a.min()), "max": float(a.max()),
                 "samples": int(a.size),
                 "source": "amdsmi GFX clock (current entry of the clock table), sampled every "
-                          "~4 ms while the step ran untimed (second half of the clock-settle "
-                          "phase)"}
-
-
-CLOCK = [None]
+                          "~4 ms while the step ran untimed after the timed regions"}
 
 
 def settle(torch, ops):
     """Run the step, untimed, for SETTLE_MS of wall time (first call only).  An
     idle MI355X takes a few hundred milliseconds of load to reach its working
     clocks; without this the first few hundred steps run up to 15 % slower.
-    The shader clock is sampled during the second half of this phase."""
+    Work stays queued throughout (the GPU runs slower for some tens of
+    milliseconds after even a few milliseconds without work)."""
     if _settled[0] or SETTLE_MS <= 0:
         return
     s = torch.cuda.current_stream()
-    clock = ClockSampler()
     t0 = time.perf_counter()
-    sampling = False
     while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
-        if not sampling and (time.perf_counter() - t0) * 1e3 >= SETTLE_MS / 2:
-            clock.start()
-            sampling = True
-        for _ in range(20):
+        for _ in range(SETTLE_CHUNK):
             for _, fn in ops:
                 fn(s)
         torch.cuda.synchronize()
-    clock.stop()
-    CLOCK[0] = clock.summary()
     _settled[0] = True
+
+
+def measure_clock(torch, ops, ms=200.0):
+    """Shader clock while the step runs untimed for `ms` of wall time, after
+    every timed region: polling the SMU through amdsmi slows the GPU for some
+    tens of milliseconds afterwards, so no timed region follows it."""
+    s = torch.cuda.current_stream()
+    clock = ClockSampler()
+    t0 = time.perf_counter()
+    started = False
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(SETTLE_CHUNK):
+            for _, fn in ops:
+                fn(s)
+        if not started:
+            clock.start()
+            started = True
+        torch.cuda.synchronize()
+    clock.stop()
+    return clock.summary()
+
+
+BATCHES, BATCH_LAUNCHES = 5, 100
+HOST_BOUND = set()
 
 
 def timed_steps(torch, ops, steps, warmup):
@@ -367,11 +386,14 @@ def timed_steps(torch, ops, steps, warmup):
     through the C ABI.
 
     Timed region: `steps` steps with nothing else on the stream, bracketed by
-    device synchronisation; the wall time gives ms per step.  Kernel
-    durations: a second pass of `steps` steps in which every op is bracketed
-    by two timing events recorded on the stream it is launched on (each
-    record costs about 2 us of GPU time, so they stay out of the first pass).
-    Returns (wall ms per step, {name: mean event ms per call})."""
+    device synchronisation; the wall time gives ms per step.  Time per launch
+    of each op: BATCHES batches of BATCH_LAUNCHES back-to-back launches of that
+    op alone, each batch bracketed by two timing events on the stream the op
+    is launched on; the median batch divided by BATCH_LAUNCHES (an event pair
+    around every single launch would add its own ~2 us to each).  An op whose
+    launches take the host nearly as long to enqueue as the GPU takes to run
+    them is named in HOST_BOUND (its time is then the host's).
+    Returns (wall ms per step, {name: ms per launch})."""
     settle(torch, ops)
     s = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -385,19 +407,27 @@ def timed_steps(torch, ops, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     hev = HipEvents()
-    ev = {name: [(hev.new(), hev.new()) for _ in range(steps)] for name, _ in ops}
-    torch.cuda.synchronize()
-    for i in range(steps):
-        for name, fn in ops:
-            e0, e1 = ev[name][i]
-            hev.record(e0, s)
+    per = {}
+    for name, fn in ops:
+        for _ in range(3):
             fn(s)
+        ev = [(hev.new(), hev.new()) for _ in range(BATCHES)]
+        torch.cuda.synchronize()
+        host = []
+        for e0, e1 in ev:
+            t = time.perf_counter()
+            hev.record(e0, s)
+            for _ in range(BATCH_LAUNCHES):
+                fn(s)
             hev.record(e1, s)
-    torch.cuda.synchronize()
-    mean = {name: sum(hev.ms(a, b) for a, b in pairs) / max(len(pairs), 1)
-            for name, pairs in ev.items()}
+            host.append((time.perf_counter() - t) * 1e3)
+        torch.cuda.synchronize()
+        gpu = sorted(hev.ms(a, b) for a, b in ev)
+        per[name] = gpu[len(gpu) // 2] / BATCH_LAUNCHES
+        if sorted(host)[len(host) // 2] >= 0.9 * gpu[len(gpu) // 2]:
+            HOST_BOUND.add(name)
     hev.close()
-    return wall, mean
+    return wall, per
 
 
 def cpu_baseline_linear(d, target_s):
@@ -466,7 +496,7 @@ def bench_linear(args, torch, dig, synth):
               "bwd": 2 * (m * n + k * n + m * k) + 2 * (m * k + k * n)}
     dominant = max(per, key=per.get)
     achieved = flops[dominant] / (per[dominant] * 1e-3) / 1e12
-    clock = dict(CLOCK[0] or {"mhz": None, "source": "no clock-settle phase"})
+    clock = measure_clock(torch, ops)
     # the dense bf16 MFMA peak at the measured clock, for context beside the
     # fraction of the 2.4 GHz specification peak
     peak_at_clock = (BF16_FLOP_PER_CLK * clock["mhz"] * 1e6 / 1e12) if clock["mhz"] else None
@@ -498,9 +528,7 @@ def bench_linear(args, torch, dig, synth):
                                "M=4096: forward + dX + dW, MFMA tier",
                    "M": m, "K": k, "N": n, "bias": True,
                    "calls": "bi_forward, bi_linear_backward"},
-        "timing": f"value: wall time of the timed steps (no events), after {SETTLE_MS:.0f} ms of "
-                  "untimed steps (clock ramp) and the warm-up steps; kernel times: HIP events "
-                  "around each launch in a second pass of the same steps",
+        "timing": TIMING,
         "roofline": {"bound": "mfma", "kernel": dominant,
                      "achieved": round(achieved, 2), "peak": BF16_PEAK, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK, 4),
@@ -817,7 +845,7 @@ def bench_tiles(args, torch, dig, synth):
             "ms_per_step": round(default_ms, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": "bf16 linear 768->3072 at M=4096, each op on each candidate "
-                                   "tile (events per launch)", "M": m, "K": k, "N": n},
+                                   "tile", "M": m, "K": k, "N": n},
             "roofline": None, "tiles": res}
 
 
@@ -864,6 +892,9 @@ def main():
           "sweep": bench_sweep, "bias_grad": bench_bias_grad, "tiles": bench_tiles,
           "copy": bench_copy, "scalar": bench_scalar}[args.workload]
     out = fn(args, torch, dig, synth)
+    out.setdefault("timing", TIMING)
+    if HOST_BOUND:
+        out["host_bound_ops"] = sorted(HOST_BOUND)
     print(json.dumps(out), flush=True)
 
 
