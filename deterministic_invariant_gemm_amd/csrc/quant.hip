@@ -125,6 +125,12 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t *src, const
 // destination written in TR-byte row pieces.  vec_in: cols % 8 == 0 and src
 // 16-byte aligned; vec_out: rows % 16 == 0 and dst 16-byte aligned.
 constexpr int TR = 256;
+// LDS layout of the tile: the dword holding source columns 4c .. 4c+3 of source
+// row r sits at word r * TP + (c ^ tile_swz(r)).  With this pitch and swizzle
+// the write phase's reads (lanes: 16 row blocks x 4 dword columns) fall in 64
+// distinct banks and the read phase's writes meet at most two to a bank.
+constexpr int TP = 19;
+__device__ __forceinline__ int tile_swz(int r) { return 4 * ((r >> 6) & 3); }
 
 // dst_rows (nullable): also the untransposed codes, [rows, cols], from the same
 // read of the source; vec_rows: its 16-byte pieces may be stored whole.
@@ -132,7 +138,7 @@ template <int FMT>
 __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
     const uint16_t *src, const float *scale_inv, uint8_t *dst, uint8_t *dst_rows, float *amax,
     int64_t rows, int64_t cols, int vec_in, int vec_out, int vec_rows) {
-    __shared__ uint32_t tile[TR][64 / 4 + 1];  // bytes of source row r at tile[r][..], padded
+    __shared__ uint32_t tile[TR][TP];
     const float s = *scale_inv;
     const int64_t r0 = (int64_t)blockIdx.y * TR, c0 = (int64_t)blockIdx.x * 64;
     const int t = threadIdx.x;
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
                                  fmaxf(fabsf(f[4 * q + 2]), fabsf(f[4 * q + 3]))));
             code[q] = (uint32_t)cvt2<FMT, true>(
                 f[4 * q + 2] * s, f[4 * q + 3] * s, cvt2<FMT, false>(f[4 * q] * s, f[4 * q + 1] * s, 0));
-            tile[rr][cc / 4 + q] = code[q];
+            tile[rr][(cc / 4 + q) ^ tile_swz(rr)] = code[q];
         }
         if (dst_rows && gr < rows) {
             uint8_t *d = dst_rows + gr * cols + gc;
@@ -176,29 +182,46 @@ __global__ __launch_bounds__(QT) void transpose_quantize_kernel(
         }
     }
     __syncthreads();
-    // write: 64 destination rows x TR/16 pieces of 16 bytes; thread t takes
-    // destination row t / 4 (+ 64 per pass over the pieces) ... mapped so a
-    // wave covers whole TR-byte row pieces
-    constexpr int PIECES = TR / 16;  // 16-byte pieces per destination row
+    // write: thread t takes dword column c of the tile (destination rows
+    // c0 + 4c .. c0 + 4c + 3) and source rows 16 rb .. 16 rb + 15 (16 bytes of
+    // each of those destination rows): 16 LDS reads, a 4 x 4 byte transpose per
+    // four of them, four 16-byte stores.  Lanes of a wave: rb = lane % 16,
+    // c = lane / 16 + 4 * wave, so a store instruction writes 256 contiguous
+    // bytes of each of four destination rows.
+    static_assert(TR == 256 && QT == 256, "one thread per (row block, dword column)");
+    {
+        const int lane = t & 63, rb = lane & 15, c = (lane >> 4) + 4 * (t >> 6);
+        uint32_t v[16];
 #pragma unroll
-    for (int j = 0; j < 64 * PIECES / QT; ++j) {
-        const int idx = t + QT * j;
-        const int oc = idx / PIECES, rb = 16 * (idx % PIECES);
-        const int64_t go = c0 + oc, gr = r0 + rb;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int i = 0; i < 16; ++i) v[i] = tile[16 * rb + i][c ^ tile_swz(16 * rb + i)];
+        // o[e][q]: bytes e of v[4q] .. v[4q+3], i.e. destination row 4c + e,
+        // source rows 16 rb + 4q .. 16 rb + 4q + 3 (v_perm_b32 takes bytes 0-3
+        // from its second operand, 4-7 from its first)
+        uint32_t o[4][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t b = (tile[rb + i][oc >> 2] >> (8 * (oc & 3))) & 0xffu;
-            w[i >> 2] |= b << (8 * (i & 3));
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t x = __builtin_amdgcn_perm(v[4 * q + 1], v[4 * q], 0x05010400u);
+            const uint32_t y = __builtin_amdgcn_perm(v[4 * q + 1], v[4 * q], 0x07030602u);
+            const uint32_t z = __builtin_amdgcn_perm(v[4 * q + 3], v[4 * q + 2], 0x05010400u);
+            const uint32_t w = __builtin_amdgcn_perm(v[4 * q + 3], v[4 * q + 2], 0x07030602u);
+            o[0][q] = __builtin_amdgcn_perm(z, x, 0x05040100u);
+            o[1][q] = __builtin_amdgcn_perm(z, x, 0x07060302u);
+            o[2][q] = __builtin_amdgcn_perm(w, y, 0x05040100u);
+            o[3][q] = __builtin_amdgcn_perm(w, y, 0x07060302u);
         }
-        if (go < cols) {
-            uint8_t *d = dst + go * rows + gr;
-            if (vec_out && gr + 16 <= rows) {
-                *reinterpret_cast<u32x4 *>(d) = u32x4{w[0], w[1], w[2], w[3]};
-            } else {
+        const int64_t gr = r0 + 16 * rb;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (gr + i < rows) d[i] = (uint8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xffu);
+        for (int e = 0; e < 4; ++e) {
+            const int64_t go = c0 + 4 * c + e;
+            if (go < cols && gr < rows) {
+                uint8_t *d = dst + go * rows + gr;
+                if (vec_out && gr + 16 <= rows) {
+                    *reinterpret_cast<u32x4 *>(d) = u32x4{o[e][0], o[e][1], o[e][2], o[e][3]};
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (gr + i < rows) d[i] = (uint8_t)((o[e][i >> 2] >> (8 * (i & 3))) & 0xffu);
+                }
             }
         }
     }
