@@ -180,29 +180,80 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
     return pl;
 }
 
-// Tile for the batch at hand (forward, dX, fp8): the default tile of (k, n)
-// while it gives at least 192 workgroups (three quarters of the CUs), else
-// 128x128 (eight waves) if that does.  Smaller batches stream B through a few
-// rows of A: one round (at most 256 workgroups) of a narrow tile spreads that
-// stream over the most workgroups, and their time goes mostly to the fixed
-// cost of each LDS stage, so the forward and fp8 take the deep-stage variants
-// (32x32 with 512-byte stage rows while it fits one round, else 64x32 with
-// 256-byte rows) and dX the 64x32 tile; beyond that the wider of the two tiles
-// that gives more workgroups (narrow tiles over several rounds re-read B and
-// run 1.5-3x slower).  The tile may follow m because every tile issues the same
-// MFMA sequence per element (the bits do not change); the tier never follows
-// m.  Forced tiles are kept.
-int batch_tile(const Plan &pl, int tc, int64_t m, int64_t cols, bool deep) {
+// Launch-time model of the forward and dX tiles.  A launch of W workgroups
+// (one per CU: every candidate's LDS ring takes most of a CU's LDS) runs in
+// R = ceil(W / 256) rounds; a round costs the tile's fixed time f (prologue,
+// epilogue, dispatch) plus p per output element and 64-deep stage, and a
+// partial round of w workgroups less in proportion to how few CUs it occupies
+// (they share L2 and memory bandwidth with fewer others):
+//   t = f R + p S E ((R - 1) + a + (1 - a) w / 256)
+// with S = ceil(reduction / 64) stages and E = BM BN elements per tile.  f, p
+// and a are least-squares fits to forced-tile timings on one MI355X (M 4096
+// and 16384, reductions 512 to 4096, output widths 1024 to 5120; the choices
+// at the fitted shapes are within 2 % (forward) and 11 % (dX, 0.5 % on
+// average) of the fastest candidate, against 11-15 % on average and up to
+// 36-56 % for a fixed tile per (k, n)).  Tiles change speed only, never bits.
+struct TileCost {
+    int id;
+    double f_us, p_ps;
+};
+constexpr TileCost kFwdCost[] = {{111, 6.59, 24.06}, {52, 7.69, 23.28}, {53, 4.13, 30.52},
+                                 {44, 3.25, 28.36}};
+constexpr double kFwdShare = 0.65;
+constexpr TileCost kDxCost[] = {{45, 3.02, 31.58}, {50, 4.98, 26.34}, {53, 4.12, 30.29},
+                                {55, 2.29, 35.68}, {111, 6.75, 25.55}};
+constexpr double kDxShare = 0.35;
+constexpr int64_t kCUs = 256;
+
+template <size_t N>
+int model_tile(const TileCost (&tab)[N], double a, int64_t m, int64_t cols, int64_t red) {
+    int best = tab[0].id;
+    double best_t = 0.0;
+    for (size_t i = 0; i < N; ++i) {
+        const TileShape *ts = mfma_tile(tab[i].id);
+        const int64_t w = cdiv(m, ts->bm) * cdiv(cols, ts->bn);
+        const int64_t r = cdiv(w, kCUs), last = w - kCUs * (r - 1);
+        const double stage = tab[i].p_ps * 1e-6 * (double)ts->bm * (double)ts->bn;
+        const double t = tab[i].f_us * (double)r +
+                         stage * (double)cdiv(red, 64) *
+                             ((double)(r - 1) + a + (1.0 - a) * (double)last / (double)kCUs);
+        if (i == 0 || t < best_t) {
+            best = tab[i].id;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
+// Tile for the batch at hand (forward, dX, fp8; cols = the output width,
+// red = the reduction length).  Small batches (128x128 tiles would fill under
+// three quarters of the CUs) stream B through a few rows of A: one round (at
+// most 256 workgroups) of a narrow tile spreads that stream over the most
+// workgroups, and their time goes mostly to the fixed cost of each LDS stage,
+// so the forward and fp8 take the deep-stage variants (32x32 with 512-byte
+// stage rows while it fits one round, else 64x32 with 256-byte rows) and dX
+// the 64x32 tile.  Otherwise the forward and dX take the candidate the launch
+// model above finds fastest; fp8 keeps the default tile of (k, n) while it
+// gives at least 192 workgroups, else 128x128 (eight waves) if that does, else
+// the wider of the two that gives more workgroups.  The tile may follow m
+// because every tile issues the same MFMA sequence per element (the bits do
+// not change); the tier never follows m.  Forced tiles are kept.
+int batch_tile(int op, const Plan &pl, int tc, int64_t m, int64_t cols, int64_t red) {
     if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
     auto wgs = [&](int id) {
         const TileShape *ts = mfma_tile(id);
         return cdiv(m, ts->bm) * cdiv(cols, ts->bn);
     };
-    if (wgs(pl.tile) >= 192) return pl.tile;
+    const bool deep = op == OP_FWD || op == OP_FP8;
+    if (op == OP_FP8 && wgs(pl.tile) >= 192) return pl.tile;
+    if (wgs(115) < 192) {
+        if (deep && wgs(321) <= 256) return 321;
+        if (deep && wgs(220) <= 256) return 220;
+        if (wgs(120) <= 256) return 120;
+    }
+    if (op == OP_FWD) return model_tile(kFwdCost, kFwdShare, m, cols, red);
+    if (op == OP_DX) return model_tile(kDxCost, kDxShare, m, cols, red);
     if (wgs(115) >= 192) return 115;
-    if (deep && wgs(321) <= 256) return 321;
-    if (deep && wgs(220) <= 256) return 220;
-    if (wgs(120) <= 256) return 120;
     return wgs(pl.tile) >= wgs(115) ? pl.tile : 115;
 }
 
@@ -290,6 +341,17 @@ int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows
     return pl.tile;
 }
 
+int bi_plan_batch(int op, int dtype, int tc, int64_t m, int64_t k, int64_t n) {
+    const int t = bi_plan(op, dtype, tc, k, n, nullptr);
+    if (t <= 0) return t;
+    if (m < 0) return BI_ERR_SHAPE;
+    if (m == 0) return t;
+    const Plan pl = make_plan(op, op == OP_FP8 ? BI_BF16 : dtype, tc, k, n);
+    if (op == OP_FWD || op == OP_FP8) return batch_tile(op, pl, tc, m, n, k);
+    if (op == OP_DX) return batch_tile(op, pl, tc, m, k, n);
+    return t;
+}
+
 int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t m, int64_t k,
                int64_t n, int dtype, hipStream_t stream, int tc) {
     if (!dtype_ok(dtype)) return BI_ERR_DTYPE;
@@ -315,7 +377,7 @@ int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t 
     a.vec_a = aligned16(x) && k % 8 == 0;
     a.vec_b = aligned16(w) && n % 8 == 0;
     a.vec_c = aligned8(y) && n % 4 == 0;
-    const int tile = direct_tile(a, batch_tile(pl, tc, m, n, true), 2 * m * k, 2 * k * n);
+    const int tile = direct_tile(a, batch_tile(OP_FWD, pl, tc, m, n, k), 2 * m * k, 2 * k * n);
     return hip_status(launch_mfma_gemm(a, tile, dtype, /*layout A rc, B strided*/ 1, 0, stream));
 }
 
@@ -339,7 +401,7 @@ int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k
         return hip_status(launch_scalar_gemm(a, dtype, dtype, 0, stream));
     }
     MfmaArgs a{};
-    const int tile = dx_mfma_args(a, dx, dy, w, m, k, n, batch_tile(pl, tc, m, k, false));
+    const int tile = dx_mfma_args(a, dx, dy, w, m, k, n, batch_tile(OP_DX, pl, tc, m, k, n));
     return hip_status(launch_mfma_gemm(a, tile, dtype, /*both rc*/ 3, 0, stream));
 }
 
@@ -416,7 +478,8 @@ int bi_linear_backward(void *dx, void *dw, const void *dy, const void *x, const 
         return BI_ERR_WORKSPACE;
     if (m > 0 && k > 0 && n > 0 && px.tile != 0 && pw.tile != 0 && chunks == 1) {
         MfmaArgs ax{}, aw{};
-        const int tx = dx_mfma_args(ax, dx, dy, w, m, k, n, batch_tile(px, tc, m, k, false));
+        // the pair runs the (k, n) default dX tile (128x96 where it applies)
+        const int tx = dx_mfma_args(ax, dx, dy, w, m, k, n, px.tile);
         const int tw = dw_mfma_args(aw, dw, x, dy, m, k, n, pw, 1, nullptr);
         // one launch pays off while the dX tiles alone fill most CUs; with fewer,
         // the dX tiles (on the critical path, with the shorter ring of the
@@ -488,7 +551,7 @@ int fp8_gemm(void *y, const void *a, const void *bt, const float *a_dequant,
         d.vec_c = aligned8(y) && n % 4 == 0;
         d.scale_a = a_dequant; d.scale_b = b_dequant;
         d.bias = bias;
-        const int tile = direct_tile(d, batch_tile(pl, tc, m, n, true), m * k, n * k);
+        const int tile = direct_tile(d, batch_tile(OP_FP8, pl, tc, m, n, k), m * k, n * k);
         return hip_status(launch_fp8_dl(d, tile, fast, stream));
     }
     // register-staged fp8 kernel: 256x256, 128x128 or 64x64 tiles

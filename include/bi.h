@@ -129,7 +129,8 @@ int bi_forward(void *y, const void *x, const void *w, const void *bias, int64_t 
 
 /* Input gradient (ffma.py, _FFMAAddmm.backward: gx = gy W^T):
  *   dx[m,k] = RNE_dtype( sum_n dy[m,n] * w[k,n] )
- * dy: [m,n], w: [k,n], dx: [m,k].  Tier and tile depend on (k, n) only. */
+ * dy: [m,n], w: [k,n], dx: [m,k].  The tier depends on (k, n) only; the tile
+ * may also follow m (identical bits, see bi_plan). */
 int bi_backward_dx(void *dx, const void *dy, const void *w, int64_t m, int64_t k, int64_t n,
                    int dtype, hipStream_t stream, int tc);
 
@@ -321,12 +322,23 @@ const char *bi_status_string(int status);
  * 6 grouped dweights.  Returns 0 for the scalar tier, a positive tile id for
  * the MFMA tier, or a negative bi_status.  Depends on (op, dtype, tc, k, n)
  * only: the tier and the dW chunk length C never depend on m.  The tile
- * reported is the default for large batches; forward, dX and fp8 calls whose
- * m gives that tile fewer than 192 workgroups run 128x128 or a narrow 64x32
- * tile instead (every tile issues the same MFMA sequence per element, so the
- * bits are the same).  For dW, *chunk_rows (if not NULL) receives the chunk
- * length C. */
+ * reported is the default of (k, n); forward and dX calls run the tile a
+ * launch-time model finds fastest for (m, k, n) among a few candidates, small
+ * batches narrow 64x32 or 32x32 tiles, and fp8 calls whose m gives the default
+ * fewer than 192 workgroups 128x128 or a narrow tile (every tile issues the
+ * same MFMA sequence per element, so the bits are the same).  For dW,
+ * *chunk_rows (if not NULL) receives the chunk length C. */
 int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows);
+
+/* The tile a call of `op` (as in bi_plan) with batch m launches when its rows
+ * are 16-byte aligned, their lengths multiples of 8 elements and each operand
+ * below 2^30 bytes (otherwise the register-staged kernel runs 256x256, 128x128
+ * or 64x64): the batch-dependent choice of forward, dX and fp8 calls, the
+ * bi_plan tile for the other ops and for m == 0.  Returns 0 for the scalar
+ * tier or a negative bi_status (as bi_plan; BI_ERR_SHAPE for m < 0).  The
+ * m rows of a batch is the rows of A: x for the forward, dy for dX, a for fp8.
+ * Launches nothing. */
+int bi_plan_batch(int op, int dtype, int tc, int64_t m, int64_t k, int64_t n);
 
 #ifdef __cplusplus
 }

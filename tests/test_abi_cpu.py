@@ -101,6 +101,42 @@ def test_plan_is_shape_only_and_follows_fallback_rule(lib):
         assert dig.bi_plan(dig.OP_DW, dig.BI_BF16, 0, k, n) == dig.bi_plan(dig.OP_DW, dig.BI_F32, 0, k, n)
 
 
+def test_plan_batch_follows_the_launch_model(lib):
+    """The batch-dependent tile (bits never change with it): the default
+    workload's forward on 256x192 and dX on 128x96, the 8192x4096x4096 forward
+    on 256x256, the deep-stage narrow tiles for tiny batches, and the choices
+    the launch model makes where forced-tile timings on MI355X found another
+    tile fastest (forward 16384x2048x1408 on 256x192 (93 against 110 us for
+    128x128), 4096x2048x1024 on 128x128 (20 against 27 us), dX with K = 1280
+    on 256x96 (27 against 38 us))."""
+    bf, fwd, dx, fp8 = dig.BI_BF16, dig.OP_FWD, dig.OP_DX, dig.OP_FP8
+    assert dig.bi_plan_batch(fwd, bf, 1, 4096, 768, 3072) == 111
+    assert dig.bi_plan_batch(dx, bf, 1, 4096, 768, 3072) == 45
+    assert dig.bi_plan_batch(fwd, bf, 1, 8192, 4096, 4096) == 52
+    assert dig.bi_plan_batch(fwd, bf, 1, 1, 4096, 4096) == 321
+    assert dig.bi_plan_batch(fwd, bf, 1, 128, 4096, 4096) == 220
+    assert dig.bi_plan_batch(dx, bf, 1, 17, 4096, 4096) == 120
+    assert dig.bi_plan_batch(fwd, bf, 1, 16384, 2048, 1408) == 111
+    assert dig.bi_plan_batch(fwd, bf, 1, 4096, 2048, 1024) == 44
+    assert dig.bi_plan_batch(dx, bf, 1, 4096, 1280, 2048) == 50
+    assert dig.bi_plan_batch(fp8, 0, 1, 8192, 4096, 4096) == 41
+    assert dig.bi_plan_batch(fp8, 0, 1, 16, 4096, 4096) == 321
+    # m == 0: the bi_plan tile; the scalar tier and bad arguments as in bi_plan
+    assert dig.bi_plan_batch(fwd, bf, 1, 0, 768, 3072) == dig.bi_plan(fwd, bf, 1, 768, 3072)[0]
+    assert dig.bi_plan_batch(fwd, bf, 1, 4096, 768, 48) == 0
+    assert dig.bi_plan_batch(fwd, bf, 1, -1, 768, 3072) == -3
+    assert dig.bi_plan_batch(fwd, 9, 1, 4096, 768, 3072) == dig.bi_plan(fwd, 9, 1, 768, 3072)[0]
+    # dW and grouped ops: the bi_plan tile at any batch
+    for op in (dig.OP_DW, dig.OP_GFWD, dig.OP_GDIN, dig.OP_GDW):
+        for m in (1, 4096, 65536):
+            assert dig.bi_plan_batch(op, bf, 1, m, 2048, 1408) == dig.bi_plan(op, bf, 1, 2048, 1408)[0]
+    # every batch size of a sweep runs a tile that exists
+    for m in (1, 2, 31, 64, 100, 256, 1000, 2049, 4096, 10000, 65536):
+        for k, n in ((768, 3072), (4096, 4096), (1408, 2048), (2048, 1024)):
+            assert dig.bi_plan_batch(fwd, bf, 1, m, k, n) in (44, 52, 53, 111, 120, 220, 321)
+            assert dig.bi_plan_batch(dx, bf, 1, m, k, n) in (45, 50, 53, 55, 111, 120)
+
+
 def test_fp8_producer_validation(lib):
     assert dig.bi_fp8_quantize(F, F, F, None, 4, 7) == -2
     assert dig.bi_fp8_quantize(F, F, F, None, -1, dig.BI_FP8_E4M3) == -3
