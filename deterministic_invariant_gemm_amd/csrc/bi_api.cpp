@@ -180,7 +180,7 @@ Plan make_plan(int op, int dt, int tc, int64_t k, int64_t n) {
     return pl;
 }
 
-// Launch-time model of the forward and dX tiles.  A launch of W workgroups
+// Launch-time model of the forward, dX and fp8 tiles.  A launch of W workgroups
 // (one per CU: every candidate's LDS ring takes most of a CU's LDS) runs in
 // R = ceil(W / 256) rounds; a round costs the tile's fixed time f (prologue,
 // epilogue, dispatch) plus p per output element and 64-deep stage, and a
@@ -203,6 +203,18 @@ constexpr double kFwdShare = 0.65;
 constexpr TileCost kDxCost[] = {{45, 3.02, 31.58}, {50, 4.98, 26.34}, {53, 4.12, 30.29},
                                 {55, 2.29, 35.68}, {111, 6.75, 25.55}};
 constexpr double kDxShare = 0.35;
+// fp8 (A [m,k] and B^T [n,k] both reduction-contiguous): the exact path
+// (codes widened to bf16) and the fp8-instruction path, fitted the same way at
+// 28 shapes each (M 2048-16384, K and N 1024-8192): leave-one-out within 0.2 %
+// (exact) and 0.03 % (fast) of the fastest candidate on average, 3.5 % and
+// 0.6 % at worst, against 9 % and 4 % on average, up to 35 % and 48 %, for the
+// default tile of (k, n)
+constexpr TileCost kFp8Cost[] = {{52, 10.06, 23.26}, {111, 8.18, 22.96}, {54, 4.55, 27.03},
+                                 {44, 3.72, 25.98}};
+constexpr double kFp8Share = 0.40;
+constexpr TileCost kFp8FastCost[] = {{112, 7.96, 10.51}, {111, 7.33, 11.43}, {41, 10.3, 13.08},
+                                     {44, 3.35, 13.65}, {115, 2.58, 15.68}};
+constexpr double kFp8FastShare = 0.35;
 constexpr int64_t kCUs = 256;
 
 template <size_t N>
@@ -232,12 +244,10 @@ int model_tile(const TileCost (&tab)[N], double a, int64_t m, int64_t cols, int6
 // workgroups, and their time goes mostly to the fixed cost of each LDS stage,
 // so the forward and fp8 take the deep-stage variants (32x32 with 512-byte
 // stage rows while it fits one round, else 64x32 with 256-byte rows) and dX
-// the 64x32 tile.  Otherwise the forward and dX take the candidate the launch
-// model above finds fastest; fp8 keeps the default tile of (k, n) while it
-// gives at least 192 workgroups, else 128x128 (eight waves) if that does, else
-// the wider of the two that gives more workgroups.  The tile may follow m
-// because every tile issues the same MFMA sequence per element (the bits do
-// not change); the tier never follows m.  Forced tiles are kept.
+// the 64x32 tile.  Otherwise the candidate the launch model above finds
+// fastest.  The tile may follow m because every tile issues the same MFMA
+// sequence per element (the bits do not change); the tier never follows m.
+// Forced tiles are kept.
 int batch_tile(int op, const Plan &pl, int tc, int64_t m, int64_t cols, int64_t red) {
     if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
     auto wgs = [&](int id) {
@@ -245,7 +255,6 @@ int batch_tile(int op, const Plan &pl, int tc, int64_t m, int64_t cols, int64_t 
         return cdiv(m, ts->bm) * cdiv(cols, ts->bn);
     };
     const bool deep = op == OP_FWD || op == OP_FP8;
-    if (op == OP_FP8 && wgs(pl.tile) >= 192) return pl.tile;
     if (wgs(115) < 192) {
         if (deep && wgs(321) <= 256) return 321;
         if (deep && wgs(220) <= 256) return 220;
@@ -253,8 +262,10 @@ int batch_tile(int op, const Plan &pl, int tc, int64_t m, int64_t cols, int64_t 
     }
     if (op == OP_FWD) return model_tile(kFwdCost, kFwdShare, m, cols, red);
     if (op == OP_DX) return model_tile(kDxCost, kDxShare, m, cols, red);
-    if (wgs(115) >= 192) return 115;
-    return wgs(pl.tile) >= wgs(115) ? pl.tile : 115;
+    if (op == OP_FP8)
+        return fp8_fast(tc) ? model_tile(kFp8FastCost, kFp8FastShare, m, cols, red)
+                            : model_tile(kFp8Cost, kFp8Share, m, cols, red);
+    return pl.tile;
 }
 
 int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.chunk); }

@@ -322,11 +322,10 @@ const char *bi_status_string(int status);
  * 6 grouped dweights.  Returns 0 for the scalar tier, a positive tile id for
  * the MFMA tier, or a negative bi_status.  Depends on (op, dtype, tc, k, n)
  * only: the tier and the dW chunk length C never depend on m.  The tile
- * reported is the default of (k, n); forward and dX calls run the tile a
+ * reported is the default of (k, n); forward, dX and fp8 calls run the tile a
  * launch-time model finds fastest for (m, k, n) among a few candidates, small
- * batches narrow 64x32 or 32x32 tiles, and fp8 calls whose m gives the default
- * fewer than 192 workgroups 128x128 or a narrow tile (every tile issues the
- * same MFMA sequence per element, so the bits are the same).  For dW,
+ * batches narrow 64x32 or 32x32 tiles (every tile issues the same MFMA
+ * sequence per element, so the bits are the same).  For dW,
  * *chunk_rows (if not NULL) receives the chunk length C. */
 int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows);
 

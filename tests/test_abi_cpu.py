@@ -119,8 +119,15 @@ def test_plan_batch_follows_the_launch_model(lib):
     assert dig.bi_plan_batch(fwd, bf, 1, 16384, 2048, 1408) == 111
     assert dig.bi_plan_batch(fwd, bf, 1, 4096, 2048, 1024) == 44
     assert dig.bi_plan_batch(dx, bf, 1, 4096, 1280, 2048) == 50
-    assert dig.bi_plan_batch(fp8, 0, 1, 8192, 4096, 4096) == 41
+    # fp8 8192x4096x4096: 256x256 with eight waves (exact path; 201 against 204 us
+    # for four waves of 128x128), the spread-copy 256x256 tile on the fp8
+    # instruction (tc = 3); 4096x1024x4096 (K = 4096, N = 1024) on 128x128
+    # (exact 32 against 40 us for the default)
+    assert dig.bi_plan_batch(fp8, 0, 1, 8192, 4096, 4096) == 52
+    assert dig.bi_plan_batch(fp8, 0, 3, 8192, 4096, 4096) == 112
+    assert dig.bi_plan_batch(fp8, 0, 1, 4096, 4096, 1024) == 44
     assert dig.bi_plan_batch(fp8, 0, 1, 16, 4096, 4096) == 321
+    assert dig.bi_plan_batch(fp8, 0, 3, 16, 4096, 4096) == 321
     # m == 0: the bi_plan tile; the scalar tier and bad arguments as in bi_plan
     assert dig.bi_plan_batch(fwd, bf, 1, 0, 768, 3072) == dig.bi_plan(fwd, bf, 1, 768, 3072)[0]
     assert dig.bi_plan_batch(fwd, bf, 1, 4096, 768, 48) == 0
@@ -135,6 +142,8 @@ def test_plan_batch_follows_the_launch_model(lib):
         for k, n in ((768, 3072), (4096, 4096), (1408, 2048), (2048, 1024)):
             assert dig.bi_plan_batch(fwd, bf, 1, m, k, n) in (44, 52, 53, 111, 120, 220, 321)
             assert dig.bi_plan_batch(dx, bf, 1, m, k, n) in (45, 50, 53, 55, 111, 120)
+            assert dig.bi_plan_batch(fp8, 0, 1, m, k, n) in (44, 52, 54, 111, 120, 220, 321)
+            assert dig.bi_plan_batch(fp8, 0, 3, m, k, n) in (41, 44, 111, 112, 115, 120, 220, 321)
 
 
 def test_fp8_producer_validation(lib):
