@@ -172,21 +172,21 @@ __global__ __launch_bounds__(256) void scalar_gemm_kernel(ScalarGemmArgs p) {
     }
 }
 
-// Narrow outputs (at most 64 columns, such as a 48-wide layer).  The tiled
-// kernel above would leave the columns past the output's width idle in every
-// 64-column tile and make few tiles; here a lane owns ONE row and CW adjacent
-// columns (CW = 4, or 2 when that gives too few workgroups), a workgroup 256
-// consecutive rows (one per lane of its four waves) of the same columns.  The
-// B values of a reduction index are the same for every lane: they are staged
-// per slice into LDS and read back as one broadcast LDS read per reduction
-// index; each lane's A values come straight from memory into
-// registers, 16 bytes at a time along the reduction when rows are contiguous
-// and aligned (VEC), one value per reduction index otherwise (coalesced across
-// lanes when A is contiguous along its rows, as in dW).  The next slice's A and
-// B are loaded while the current one is multiplied; a partial last slice loads
-// each value as it multiplies it.  Each output is the same chain as in the
-// tiled kernel: fmaf over the reduction indices of its range in ascending
-// order from +0, nothing past the range.
+// Narrow outputs (at most 64 columns, such as a 48-wide layer) whose rows of A
+// are not contiguous along the reduction, or not 16-byte aligned (dW, where A
+// is contiguous across rows instead).  The tiled kernel above would leave the
+// columns past the output's width idle in every 64-column tile and make few
+// tiles; here a lane owns ONE row and CW adjacent columns (CW = 4, or 2 when
+// that gives too few workgroups), a workgroup 256 consecutive rows (one per
+// lane of its four waves) of the same columns.  The B values of a reduction
+// index are the same for every lane: they are staged per slice into LDS and
+// read back as one broadcast LDS read per reduction index; each lane's A
+// values come straight from memory into registers, one value per reduction
+// index (coalesced across lanes when A is contiguous along its rows, as in
+// dW).  The next slice's A and B are loaded while the current one is
+// multiplied; a partial last slice loads each value as it multiplies it.  Each
+// output is the same chain as in the tiled kernel: fmaf over the reduction
+// indices of its range in ascending order from +0, nothing past the range.
 
 template <int DT>
 __device__ __forceinline__ float vec_elem(const u32x4 &v, int q) {
@@ -200,16 +200,10 @@ __device__ __forceinline__ float vec_elem(const u32x4 &v, int q) {
     }
 }
 
-template <int DT_IN, int DT_OUT, int EPI, int CW, bool VEC>
+template <int DT_IN, int DT_OUT, int EPI, int CW>
 __global__ __launch_bounds__(256) void scalar_narrow_kernel(ScalarGemmArgs p) {
-    constexpr int ESZ = DT_IN == DT_F32 ? 4 : DT_IN == DT_E4M3 ? 1 : 2;
-    // reduction indices per staged slice: 256 bytes of each lane's A row when
-    // it is loaded 16 bytes at a time, 64 values otherwise
-    constexpr int NR_SL = VEC ? 256 / ESZ : 64;
+    constexpr int NR_SL = 64;  // reduction indices per staged slice
     constexpr int NBS = (NR_SL * CW + 255) / 256;  // B values staged per thread
-    constexpr int AV = 16 / ESZ;      // A values per 16-byte load
-    constexpr int NV = NR_SL / AV;    // 16-byte loads per lane and slice
-    constexpr int NA = VEC ? 1 : NR_SL;
     using BV = typename std::conditional<CW == 4, f32x4, f32x2>::type;
     __shared__ __align__(16) float Bs[2][NR_SL][CW];
 
@@ -246,19 +240,11 @@ __global__ __launch_bounds__(256) void scalar_narrow_kernel(ScalarGemmArgs p) {
         }
     };
     // this lane's A values of a whole slice
-    u32x4 av_next[VEC ? NV : 1], av_cur[VEC ? NV : 1];
-    float as_next[NA], as_cur[NA];
+    float as_next[NR_SL], as_cur[NR_SL];
     auto load_a = [&](int64_t rs) {
-        if constexpr (VEC) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(
-                static_cast<const char *>(p.a) + (ic * p.a_is + rs) * ESZ);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) av_next[v] = src[v];
-        } else {
-#pragma unroll
-            for (int q = 0; q < NR_SL; ++q)
-                as_next[q] = load_elem<DT_IN>(p.a, ic * p.a_is + (rs + q) * p.a_rs);
-        }
+        for (int q = 0; q < NR_SL; ++q)
+            as_next[q] = load_elem<DT_IN>(p.a, ic * p.a_is + (rs + q) * p.a_rs);
     };
 
     if (r_begin < r_end) {
@@ -274,13 +260,8 @@ __global__ __launch_bounds__(256) void scalar_narrow_kernel(ScalarGemmArgs p) {
         }
         const bool full = rs + NR_SL <= r_end;
         if (full) {
-            if constexpr (VEC) {
 #pragma unroll
-                for (int v = 0; v < NV; ++v) av_cur[v] = av_next[v];
-            } else {
-#pragma unroll
-                for (int q = 0; q < NR_SL; ++q) as_cur[q] = as_next[q];
-            }
+            for (int q = 0; q < NR_SL; ++q) as_cur[q] = as_next[q];
         }
         __syncthreads();
         if (rs + NR_SL < r_end) {  // in flight while this slice is multiplied
@@ -296,10 +277,7 @@ __global__ __launch_bounds__(256) void scalar_narrow_kernel(ScalarGemmArgs p) {
                 const f32x4 b = *reinterpret_cast<const f32x4 *>(&Bs[buf][r0][0]);
 #pragma unroll
                 for (int u = 0; u < RPR; ++u) {
-                    const int rr = r0 + u;
-                    float a;
-                    if constexpr (VEC) a = vec_elem<DT_IN>(av_cur[rr / AV], rr % AV);
-                    else a = as_cur[rr];
+                    const float a = as_cur[r0 + u];
 #pragma unroll
                     for (int c = 0; c < CW; ++c) acc[c] = __builtin_fmaf(a, b[u * CW + c], acc[c]);
                 }
@@ -319,6 +297,202 @@ __global__ __launch_bounds__(256) void scalar_narrow_kernel(ScalarGemmArgs p) {
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
         const int64_t j = j0 + c;
+        if (j >= p.cols) continue;
+        float v = acc[c];
+        if constexpr (EPI == EPI_PARTIAL) {
+            p.ws[(chunk * p.rows + i) * p.cols + j] = v;
+        } else {
+            if constexpr (EPI == EPI_FP8) {
+                v = v * p.scale_a[0];
+                v = v * p.scale_b[0];
+                if (p.bias) v = v + load_elem<DT_OUT>(p.bias, j);  // bf16 bias
+            } else {
+                if (p.bias) v = v + load_elem<DT_IN>(p.bias, j);
+            }
+            store_elem<DT_OUT>(p.c, i * p.ldc + j, v);
+        }
+    }
+}
+
+// Narrow outputs whose rows of A are contiguous along the reduction (forward,
+// dX, fp8; 16-byte aligned rows): a workgroup owns 64 rows (one per lane) and
+// CB = waves x CW adjacent columns (CW per wave), so each slice of A (64 rows x 128 bytes) is
+// loaded once per workgroup, in coalesced 16-byte row pieces, into LDS (rows
+// padded by 16 bytes so that the lanes' 16-byte reads of their own rows fall
+// in distinct banks) instead of once per column group straight into each
+// lane's registers.  B is staged per slice as f32 columns ([c][r]) and read as
+// broadcast 16-byte reads of four reduction indices.  The next full slice is
+// loaded into registers while the current one is multiplied (two LDS buffers,
+// one barrier per slice); a partial last slice is staged element by element
+// and multiplied one reduction index at a time up to the end of the range.
+// Each output is the same chain as in the kernels above.
+constexpr int RB_SLB = 128;  // bytes of a row of A per slice
+constexpr int64_t RB_WGS = 256;  // workgroups the launcher aims for
+
+template <int DT>
+__device__ __forceinline__ float lds_elem(const char *row, int q) {
+    if constexpr (DT == DT_F32) return *reinterpret_cast<const float *>(row + 4 * q);
+    else if constexpr (DT == DT_BF16)
+        return bf16_bits_to_f32(*reinterpret_cast<const uint16_t *>(row + 2 * q));
+    else if constexpr (DT == DT_F16)
+        return f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(row + 2 * q));
+    else return e4m3_bits_to_f32(*reinterpret_cast<const uint8_t *>(row + q));
+}
+
+template <int DT>
+__device__ __forceinline__ void copy_elem(char *dst, const void *src, int64_t i) {
+    if constexpr (DT == DT_F32) *reinterpret_cast<float *>(dst) = static_cast<const float *>(src)[i];
+    else if constexpr (DT == DT_BF16 || DT == DT_F16)
+        *reinterpret_cast<uint16_t *>(dst) = static_cast<const uint16_t *>(src)[i];
+    else *reinterpret_cast<uint8_t *>(dst) = static_cast<const uint8_t *>(src)[i];
+}
+
+// blockDim.x = 64 x (4 .. 8 waves); cblocks column blocks of CB columns
+template <int DT_IN, int DT_OUT, int EPI, int CW>
+__global__ __launch_bounds__(512) void scalar_rowblock_kernel(ScalarGemmArgs p, int64_t cblocks) {
+    constexpr int ESZ = DT_IN == DT_F32 ? 4 : DT_IN == DT_E4M3 ? 1 : 2;
+    constexpr int RB_KS = RB_SLB / ESZ;       // reduction indices per slice
+    constexpr int AV = 16 / ESZ;              // A values per 16-byte piece
+    constexpr int PPR = RB_KS * ESZ / 16;     // 16-byte pieces per row and slice
+    constexpr int APITCH = RB_KS * ESZ + 16;  // LDS bytes per row of A
+    constexpr int NAP = 64 * PPR / 256;       // pieces per thread (at least four waves)
+    constexpr int NBT = (CW * RB_KS + 63) / 64;  // B values per thread (at most)
+    constexpr int BP = RB_KS + 4;             // LDS floats per column of B
+    static_assert(NAP >= 1 && (64 * PPR) % 256 == 0, "whole pieces per thread");
+    __shared__ __align__(16) char As[2][64 * APITCH];
+    __shared__ __align__(16) float Bs[2][8 * CW * BP];
+
+    const int nth = blockDim.x, t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int cb = (nth >> 6) * CW;  // columns of this workgroup
+    const int64_t rblocks = (p.rows + 63) / 64;
+    const int64_t per_chunk = rblocks * cblocks;
+    const int64_t bid = blockIdx.x;
+    const int64_t chunk = bid / per_chunk, rem = bid % per_chunk;
+    // workgroups next to each other share their rows of A
+    const int64_t i0 = (rem / cblocks) * 64, j0 = (rem % cblocks) * cb;
+    const int64_t r_begin = chunk * p.chunk;
+    const int64_t r_end = r_begin + p.chunk < p.red ? r_begin + p.chunk : p.red;
+    const bool b_cols_contig = p.b_js == 1;
+
+    // staging registers of the next full slice: A pieces e = t + nth u (row
+    // e / PPR, piece e % PPR; rows past the end re-read the last row), B values
+    // e = t + nth u of the cb x RB_KS block (column-fastest when B's columns
+    // are contiguous, reduction-fastest otherwise; +0 outside)
+    u32x4 a_next[NAP];
+    float b_next[NBT];
+    auto b_index = [&](int e, int &c, int &q) {
+        if (b_cols_contig) { c = e % cb; q = e / cb; }
+        else { c = e / RB_KS; q = e % RB_KS; }
+    };
+    auto stage_full = [&](int64_t rs) {
+#pragma unroll
+        for (int u = 0; u < NAP; ++u) {
+            const int e = t + nth * u;
+            if (e < 64 * PPR) {
+                int64_t i = i0 + e / PPR;
+                if (i >= p.rows) i = p.rows - 1;
+                a_next[u] = *reinterpret_cast<const u32x4 *>(
+                    static_cast<const char *>(p.a) + (i * p.a_is + rs) * ESZ + 16 * (e % PPR));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NBT; ++u) {
+            const int e = t + nth * u;
+            if (e < cb * RB_KS) {
+                int c, q;
+                b_index(e, c, q);
+                const int64_t j = j0 + c;
+                b_next[u] = j < p.cols ? load_elem<DT_IN>(p.b, (rs + q) * p.b_rs + j * p.b_js) : 0.0f;
+            }
+        }
+    };
+
+    float acc[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[c] = 0.0f;
+    const int wc = wave * CW;  // this wave's first column in the workgroup
+
+    if (r_begin < r_end && r_begin + RB_KS <= r_end) stage_full(r_begin);
+    int buf = 0;
+    for (int64_t rs = r_begin; rs < r_end; rs += RB_KS, buf ^= 1) {
+        const int n = r_end - rs < RB_KS ? (int)(r_end - rs) : RB_KS;
+        char *as = As[buf];
+        float *bs = Bs[buf];
+        if (n == RB_KS) {
+#pragma unroll
+            for (int u = 0; u < NAP; ++u) {
+                const int e = t + nth * u;
+                if (e < 64 * PPR)
+                    *reinterpret_cast<u32x4 *>(as + (e / PPR) * APITCH + 16 * (e % PPR)) = a_next[u];
+            }
+#pragma unroll
+            for (int u = 0; u < NBT; ++u) {
+                const int e = t + nth * u;
+                if (e < cb * RB_KS) {
+                    int c, q;
+                    b_index(e, c, q);
+                    bs[c * BP + q] = b_next[u];
+                }
+            }
+        } else {
+            // the partial last slice, element by element (nothing past r_end is read)
+            for (int e = t; e < 64 * RB_KS; e += nth) {
+                const int row = e / RB_KS, q = e % RB_KS;
+                int64_t i = i0 + row;
+                if (i >= p.rows) i = p.rows - 1;
+                if (q < n) copy_elem<DT_IN>(as + row * APITCH + q * ESZ, p.a, i * p.a_is + rs + q);
+            }
+            for (int e = t; e < cb * RB_KS; e += nth) {
+                int c, q;
+                b_index(e, c, q);
+                const int64_t j = j0 + c;
+                bs[c * BP + q] = (q < n && j < p.cols)
+                                     ? load_elem<DT_IN>(p.b, (rs + q) * p.b_rs + j * p.b_js)
+                                     : 0.0f;
+            }
+        }
+        __syncthreads();
+        if (rs + 2 * RB_KS <= r_end) stage_full(rs + RB_KS);  // in flight during this slice
+        const char *arow = as + lane * APITCH;
+        const float *bcol = bs + wc * BP;
+        if (n == RB_KS) {
+            // one 16-byte piece of this lane's row: AV reduction indices
+            auto piece = [&](int kk) {
+                const u32x4 av = *reinterpret_cast<const u32x4 *>(arow + kk * ESZ);
+#pragma unroll
+                for (int j = 0; j < AV; j += 4) {
+                    f32x4 b[CW];
+#pragma unroll
+                    for (int c = 0; c < CW; ++c)
+                        b[c] = *reinterpret_cast<const f32x4 *>(bcol + c * BP + kk + j);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float a = vec_elem<DT_IN>(av, j + u);
+#pragma unroll
+                        for (int c = 0; c < CW; ++c) acc[c] = __builtin_fmaf(a, b[c][u], acc[c]);
+                    }
+                }
+            };
+            // two pieces per loop iteration (fully unrolled, the slice's LDS
+            // reads would be hoisted into more registers than two waves per
+            // SIMD have)
+#pragma unroll 2
+            for (int kk = 0; kk < RB_KS; kk += AV) piece(kk);
+        } else {
+            for (int q = 0; q < n; ++q) {
+                const float a = lds_elem<DT_IN>(arow, q);
+#pragma unroll
+                for (int c = 0; c < CW; ++c) acc[c] = __builtin_fmaf(a, bcol[c * BP + q], acc[c]);
+            }
+        }
+    }
+
+    const int64_t i = i0 + lane;
+    if (i >= p.rows) return;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+        const int64_t j = j0 + wc + c;
         if (j >= p.cols) continue;
         float v = acc[c];
         if constexpr (EPI == EPI_PARTIAL) {
@@ -426,6 +600,56 @@ __global__ __launch_bounds__(256) void grouped_dweights_scalar_kernel(GroupedSca
         hipLaunchKernelGGL(kern, dim3(grid), dim3(block), 0, stream, __VA_ARGS__);   \
     } while (0)
 
+// narrow outputs with aligned rows of A contiguous along the reduction: 64-row
+// workgroups of 4 to 8 waves, CW columns per wave (four while that still
+// gives 1024 waves, else two, else one)
+static hipError_t launch_scalar_rowblock(const ScalarGemmArgs &p, int dt_in, int dt_out,
+                                         int epi, hipStream_t s) {
+    const int64_t rblocks = (p.rows + 63) / 64;
+    int cw = 1;
+    for (int cand : {4, 2}) {
+        // (e4m3: at most two, four columns' conversions spill)
+        if (cand == 4 && dt_in == DT_E4M3) continue;
+        if (rblocks * ((p.cols + cand - 1) / cand) * p.nchunks >= 1024) {
+            cw = cand;
+            break;
+        }
+    }
+    // one wave per CW columns, split into enough column blocks of 4 to 8
+    // waves to give the chip RB_WGS workgroups where the columns allow
+    const int64_t waves = (p.cols + cw - 1) / cw;
+    const int64_t rows_chunks = rblocks * p.nchunks;
+    int64_t want = (RB_WGS + rows_chunks - 1) / rows_chunks;
+    if (want < (waves + 7) / 8) want = (waves + 7) / 8;
+    int64_t nw = (waves + want - 1) / want;
+    nw = nw < 4 ? 4 : nw > 8 ? 8 : nw;
+    const int64_t cblocks = (waves + nw - 1) / nw;
+    const int64_t grid = rows_chunks * cblocks;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int nth = (int)(64 * nw);
+#define RCASE(DI, DO, E)                                                                          \
+    if (dt_in == DI && dt_out == DO && epi == E) {                                                \
+        if (cw == 4) BI_LAUNCH((scalar_rowblock_kernel<DI, DO, E, 4>), grid, nth, s, p, cblocks);  \
+        else if (cw == 2) BI_LAUNCH((scalar_rowblock_kernel<DI, DO, E, 2>), grid, nth, s, p, cblocks); \
+        else BI_LAUNCH((scalar_rowblock_kernel<DI, DO, E, 1>), grid, nth, s, p, cblocks);          \
+        return hipGetLastError();                                                                 \
+    }
+    RCASE(DT_F32, DT_F32, EPI_ROUND)
+    RCASE(DT_BF16, DT_BF16, EPI_ROUND)
+    RCASE(DT_F16, DT_F16, EPI_ROUND)
+    RCASE(DT_F32, DT_F32, EPI_PARTIAL)
+    RCASE(DT_BF16, DT_F32, EPI_PARTIAL)
+    RCASE(DT_F16, DT_F32, EPI_PARTIAL)
+#undef RCASE
+    if (dt_in == DT_E4M3 && dt_out == DT_BF16 && epi == EPI_FP8) {
+        if (cw == 2) BI_LAUNCH((scalar_rowblock_kernel<DT_E4M3, DT_BF16, EPI_FP8, 2>), grid, nth, s, p, cblocks);
+        else BI_LAUNCH((scalar_rowblock_kernel<DT_E4M3, DT_BF16, EPI_FP8, 1>), grid, nth, s, p, cblocks);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
 // narrow outputs (at most 64 columns): one row per lane
 static hipError_t launch_scalar_narrow(const ScalarGemmArgs &p, int dt_in, int dt_out,
                                        int epi, hipStream_t s) {
@@ -436,16 +660,15 @@ static hipError_t launch_scalar_narrow(const ScalarGemmArgs &p, int dt_in, int d
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const int esz = dt_in == DT_F32 ? 4 : dt_in == DT_E4M3 ? 1 : 2;
-    // 16-byte loads of A along the reduction: contiguous, aligned rows and
-    // chunk starts
+    // rows of A contiguous along the reduction, 16-byte aligned, and so are
+    // the chunk starts: the row-block kernel
     const bool vec = p.a_rs == 1 && reinterpret_cast<uintptr_t>(p.a) % 16 == 0 &&
                      (p.a_is * esz) % 16 == 0 && (p.nchunks == 1 || (p.chunk * esz) % 16 == 0);
+    if (vec) return launch_scalar_rowblock(p, dt_in, dt_out, epi, s);
 #define NCASE(DI, DO, E)                                                                    \
     if (dt_in == DI && dt_out == DO && epi == E) {                                          \
-        if (cw == 4 && vec) BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 4, true>), grid, 256, s, p);  \
-        else if (cw == 4) BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 4, false>), grid, 256, s, p);   \
-        else if (vec) BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 2, true>), grid, 256, s, p);        \
-        else BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 2, false>), grid, 256, s, p);                \
+        if (cw == 4) BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 4>), grid, 256, s, p);      \
+        else BI_LAUNCH((scalar_narrow_kernel<DI, DO, E, 2>), grid, 256, s, p);              \
         return hipGetLastError();                                                           \
     }
     NCASE(DT_F32, DT_F32, EPI_ROUND)
@@ -454,14 +677,8 @@ static hipError_t launch_scalar_narrow(const ScalarGemmArgs &p, int dt_in, int d
     NCASE(DT_F32, DT_F32, EPI_PARTIAL)
     NCASE(DT_BF16, DT_F32, EPI_PARTIAL)
     NCASE(DT_F16, DT_F32, EPI_PARTIAL)
+    NCASE(DT_E4M3, DT_BF16, EPI_FP8)
 #undef NCASE
-    // e4m3 codes one at a time (16-byte loads of 16 codes cost registers the
-    // conversions need)
-    if (dt_in == DT_E4M3 && dt_out == DT_BF16 && epi == EPI_FP8) {
-        if (cw == 4) BI_LAUNCH((scalar_narrow_kernel<DT_E4M3, DT_BF16, EPI_FP8, 4, false>), grid, 256, s, p);
-        else BI_LAUNCH((scalar_narrow_kernel<DT_E4M3, DT_BF16, EPI_FP8, 2, false>), grid, 256, s, p);
-        return hipGetLastError();
-    }
     return hipErrorInvalidValue;
 }
 

@@ -49,7 +49,7 @@ def test_e4m3_format_is_ocp():
 
 @pytest.mark.parametrize("tc", [0, 1, FAST])
 @pytest.mark.parametrize("shape", [(300, 256, 260), (129, 200, 96), (1, 64, 64),
-                                   (70, 1000, 130), (5, 7, 3)],
+                                   (70, 1000, 130), (5, 7, 3), (300, 1008, 48)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_fp8_parity_small(tc, shape):
     m, k, n = shape

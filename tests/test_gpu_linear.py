@@ -81,7 +81,7 @@ def test_linear_parity_small(dt, tc, shape):
 # whole and partial reduction slices, 16-byte and one-value loads of A (odd K),
 # one column, a dW reduced over three 256-row chunks (M = 700)
 NARROW = [(300, 1000, 48), (257, 256, 1), (65, 520, 63), (1, 384, 17), (700, 136, 40),
-          (130, 301, 48)]
+          (130, 301, 48), (300, 48, 1000), (129, 40, 136), (2000, 64, 33), (70, 17, 200)]
 
 
 @pytest.mark.parametrize("dt", [synth.F32, synth.BF16, synth.F16])
