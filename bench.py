@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=400.0,
                     help="untimed run of the step before the warm-up steps, so that the GPU "
                          "clocks have left their idle state (once per process)")
+    ap.add_argument("--batch-launches", type=int, default=100,
+                    help="back-to-back launches per timing batch of each op (five batches); "
+                         "fewer keep profiler output small")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -174,7 +177,8 @@ def write_traffic_record(rd_dir: str, wr_dir: str, copy_rd_dir: str, copy_wr_dir
         json.dump(rec, f, indent=1)
         f.write("\n")
     cmd = ("rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- "
-           "python3 bench.py{w} --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline")
+           "python3 bench.py{w} --steps 3 --warmup 1 --settle-ms 0 --batch-launches 5 "
+           "--no-cpu-baseline")
     rdc, wrc = "TCC_EA0_RDREQ_32B TCC_EA0_RDREQ_64B TCC_EA0_RDREQ_128B", \
         "TCC_EA0_WRREQ TCC_EA0_WRREQ_64B"
     lines = ["# HBM traffic: bf16 linear 768->3072 at M=4096", "",
@@ -275,10 +279,11 @@ class HipEvents:
 
 SETTLE_MS = 400.0
 SETTLE_CHUNK = 100  # steps queued between synchronisations
-TIMING = ("value: wall time of the timed steps (no events), after the clock-settle phase "
-          "(untimed steps) and the warm-up steps; time per launch of each op: median of "
-          "5 batches of 100 back-to-back launches of that op, each batch bracketed by HIP "
-          "events on its stream, divided by 100")
+def timing_note():
+    return ("value: wall time of the timed steps (no events), after the clock-settle phase "
+            "(untimed steps) and the warm-up steps; time per launch of each op: median of "
+            f"{BATCHES} batches of {BATCH_LAUNCHES} back-to-back launches of that op, each batch "
+            f"bracketed by HIP events on its stream, divided by {BATCH_LAUNCHES}")
 _settled = [False]
 
 
@@ -528,7 +533,7 @@ def bench_linear(args, torch, dig, synth):
                                "M=4096: forward + dX + dW, MFMA tier",
                    "M": m, "K": k, "N": n, "bias": True,
                    "calls": "bi_forward, bi_linear_backward"},
-        "timing": TIMING,
+        "timing": timing_note(),
         "roofline": {"bound": "mfma", "kernel": dominant,
                      "achieved": round(achieved, 2), "peak": BF16_PEAK, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK, 4),
@@ -874,8 +879,9 @@ def main():
     if args.traffic_record:
         write_traffic_record(*args.traffic_record)
         return
-    global SETTLE_MS
+    global SETTLE_MS, BATCH_LAUNCHES
     SETTLE_MS = args.settle_ms
+    BATCH_LAUNCHES = max(1, args.batch_launches)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
@@ -892,7 +898,7 @@ def main():
           "sweep": bench_sweep, "bias_grad": bench_bias_grad, "tiles": bench_tiles,
           "copy": bench_copy, "scalar": bench_scalar}[args.workload]
     out = fn(args, torch, dig, synth)
-    out.setdefault("timing", TIMING)
+    out.setdefault("timing", timing_note())
     if HOST_BOUND:
         out["host_bound_ops"] = sorted(HOST_BOUND)
     print(json.dumps(out), flush=True)
