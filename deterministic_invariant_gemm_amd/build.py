@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libbi.so")
 LIB_TESTING = os.path.join(HERE, "libbi_testing.so")
 SOURCES = ["bi_api.cpp", "scalar_tier.hip", "mfma_tier.hip", "mfma_fwd.hip", "mfma_dx.hip",
            "mfma_dw.hip", "mfma_grouped.hip", "fp8_tier.hip", "fp8_dl.hip",
-           "quant.hip", "bias_grad.hip", "mfma_bwd.hip", "static_scratch.hip"]
+           "quant.hip", "bias_grad.hip", "mfma_bwd.hip", "mfma_gbwd.hip", "static_scratch.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",

@@ -749,31 +749,32 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
     { const int ts = tier_check(OP_GDW, dtype, tc, k, n); if (ts != BI_OK) return ts; }
     if (!dweights || !offsets) return BI_ERR_NULL;
     if (m > 0 && (!dinput || !input || !weights || !grad_out || !row_experts)) return BI_ERR_NULL;
-    // dinput (skipped for an empty batch)
+    // dinput (skipped for an empty batch): the scalar tier launches here, the
+    // MFMA tier below (with dweights in one launch where the tile pair allows)
+    MfmaArgs ad{};
+    int tile_d = 0;
     if (m > 0) {
         const Plan pl = make_plan(OP_GDIN, dtype, tc, k, n);
-        hipError_t er;
         if (pl.tile == 0) {
             GroupedScalarArgs g{};
             g.grad_out = grad_out; g.weights = weights; g.row_experts = row_experts;
             g.out = dinput; g.m = m; g.k = k; g.n = n; g.e = e;
-            er = launch_grouped_scalar(g, 1, dtype, stream);
+            if (launch_grouped_scalar(g, 1, dtype, stream) != hipSuccess) return BI_ERR_HIP;
         } else {
-            MfmaArgs a{};
-            a.a = grad_out; a.lda = n; a.b = weights; a.ldb = k; a.c = dinput; a.ldc = k;
-            a.rows = m; a.cols = k; a.red = n; a.chunk = kNoSplit; a.nchunks = 1;
-            a.offsets = offsets; a.n_experts = e; a.b_expert_stride = n * k;
-            a.vec_a = aligned16(grad_out) && n % 8 == 0;
-            a.vec_b = aligned16(weights) && k % 8 == 0;
-            a.vec_c = aligned8(dinput) && k % 4 == 0;
-            const int tile = direct_tile(a, pl.tile, 2 * m * n, 2 * e * n * k);
-            er = launch_mfma_gemm(a, tile, dtype, 1, 0, stream);
+            ad.a = grad_out; ad.lda = n; ad.b = weights; ad.ldb = k; ad.c = dinput; ad.ldc = k;
+            ad.rows = m; ad.cols = k; ad.red = n; ad.chunk = kNoSplit; ad.nchunks = 1;
+            ad.offsets = offsets; ad.n_experts = e; ad.b_expert_stride = n * k;
+            ad.vec_a = aligned16(grad_out) && n % 8 == 0;
+            ad.vec_b = aligned16(weights) && k % 8 == 0;
+            ad.vec_c = aligned8(dinput) && k % 4 == 0;
+            tile_d = direct_tile(ad, pl.tile, 2 * m * n, 2 * e * n * k);
         }
-        if (er != hipSuccess) return BI_ERR_HIP;
     }
     // dweights (always written, so experts without rows get +0)
     const Plan pw = make_plan(OP_GDW, dtype, tc, k, n);
     if (pw.tile == 0 || m == 0) {
+        if (tile_d && launch_mfma_gemm(ad, tile_d, dtype, 1, 0, stream) != hipSuccess)
+            return BI_ERR_HIP;
         GroupedScalarArgs g{};
         g.input = input; g.grad_out = grad_out; g.offsets = offsets; g.dweights = dweights;
         g.m = m; g.k = k; g.n = n; g.e = e;
@@ -787,6 +788,9 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
     a.vec_b = aligned16(input) && k % 8 == 0;
     a.vec_c = aligned16(dweights) && k % 4 == 0;
     const int tile = direct_tile(a, pw.tile, 2 * m * n, 2 * m * k);
+    if (tile_d && mfma_grouped_backward_pair(tile_d, tile, dtype))
+        return hip_status(launch_mfma_grouped_backward(ad, tile_d, a, tile, dtype, stream));
+    if (tile_d && launch_mfma_gemm(ad, tile_d, dtype, 1, 0, stream) != hipSuccess) return BI_ERR_HIP;
     return hip_status(launch_mfma_gemm(a, tile, dtype, 0, 2, stream));
 }
 

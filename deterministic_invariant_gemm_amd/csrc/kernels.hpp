@@ -116,6 +116,14 @@ bool mfma_backward_pair(int tile_x, int tile_w, int dt);
 hipError_t launch_mfma_backward(const MfmaArgs &px, int tile_x, const MfmaArgs &pw, int tile_w,
                                 int dt, hipStream_t s);
 
+// Grouped dinput (pd: segment-anchored rows) and f32 dweights (pw: expert-local
+// reduction) in one launch, for the direct-load tile pair
+// mfma_grouped_backward_pair() accepts (bf16 / f16); bits equal those of the
+// two launches.  hipErrorNotSupported (nothing launched) otherwise.
+bool mfma_grouped_backward_pair(int tile_d, int tile_w, int dt);
+hipError_t launch_mfma_grouped_backward(const MfmaArgs &pd, int tile_d, const MfmaArgs &pw,
+                                        int tile_w, int dt, hipStream_t s);
+
 // fp8 e4m3 GEMM on the register-staged kernel (tile ids 1, 4, 6) and on the
 // direct-load kernel (tile ids 40 + base, 100 + base):
 // C(i,j) = RNE_bf16((sum_r A(i,r) B(j,r)) * scale_a * scale_b), both operands
