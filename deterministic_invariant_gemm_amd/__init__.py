@@ -100,7 +100,7 @@ def _bind(path: str) -> ctypes.CDLL:
     L.bi_status_string.argtypes = [i32]
     L.bi_status_string.restype = ctypes.c_char_p
     L.bi_plan.argtypes = [i32, i32, i32, i64, i64, ctypes.POINTER(i64)]
-    L.bi_plan_batch.argtypes = [i32, i32, i32, i64, i64, i64]
+    L.bi_plan_batch.argtypes = [i32, i32, i32, i64, i64, i64, i64]
     for f in ("bi_forward", "bi_backward_dx", "bi_backward_dw", "bi_fp8_mm", "bi_grouped_nt",
               "bi_grouped_nt_backward", "bi_plan", "bi_plan_batch"):
         getattr(L, f).restype = i32
@@ -225,9 +225,10 @@ def bi_plan(op, dtype, tc, k, n):
     return r, chunk.value
 
 
-def bi_plan_batch(op, dtype, tc, m, k, n):
-    """Tile id a call with batch m launches on aligned operands (0: scalar tier)."""
-    return load().bi_plan_batch(op, dtype, tc, m, k, n)
+def bi_plan_batch(op, dtype, tc, m, k, n, e=0):
+    """Tile id a call with batch m (e experts for the grouped forward) launches
+    on aligned operands (0: scalar tier)."""
+    return load().bi_plan_batch(op, dtype, tc, m, k, n, e)
 
 
 def bi_status_string(status: int) -> str:

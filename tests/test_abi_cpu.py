@@ -133,10 +133,17 @@ def test_plan_batch_follows_the_launch_model(lib):
     assert dig.bi_plan_batch(fwd, bf, 1, 4096, 768, 48) == 0
     assert dig.bi_plan_batch(fwd, bf, 1, -1, 768, 3072) == -3
     assert dig.bi_plan_batch(fwd, 9, 1, 4096, 768, 3072) == dig.bi_plan(fwd, 9, 1, 768, 3072)[0]
-    # dW and grouped ops: the bi_plan tile at any batch
-    for op in (dig.OP_DW, dig.OP_GFWD, dig.OP_GDIN, dig.OP_GDW):
+    # grouped forward (e experts: one partial row tile per expert): 256x256 for
+    # 32768 rows x 4096 columns (265 against 323 us for 256x192), 128x128 with
+    # copy waves for 4096 x 4096 -> 2048 with 8 experts (73 against 143 us)
+    gf = dig.OP_GFWD
+    assert dig.bi_plan_batch(gf, bf, 1, 32768, 1024, 4096, 8) == 112
+    assert dig.bi_plan_batch(gf, bf, 1, 4096, 4096, 2048, 8) == 44
+    assert dig.bi_plan_batch(gf, bf, 1, 16384, 2048, 1408, -1) == -3
+    # dW and the grouped backward: the bi_plan tile at any batch
+    for op in (dig.OP_DW, dig.OP_GDIN, dig.OP_GDW):
         for m in (1, 4096, 65536):
-            assert dig.bi_plan_batch(op, bf, 1, m, 2048, 1408) == dig.bi_plan(op, bf, 1, 2048, 1408)[0]
+            assert dig.bi_plan_batch(op, bf, 1, m, 2048, 1408, 8) == dig.bi_plan(op, bf, 1, 2048, 1408)[0]
     # every batch size of a sweep runs a tile that exists
     for m in (1, 2, 31, 64, 100, 256, 1000, 2049, 4096, 10000, 65536):
         for k, n in ((768, 3072), (4096, 4096), (1408, 2048), (2048, 1024)):
