@@ -221,23 +221,34 @@ constexpr double kFp8FastShare = 0.35;
 // of (k, n) was 25 % slower on average and up to 2x
 constexpr TileCost kGfwdCost[] = {{112, 4.35, 22.95}, {111, 7.24, 22.5}, {44, 4.08, 26.06}};
 constexpr double kGfwdShare = 0.85;
+// grouped dinput (same segments, output width k, reduction n): 256x256 (eight
+// waves, which shares a launch with the default dweights tile, so the launch's
+// tail fills with dweights tiles) unless 128x128 with copy waves is modelled
+// 10 % faster, both priced with the forward's fit; forced-tile timings of the
+// backward at 10 shapes put this choice at the best dinput tile or within 2 %
+// of it (up to 30 % faster than the tile of (k, n))
+constexpr TileCost kGdinWide = {52, 4.35, 22.95}, kGdinNarrow = {44, 4.08, 26.06};
 constexpr int64_t kCUs = 256;
 
-// (extra: row tiles beyond ceil(m / BM), the grouped GEMM's one partial tile
-// per expert segment)
+// Modelled time of tile c (extra: row tiles beyond ceil(m / BM), the grouped
+// GEMM's one partial tile per expert segment)
+double model_us(const TileCost &c, double a, int64_t m, int64_t cols, int64_t red,
+                int64_t extra = 0) {
+    const TileShape *ts = mfma_tile(c.id);
+    const int64_t w = (cdiv(m, ts->bm) + extra) * cdiv(cols, ts->bn);
+    const int64_t r = cdiv(w, kCUs), last = w - kCUs * (r - 1);
+    const double stage = c.p_ps * 1e-6 * (double)ts->bm * (double)ts->bn;
+    return c.f_us * (double)r + stage * (double)cdiv(red, 64) *
+                                    ((double)(r - 1) + a + (1.0 - a) * (double)last / (double)kCUs);
+}
+
 template <size_t N>
 int model_tile(const TileCost (&tab)[N], double a, int64_t m, int64_t cols, int64_t red,
                int64_t extra = 0) {
     int best = tab[0].id;
     double best_t = 0.0;
     for (size_t i = 0; i < N; ++i) {
-        const TileShape *ts = mfma_tile(tab[i].id);
-        const int64_t w = (cdiv(m, ts->bm) + extra) * cdiv(cols, ts->bn);
-        const int64_t r = cdiv(w, kCUs), last = w - kCUs * (r - 1);
-        const double stage = tab[i].p_ps * 1e-6 * (double)ts->bm * (double)ts->bn;
-        const double t = tab[i].f_us * (double)r +
-                         stage * (double)cdiv(red, 64) *
-                             ((double)(r - 1) + a + (1.0 - a) * (double)last / (double)kCUs);
+        const double t = model_us(tab[i], a, m, cols, red, extra);
         if (i == 0 || t < best_t) {
             best = tab[i].id;
             best_t = t;
@@ -279,10 +290,17 @@ int batch_tile(int op, const Plan &pl, int tc, int64_t m, int64_t cols, int64_t 
 
 int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.chunk); }
 
-// Grouped forward tile for m rows routed to e experts (forced tiles kept)
+// Grouped forward and dinput tiles for m rows routed to e experts (forced
+// tiles kept)
 int grouped_fwd_tile(const Plan &pl, int tc, int64_t m, int64_t k, int64_t n, int64_t e) {
     if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
     return model_tile(kGfwdCost, kGfwdShare, m, n, k, e);
+}
+int grouped_din_tile(const Plan &pl, int tc, int64_t m, int64_t k, int64_t n, int64_t e) {
+    if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
+    const double wide = model_us(kGdinWide, kGfwdShare, m, k, n, e);
+    const double narrow = model_us(kGdinNarrow, kGfwdShare, m, k, n, e);
+    return narrow < 0.9 * wide ? kGdinNarrow.id : kGdinWide.id;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
@@ -376,6 +394,7 @@ int bi_plan_batch(int op, int dtype, int tc, int64_t m, int64_t k, int64_t n, in
     if (op == OP_FWD || op == OP_FP8) return batch_tile(op, pl, tc, m, n, k);
     if (op == OP_DX) return batch_tile(op, pl, tc, m, k, n);
     if (op == OP_GFWD) return grouped_fwd_tile(pl, tc, m, k, n, e);
+    if (op == OP_GDIN) return grouped_din_tile(pl, tc, m, k, n, e);
     return t;
 }
 
@@ -783,7 +802,7 @@ int bi_grouped_nt_backward(void *dinput, float *dweights, const void *input, con
             ad.vec_a = aligned16(grad_out) && n % 8 == 0;
             ad.vec_b = aligned16(weights) && k % 8 == 0;
             ad.vec_c = aligned8(dinput) && k % 4 == 0;
-            tile_d = direct_tile(ad, pl.tile, 2 * m * n, 2 * e * n * k);
+            tile_d = direct_tile(ad, grouped_din_tile(pl, tc, m, k, n, e), 2 * m * n, 2 * e * n * k);
         }
     }
     // dweights (always written, so experts without rows get +0)

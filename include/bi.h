@@ -332,12 +332,12 @@ int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows
 /* The tile a call of `op` (as in bi_plan) with batch m launches when its rows
  * are 16-byte aligned, their lengths multiples of 8 elements and each operand
  * below 2^30 bytes (otherwise the register-staged kernel runs 256x256, 128x128
- * or 64x64): the batch-dependent choice of forward, dX, fp8 and grouped
- * forward calls (e = the grouped call's number of experts; ignored by the
- * other ops), the bi_plan tile for dW, the grouped backward and m == 0.
+ * or 64x64): the batch-dependent choice of forward, dX, fp8, grouped forward
+ * and grouped dinput calls (e = the grouped call's number of experts; ignored
+ * by the other ops), the bi_plan tile for dW, the grouped dweights and m == 0.
  * Returns 0 for the scalar tier or a negative bi_status (as bi_plan;
  * BI_ERR_SHAPE for m < 0 or e < 0).  The m rows of a batch is the rows of A: x
- * for the forward, dy for dX, a for fp8, input for the grouped forward.
+ * for the forward, dy for dX, a for fp8, input / dY for the grouped forward / dinput.
  * Launches nothing. */
 int bi_plan_batch(int op, int dtype, int tc, int64_t m, int64_t k, int64_t n, int64_t e);
 

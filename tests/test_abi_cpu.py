@@ -140,8 +140,14 @@ def test_plan_batch_follows_the_launch_model(lib):
     assert dig.bi_plan_batch(gf, bf, 1, 32768, 1024, 4096, 8) == 112
     assert dig.bi_plan_batch(gf, bf, 1, 4096, 4096, 2048, 8) == 44
     assert dig.bi_plan_batch(gf, bf, 1, 16384, 2048, 1408, -1) == -3
-    # dW and the grouped backward: the bi_plan tile at any batch
-    for op in (dig.OP_DW, dig.OP_GDIN, dig.OP_GDW):
+    # grouped dinput: 256x256 (sharing a launch with the 192x256 dweights tiles)
+    # for 16384 rows of 2048 -> 1408, 128x128 with copy waves for 4096 rows of
+    # 4096 -> 2048 with 8 experts (182 against 202 us for the backward)
+    gd = dig.OP_GDIN
+    assert dig.bi_plan_batch(gd, bf, 1, 16384, 2048, 1408, 8) == 52
+    assert dig.bi_plan_batch(gd, bf, 1, 4096, 4096, 2048, 8) == 44
+    # dW and the grouped dweights: the bi_plan tile at any batch
+    for op in (dig.OP_DW, dig.OP_GDW):
         for m in (1, 4096, 65536):
             assert dig.bi_plan_batch(op, bf, 1, m, 2048, 1408, 8) == dig.bi_plan(op, bf, 1, 2048, 1408)[0]
     # every batch size of a sweep runs a tile that exists
