@@ -280,6 +280,9 @@ int batch_tile(int op, const Plan &pl, int tc, int64_t m, int64_t cols, int64_t 
         if (deep && wgs(220) <= 256) return 220;
         if (wgs(120) <= 256) return 120;
     }
+    // outputs narrower than 128 columns keep the 64x64 default (the model's
+    // candidates are 128 to 256 columns wide)
+    if (cols < 128) return pl.tile;
     if (op == OP_FWD) return model_tile(kFwdCost, kFwdShare, m, cols, red);
     if (op == OP_DX) return model_tile(kDxCost, kDxShare, m, cols, red);
     if (op == OP_FP8)
@@ -291,13 +294,13 @@ int batch_tile(int op, const Plan &pl, int tc, int64_t m, int64_t cols, int64_t 
 int64_t dw_chunks(const Plan &pl, int64_t m) { return m <= 0 ? 1 : cdiv(m, pl.chunk); }
 
 // Grouped forward and dinput tiles for m rows routed to e experts (forced
-// tiles kept)
+// tiles kept; outputs narrower than 128 columns keep the default)
 int grouped_fwd_tile(const Plan &pl, int tc, int64_t m, int64_t k, int64_t n, int64_t e) {
-    if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
+    if (pl.tile < 40 || (kForceHook && tc >= kForceBase) || n < 128) return pl.tile;
     return model_tile(kGfwdCost, kGfwdShare, m, n, k, e);
 }
 int grouped_din_tile(const Plan &pl, int tc, int64_t m, int64_t k, int64_t n, int64_t e) {
-    if (pl.tile < 40 || (kForceHook && tc >= kForceBase)) return pl.tile;
+    if (pl.tile < 40 || (kForceHook && tc >= kForceBase) || k < 128) return pl.tile;
     const double wide = model_us(kGdinWide, kGfwdShare, m, k, n, e);
     const double narrow = model_us(kGdinNarrow, kGfwdShare, m, k, n, e);
     return narrow < 0.9 * wide ? kGdinNarrow.id : kGdinWide.id;

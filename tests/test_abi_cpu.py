@@ -119,6 +119,9 @@ def test_plan_batch_follows_the_launch_model(lib):
     assert dig.bi_plan_batch(fwd, bf, 1, 16384, 2048, 1408) == 111
     assert dig.bi_plan_batch(fwd, bf, 1, 4096, 2048, 1024) == 44
     assert dig.bi_plan_batch(dx, bf, 1, 4096, 1280, 2048) == 50
+    # outputs narrower than 128 columns keep the 64x64 tile at large batches
+    assert dig.bi_plan_batch(fwd, bf, 1, 65536, 768, 96) == 46
+    assert dig.bi_plan_batch(dig.OP_GFWD, bf, 1, 65536, 768, 96, 8) == 46
     # fp8 8192x4096x4096: 256x256 with eight waves (exact path; 201 against 204 us
     # for four waves of 128x128), the spread-copy 256x256 tile on the fp8
     # instruction (tc = 3); 4096x1024x4096 (K = 4096, N = 1024) on 128x128
