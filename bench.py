@@ -435,6 +435,29 @@ def timed_steps(torch, ops, steps, warmup):
     return wall, per
 
 
+def cold_launches(torch, ops, reps=10, flush_bytes=1 << 30):
+    """Time per launch of each op with the caches cold: before every launch a
+    1 GiB buffer is overwritten on the same stream (more than the 256 MB MALL
+    and the L2s hold), and only the launch itself is bracketed by events.
+    Returns {name: mean ms}."""
+    s = torch.cuda.current_stream()
+    junk = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    hev = HipEvents()
+    out = {}
+    for name, fn in ops:
+        ev = [(hev.new(), hev.new()) for _ in range(reps)]
+        for e0, e1 in ev:
+            junk.fill_(1)
+            hev.record(e0, s)
+            fn(s)
+            hev.record(e1, s)
+        torch.cuda.synchronize()
+        out[name] = sum(hev.ms(a, b) for a, b in ev) / reps
+    hev.close()
+    del junk
+    return out
+
+
 def cpu_baseline_linear(d, target_s):
     """The oracle, as it is, on the first R rows of the batch (forward, dX and
     dW over those R rows); R grows until the sample takes about target_s."""
@@ -493,6 +516,7 @@ def bench_linear(args, torch, dig, synth):
                                                       ws if wsb else None, wsb, s, 1))),
     ]
     _, sep = timed_steps(torch, alone, args.steps, args.warmup)
+    cold = cold_launches(torch, ops)
     flop = 2.0 * m * k * n
     flops = {"fwd": flop, "bwd": 2 * flop, "dX": flop, "dW": flop}
     # algorithmic bytes per launch: each operand read once, the output written once
@@ -541,6 +565,10 @@ def bench_linear(args, torch, dig, synth):
                      "algorithmic_bytes": bytes_[dominant]},
         "ops": {name: op_entry(name, v) for name, v in per.items()},
         "separate_launches": {name: op_entry(name, v) for name, v in sep.items()},
+        "cold_caches": {"note": "each launch right after 1 GiB was written on its stream (the "
+                                "step's 36 MB otherwise stay in the 256 MB MALL); events around "
+                                "the launch alone",
+                        **{name: {"us": round(v * 1e3, 2)} for name, v in cold.items()}},
         "sclk": dict(clock, peak_bf16_at_sclk_tflops=round(peak_at_clock, 1)
                      if peak_at_clock else None),
     }
