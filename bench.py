@@ -345,16 +345,18 @@ class ClockSampler:
 
 
 def settle(torch, ops):
-    """Run the step, untimed, for SETTLE_MS of wall time (first call only).  An
-    idle MI355X takes a few hundred milliseconds of load to reach its working
-    clocks; without this the first few hundred steps run up to 15 % slower.
-    Work stays queued throughout (the GPU runs slower for some tens of
-    milliseconds after even a few milliseconds without work)."""
-    if _settled[0] or SETTLE_MS <= 0:
+    """Run the step, untimed, for SETTLE_MS of wall time (the first call; later
+    calls, after host work such as generating the next inputs, for a quarter of
+    that).  An idle MI355X takes a few hundred milliseconds of load to reach
+    its working clocks; without this the first few hundred steps run up to
+    15 % slower.  Work stays queued throughout (the GPU runs slower for some
+    tens of milliseconds after even a few milliseconds without work)."""
+    if SETTLE_MS <= 0:
         return
+    budget = SETTLE_MS if not _settled[0] else SETTLE_MS / 4
     s = torch.cuda.current_stream()
     t0 = time.perf_counter()
-    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+    while (time.perf_counter() - t0) * 1e3 < budget:
         for _ in range(SETTLE_CHUNK):
             for _, fn in ops:
                 fn(s)
@@ -517,6 +519,17 @@ def bench_linear(args, torch, dig, synth):
     ]
     _, sep = timed_steps(torch, alone, args.steps, args.warmup)
     cold = cold_launches(torch, ops)
+    # the same step in the other 16-bit dtype (same f32 samples rounded to it)
+    odt = synth.F16 if dt == synth.BF16 else synth.BF16
+    do = synth.mlp_up_linear(odt)
+    xo, wo, bo, dyo = dev(do["x"]), dev(do["w"]), dev(do["b"]), dev(do["dy"])
+    ops_o = [
+        ("fwd", lambda s: dig.check(dig.bi_forward(y, xo, wo, bo, m, k, n, odt, s, 1))),
+        ("bwd", lambda s: dig.check(dig.bi_linear_backward(dx, dw, dyo, xo, wo, m, k, n, odt,
+                                                           ws if wsb else None, wsb, s, 1))),
+    ]
+    ms_o, per_o = timed_steps(torch, ops_o, args.steps, args.warmup)
+    del xo, wo, bo, dyo
     flop = 2.0 * m * k * n
     flops = {"fwd": flop, "bwd": 2 * flop, "dX": flop, "dW": flop}
     # algorithmic bytes per launch: each operand read once, the output written once
@@ -565,6 +578,9 @@ def bench_linear(args, torch, dig, synth):
                      "algorithmic_bytes": bytes_[dominant]},
         "ops": {name: op_entry(name, v) for name, v in per.items()},
         "separate_launches": {name: op_entry(name, v) for name, v in sep.items()},
+        ("f16" if odt == synth.F16 else "bf16"): {
+            "value": round(3 * flop / (ms_o * 1e-3) / 1e12, 2), "ms_per_step": round(ms_o, 5),
+            "ops": {name: op_entry(name, v) for name, v in per_o.items()}},
         "cold_caches": {"note": "each launch right after 1 GiB was written on its stream (the "
                                 "step's 36 MB otherwise stay in the 256 MB MALL); events around "
                                 "the launch alone",
