@@ -8,8 +8,10 @@
 // MFMA tier, f32 accumulation, each output element's accumulator starting at
 // +0, reduction steps in ascending k:
 //   * default (FAST = false): every e4m3 code is widened exactly to bf16 in
-//     registers and each 16-deep step is one v_mfma_f32_32x32x16_bf16, which
-//     adds the exact products at f32 precision;
+//     registers and each 32-deep step is two v_mfma_f32_32x32x16_bf16, which
+//     add the exact products at f32 precision: lane half h holds the 16 codes
+//     32t + 16h .. + 15 of step t, the first MFMA takes codes 0..7 of each
+//     half, the second codes 8..15 (so each lane reads 16 bytes of LDS);
 //   * FAST = true (opt-in): each 64-deep step is one
 //     v_mfma_scale_f32_32x32x64_f8f6f4 with both operands in the OCP e4m3
 //     format (format code 0), which aligns the products of each group of 8
@@ -180,29 +182,35 @@ __global__ __launch_bounds__(NT) void fp8_gemm_kernel(Fp8Args p) {
             }
         } else {
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                // this lane's 8 reduction values of the 16-deep step: half
-                // `lhalf` of group kk, widened exactly to bf16
-                u32x4 fa[FM], fb[FN];
+            for (int kk = 0; kk < BK / 32; ++kk) {
+                // 32-deep step kk: this lane's 16 codes, group 2 kk + lhalf, widened
+                // exactly to bf16; the first MFMA takes codes 0..7 of each lane
+                // half, the second codes 8..15 (the direct-load kernel's order)
+                const int g = 2 * kk + lhalf;
+                u32x4 fa[2][FM], fb[2][FN];
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
                     const int row = wm * WTM + 32 * i + lrow;
-                    const u32x2 g = reinterpret_cast<const u32x2 *>(la + kk * BM + swz(row, kk))[lhalf];
-                    fa[i] = e4m3x8_to_bf16x8(g);
+                    const u32x4 w = la[g * BM + swz(row, g)];
+                    fa[0][i] = e4m3x8_to_bf16x8(u32x2{w[0], w[1]});
+                    fa[1][i] = e4m3x8_to_bf16x8(u32x2{w[2], w[3]});
                 }
 #pragma unroll
                 for (int j = 0; j < FN; ++j) {
                     const int row = wn * WTN + 32 * j + lrow;
-                    const u32x2 g = reinterpret_cast<const u32x2 *>(lb + kk * BN + swz(row, kk))[lhalf];
-                    fb[j] = e4m3x8_to_bf16x8(g);
+                    const u32x4 w = lb[g * BN + swz(row, g)];
+                    fb[0][j] = e4m3x8_to_bf16x8(u32x2{w[0], w[1]});
+                    fb[1][j] = e4m3x8_to_bf16x8(u32x2{w[2], w[3]});
                 }
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, fb[j]), __builtin_bit_cast(bf16x8, fa[i]),
-                            acc[i][j], 0, 0, 0);
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8, fb[h][j]),
+                                __builtin_bit_cast(bf16x8, fa[h][i]), acc[i][j], 0, 0, 0);
             }
         }
         __syncthreads();

@@ -144,11 +144,22 @@ struct DlType {  // bf16 / f16: v_mfma_f32_32x32x16_{bf16,f16}, 16 values per st
     static constexpr int ESZ = 2, STEPK = 16;
     using Frag = u32x4;
 };
+// fp8 e4m3 codes of the exact path: one lane's 16 codes (one 16-byte LDS read)
+struct E4m3x16 {
+    u32x4 v;
+};
+// ... widened exactly to bf16: the operands of two MFMA steps
+struct Bf16x8Pair {
+    u32x4 lo, hi;
+};
 template <>
-struct DlType<DT_E4M3> {  // fp8 e4m3 codes widened exactly to bf16:
-    // v_mfma_f32_32x32x16_bf16, 16 values per step, 8 codes (8 bytes) per lane
-    static constexpr int ESZ = 1, STEPK = 16;
-    using Frag = u32x2;
+struct DlType<DT_E4M3> {  // fp8 e4m3 codes widened exactly to bf16: two
+    // v_mfma_f32_32x32x16_bf16 per 32-deep step.  Lane half h reads the 16
+    // codes 32t + 16h .. 32t + 16h + 15 of step t; the first MFMA takes codes
+    // 0..7 of each half (reduction indices 32t + 0..7 and 32t + 16..23), the
+    // second codes 8..15 (32t + 8..15 and 32t + 24..31)
+    static constexpr int ESZ = 1, STEPK = 32;
+    using Frag = E4m3x16;
 };
 template <>
 struct DlType<DT_E4M3_FAST> {  // fp8 e4m3: v_mfma_scale_f32_32x32x64_f8f6f4, 64 per step
@@ -158,10 +169,16 @@ struct DlType<DT_E4M3_FAST> {  // fp8 e4m3: v_mfma_scale_f32_32x32x64_f8f6f4, 64
 
 // One MFMA step, B fragment first (each lane then holds 4 consecutive output
 // columns of one row).  e4m3 fragments of the exact path arrive here already
-// widened to bf16 (u32x4).
+// widened to bf16 (a pair: two MFMA steps, first codes 0..7 of each lane, then
+// codes 8..15).
 template <int DT>
 __device__ __forceinline__ f32x16 dl_mfma(u32x4 b, u32x4 a, f32x16 c) {
-    return mfma_step<DT == DT_E4M3 ? DT_BF16 : DT>(b, a, c);
+    return mfma_step<DT>(b, a, c);
+}
+template <int DT>
+__device__ __forceinline__ f32x16 dl_mfma(Bf16x8Pair b, Bf16x8Pair a, f32x16 c) {
+    c = mfma_step<DT_BF16>(b.lo, a.lo, c);
+    return mfma_step<DT_BF16>(b.hi, a.hi, c);
 }
 template <int DT>
 __device__ __forceinline__ f32x16 dl_mfma(i32x8 b, i32x8 a, f32x16 c) {
@@ -169,7 +186,10 @@ __device__ __forceinline__ f32x16 dl_mfma(i32x8 b, i32x8 a, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
 }
 // fragment as the MFMA takes it: e4m3 codes of the exact path widened to bf16
-__device__ __forceinline__ u32x4 dl_operand(u32x2 f) { return e4m3x8_to_bf16x8(f); }
+__device__ __forceinline__ Bf16x8Pair dl_operand(E4m3x16 f) {
+    return Bf16x8Pair{e4m3x8_to_bf16x8(u32x2{f.v[0], f.v[1]}),
+                      e4m3x8_to_bf16x8(u32x2{f.v[2], f.v[3]})};
+}
 __device__ __forceinline__ u32x4 dl_operand(u32x4 f) { return f; }
 __device__ __forceinline__ i32x8 dl_operand(i32x8 f) { return f; }
 
@@ -229,8 +249,8 @@ struct DLoad {
 
 // MFMA fragment reads from a reduction-contiguous stage ([rows][SR bytes]).
 // 16-bit: lane l takes 16 bytes (8 values) of row l & 31 at value 8 * (l >> 5)
-// of the 16-deep step; e4m3 (exact path): 8 bytes (8 codes) at value
-// 8 * (l >> 5) of the 16-deep step; e4m3 (fast path): 32 bytes (two chunks)
+// of the 16-deep step; e4m3 (exact path): 16 bytes (16 codes) at value
+// 16 * (l >> 5) of the 32-deep step; e4m3 (fast path): 32 bytes (two chunks)
 // at value 32 * (l >> 5) of the 64-deep step.
 template <int DT, int SR = 128>
 struct RcFrag {
@@ -243,19 +263,15 @@ struct RcFrag {
 #pragma unroll
         for (int kk = 0; kk < STEPS; ++kk)
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                if constexpr (DT == DT_E4M3)  // chunk kk holds the step, half hi the lane's
-                    koff[kk][c] = (uint32_t)(r * SR + 16 * (kk ^ rc_xor<SR>(r)) + 8 * hi);
-                else
-                    koff[kk][c] =
-                        (uint32_t)(r * SR + 16 * ((2 * CH * kk + CH * hi + c) ^ rc_xor<SR>(r)));
-            }
+            for (int c = 0; c < CH; ++c)
+                koff[kk][c] =
+                    (uint32_t)(r * SR + 16 * ((2 * CH * kk + CH * hi + c) ^ rc_xor<SR>(r)));
     }
     // rows base .. base+31 (base a multiple of 32)
     __device__ __forceinline__ auto read(const BI_LDS char *stage, int base, int kk) const {
         const BI_LDS char *row = stage + base * SR;
         if constexpr (DT == DT_E4M3) {
-            return *reinterpret_cast<const BI_LDS u32x2 *>(row + koff[kk][0]);
+            return E4m3x16{*reinterpret_cast<const BI_LDS u32x4 *>(row + koff[kk][0])};
         } else if constexpr (CH == 1) {
             return *reinterpret_cast<const BI_LDS u32x4 *>(row + koff[kk][0]);
         } else {
@@ -438,12 +454,13 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
     constexpr int RCR = DT == DT_E4M3_FAST ? 2 : 1;  // LDS reads per reduction-contiguous fragment
     constexpr int NREAD = FM * (A_RC ? RCR : 2) + FN * (B_RC ? RCR : 2);  // per step
     constexpr int NMFMA = FM * FN;
+    constexpr int MPC = DT == DT_E4M3 ? 2 : 1;  // MFMA instructions per dl_mfma
     // LDS reads of `sets` steps spread between the MFMAs of one step
     auto interleave = [&](auto sets_tag) {
         constexpr int PER = (decltype(sets_tag)::value * NREAD + NMFMA - 1) / NMFMA;
 #pragma unroll
         for (int q = 0; q < NMFMA; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x008, MPC, 0);  // one dl_mfma
             __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);  // then LDS reads
         }
         __builtin_amdgcn_sched_barrier(0);
