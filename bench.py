@@ -101,7 +101,7 @@ def recorded_traffic(record: str, op: str):
 TRAFFIC_RECORD = "linear_768x3072_m4096_traffic"
 # kernels of the default workload, by name: the step's forward and shared
 # backward, and dX and dW in launches of their own
-LINEAR_KERNELS = {"fwd": "mfma_dl_kernel<1, true, false,", "bwd": "mfma_dl_backward_kernel",
+LINEAR_KERNELS = {"fwd": "mfma_dl_kernel<1, true, false,", "bwd": "mfma_dl_backward_kernel<1>",
                   "dX": "mfma_dl_kernel<1, true, true,", "dW": "mfma_dl_kernel<1, false, false,"}
 COPY_BYTES = 512 << 20  # --workload copy
 
