@@ -774,6 +774,11 @@ int bi_grouped_nt(void *y, const void *input, const void *weights, const uint32_
     a.vec_b = aligned16(weights) && k % 8 == 0;
     a.vec_c = aligned8(y) && n % 4 == 0;
     const int tile = direct_tile(a, grouped_fwd_tile(pl, tc, m, k, n, e), 2 * m * k, 2 * e * n * k);
+    // more slots than one round: the split launch (same bits; forced tiles run
+    // the plain launch)
+    if (!(kForceHook && tc >= kForceBase) && mfma_grouped_split(tile, dtype) &&
+        seg_grid_rows(a.seg_tiles) * a.tiles_j > kGroupedSplitCUs)
+        return hip_status(launch_mfma_grouped_split(a, tile, dtype, stream));
     return hip_status(launch_mfma_gemm(a, tile, dtype, 3, 0, stream));
 }
 

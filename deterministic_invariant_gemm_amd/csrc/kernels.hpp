@@ -124,6 +124,17 @@ bool mfma_grouped_backward_pair(int tile_d, int tile_w, int dt);
 hipError_t launch_mfma_grouped_backward(const MfmaArgs &pd, int tile_d, const MfmaArgs &pw,
                                         int tile_w, int dt, hipStream_t s);
 
+// Grouped forward on tile 112 (256x256, segment-anchored rows) when its grid
+// has more slots than one round of kGroupedSplitCUs workgroups: in one launch,
+// the slots of the whole rounds run as 256x256 tiles and, if the work left
+// over (counted on the device from the offsets) fills at most half a round,
+// the remaining slots as two 256x128 column halves each, so that the last
+// round takes about half as long.  Same bits as the plain launch.
+// hipErrorNotSupported (nothing launched) for other tiles, dtypes or grids.
+constexpr int64_t kGroupedSplitCUs = 256;
+bool mfma_grouped_split(int tile, int dt);
+hipError_t launch_mfma_grouped_split(const MfmaArgs &p, int tile, int dt, hipStream_t s);
+
 // fp8 e4m3 GEMM on the register-staged kernel (tile ids 1, 4, 6) and on the
 // direct-load kernel (tile ids 40 + base, 100 + base):
 // C(i,j) = RNE_bf16((sum_r A(i,r) B(j,r)) * scale_a * scale_b), both operands

@@ -335,6 +335,25 @@ constexpr int dl_threads(int nw, bool spread, int wtm, int wtn) {
     return 64 * (nw + (dl_producer(nw, spread, wtm, wtn) ? DL_NPW : 0));
 }
 
+// Segment-anchored tile grid (MODE_SEGMENTS) of BM x BNB tiles whose slots from
+// s1 on run as two BM x (BNB / 2) column halves each: half-tile workgroup u
+// takes half (u / 8) & 1 of slot s1 + 8 * (u / 16) + u % 8, so both halves of
+// a slot run on that slot's XCD (s1 a multiple of 8).  A half past the last
+// column, or of a slot past the grid, has nothing to do.
+template <int MODE, int BM, int BNB, int NTH>
+__device__ __forceinline__ TileInfo decode_half_tile(const MfmaArgs &p, int t, int64_t u,
+                                                     int64_t s1) {
+    static_assert(MODE == MODE_SEGMENTS, "column halves of the segment grid");
+    constexpr int BNH = BNB / 2;
+    const int64_t xcd = u % 8, v = u / 8, h = v & 1;
+    TileInfo ti = decode_tile_at<MODE, BM, BNB, NTH>(p, t, s1 + 8 * (v >> 1) + xcd, 0, h * BNH, BNH);
+    if (!ti.skip) {
+        ti.col0 += h * BNH;
+        if (ti.col0 >= p.cols) ti.skip = true;
+    }
+    return ti;
+}
+
 // LDS ring bytes of a BM x BN tile with ns stages (0: dl_stages) of sr-byte
 // rows; the epilogue reuses them
 constexpr int dl_lds_bytes(int bm, int bn, int ns = 0, int sr = 128) {
@@ -345,8 +364,11 @@ constexpr int dl_lds_bytes(int bm, int bn, int ns = 0, int sr = 128) {
 // (dl_lds_bytes(BM, BN, NSV)) and bias row `lds_bias` ([BN]) owned by the
 // caller, threadIdx.x below dl_threads(...).  NSV: ring stages (0: as many as
 // fit, dl_stages); fewer leave room for a second workgroup on the CU.
+// HALF_OF > 0: the tile is a column half of the BM x HALF_OF segment grid
+// (decode_half_tile, with `blk` the half-tile index and `nblk` the first split
+// slot).
 template <int DT, bool A_RC, bool B_RC, int BM, int BN, int WGM, int WGN, int EPI, int MODE,
-          bool SPREAD, int NSV = 0, int SR = 128>
+          bool SPREAD, int NSV = 0, int SR = 128, int HALF_OF = 0>
 __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float *lds_bias,
                                         int64_t blk, int64_t nblk) {
     constexpr int NW = WGM * WGN;
@@ -374,7 +396,10 @@ __device__ __forceinline__ void dl_body(const MfmaArgs &p, char *lds_raw, float 
     const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
 
-    const TileInfo ti = decode_tile_at<MODE, BM, BN, NTH>(p, t, blk, nblk);
+    static_assert(HALF_OF == 0 || HALF_OF == 2 * BN, "halves of a tile twice as wide");
+    TileInfo ti;
+    if constexpr (HALF_OF > 0) ti = decode_half_tile<MODE, BM, HALF_OF, NTH>(p, t, blk, nblk);
+    else ti = decode_tile_at<MODE, BM, BN, NTH>(p, t, blk, nblk);
     const bool is_prod = PROD && wave >= NW;
     // index of this wave among the copying waves
     const int cwave = PROD ? (is_prod ? wave - NW : 0) : wave;

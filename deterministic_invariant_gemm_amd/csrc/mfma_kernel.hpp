@@ -307,10 +307,13 @@ struct TileInfo {
 };
 
 // Workgroup `blk` of `nblk` (blockIdx.x and gridDim.x for a launch of its own;
-// an offset index where one launch carries the tiles of two products).
+// an offset index where one launch carries the tiles of two products).  A
+// padding tile of MODE_SEGMENTS zero-fills columns col0 + fill_off ..
+// col0 + fill_off + fill_w - 1 (fill_w < 0: the whole tile width).
 template <int MODE, int BM, int BN, int NTH = NT>
 __device__ __forceinline__ TileInfo decode_tile_at(const MfmaArgs &p, int t, int64_t blk,
-                                                   int64_t nblk) {
+                                                   int64_t nblk, int64_t fill_off = 0,
+                                                   int64_t fill_w = -1) {
     TileInfo ti{};
     ti.skip = false;
     if constexpr (MODE == MODE_PLAIN) {
@@ -369,9 +372,10 @@ __device__ __forceinline__ TileInfo decode_tile_at(const MfmaArgs &p, int t, int
         if (x == p.n_experts) {
             // padding rows: exact +0 (rublas: ids outside [0,E) give zero rows)
             const int64_t r1 = ti.row0 + BM < ti.row_end ? ti.row0 + BM : ti.row_end;
+            const int64_t fw = fill_w < 0 ? BN : fill_w, c0 = ti.col0 + fill_off;
             uint16_t *pc = static_cast<uint16_t *>(p.c);
-            for (int64_t idx = t; idx < (r1 - ti.row0) * BN; idx += NTH) {
-                const int64_t i = ti.row0 + idx / BN, j = ti.col0 + idx % BN;
+            for (int64_t idx = t; idx < (r1 - ti.row0) * fw; idx += NTH) {
+                const int64_t i = ti.row0 + idx / fw, j = c0 + idx % fw;
                 if (j < p.cols) pc[i * p.ldc + j] = 0;
             }
             ti.skip = true;

@@ -338,7 +338,10 @@ int bi_plan(int op, int dtype, int tc, int64_t k, int64_t n, int64_t *chunk_rows
  * Returns 0 for the scalar tier or a negative bi_status (as bi_plan;
  * BI_ERR_SHAPE for m < 0 or e < 0).  The m rows of a batch is the rows of A: x
  * for the forward, dy for dX, a for fp8, input / dY for the grouped forward / dinput.
- * Launches nothing. */
+ * A grouped forward on tile 112 (256x256) whose grid holds more than one round
+ * of 256 workgroups may run the work left after the whole rounds as 256x128
+ * column halves of the same tiles (decided on the device from the offsets;
+ * same bits).  Launches nothing. */
 int bi_plan_batch(int op, int dtype, int tc, int64_t m, int64_t k, int64_t n, int64_t e);
 
 #ifdef __cplusplus

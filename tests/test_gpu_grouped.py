@@ -129,6 +129,55 @@ def test_grouped_16384x2048x1408_e8():
     check(dw2.reshape(G2.e * G2.n, G2.k)[wr], rw, synth.F32, "grouped_16384x2048x1408_e8 empty-expert dweights")
 
 
+def split_layout(m, n, e, offsets):
+    """Host mirror of the grouped forward's launch layout on the 256x256 tile:
+    'plain' (one round or less of slots), 'split' (whole rounds of 256x256
+    slots, then the leftover work, at most half a round, as 256x128 halves) or
+    'whole' (more left over: every slot whole)."""
+    cd = lambda a, b: -(-a // b)
+    tj = cd(n, 256)
+    nslots = cd(cd(m, 256) + e, 32) * 32 * tj
+    if nslots <= 256:
+        return "plain"
+    work = sum(cd(int(offsets[x + 1]) - int(offsets[x]), 256) for x in range(e)) * tj
+    full = work // 256 * 256
+    return "split" if full > 0 and 0 < work - full <= 128 else "whole"
+
+
+@pytest.mark.parametrize("case", [
+    # (m, k, n, e, padding rows, empty experts, seed, dtype, layout)
+    (16384, 256, 1408, 8, 819, (), 5, synth.BF16, "split"),    # tail of 128 slots, ragged N
+    (12000, 512, 1408, 8, 300, (2,), 41, synth.F16, "split"),  # an empty expert
+    (9000, 256, 4096, 3, 70, (), 44, synth.BF16, "split"),     # two whole rounds first
+    (20000, 512, 1408, 16, 500, (), 42, synth.BF16, "whole"),  # tail over half a round
+], ids=lambda c: "m{}k{}n{}e{}-{}".format(c[0], c[1], c[2], c[3], c[8]))
+def test_grouped_split_launch_same_bits(case):
+    """The grouped forward on the 256x256 tile with more slots than one round
+    runs as one launch of whole 256x256 slots and, when the work left after the
+    whole rounds fills at most half a round, 256x128 column halves of the
+    remaining slots (the choice made on the device from the offsets).  Its bits
+    equal the plain launch of the same tile and of the 128x128 tile; padding
+    rows are +0; sampled rows (from the first and the last slots) match the
+    oracle."""
+    m, k, n, e, pad, empty_x, seed, dt, want = case
+    d = synth.grouped(m, k, n, e, dt, seed=seed, pad_rows=pad, empty=empty_x)
+    assert split_layout(m, n, e, d["offsets"]) == want
+    assert dig.bi_plan_batch(dig.OP_GFWD, dt, 1, m, k, n, e) == 112
+    print(f"grouped split launch case={case}", flush=True)
+    G = Grouped(d)
+    y = host(G.forward(1), G.st)
+    with dig.testing_build():
+        for tile in (112, 44):
+            assert np.array_equal(host(G.forward(16 + tile), G.st), y), tile
+    ids = d["row_experts"]
+    assert np.all(y[ids >= e] == 0)
+    rows = np.union1d(sample_rows(m, 48, seed), np.arange(m - 40, m))
+    rows = np.union1d(rows, np.nonzero(ids < e)[0][-24:])
+    ry = oracle.grouped_fwd(dt, d["input"], d["weights"], ids, m, k, n, e, rows=rows)
+    check(y[rows], ry, dt, f"grouped split {case}")
+    assert len({digest(G.forward(1)) for _ in range(10)}) == 1
+
+
 def test_grouped_tiers_and_explicit_mfma_strategy():
     """tc = 2 (MFMA required) runs the same kernels as tc = 1 on eligible
     shapes: same bits.  The MFMA and scalar grouped backward agree bit for bit
