@@ -109,10 +109,16 @@ def test_fp8_linear_step_in_graph():
     replay_matches(step, [y, dx, dw, amax], noise)
 
 
-def test_grouped_step_in_graph():
-    d = synth.grouped(700, 136, 200, 5, synth.BF16, seed=135, pad_rows=37, empty=(3,),
+@pytest.mark.parametrize("case", [
+    (700, 136, 200, 5, 37, (3,), 135),
+    # the forward's 256x256 grid holds more than one round: the split launch
+    # (whole tiles, then 256x128 halves chosen on the device from the offsets)
+    (16384, 256, 1408, 8, 819, (), 5),
+], ids=["small", "split"])
+def test_grouped_step_in_graph(case):
+    m, k, n, e, pad, empty_x, seed = case
+    d = synth.grouped(m, k, n, e, synth.BF16, seed=seed, pad_rows=pad, empty=empty_x,
                       sigma_w=0.05)
-    m, k, n, e = d["m"], d["k"], d["n"], d["e"]
     inp, wts, gy = dev(d["input"]), dev(d["weights"]), dev(d["dy"])
     ids, off = dev(d["row_experts"]), dev(d["offsets"])
     y, di = empty((m, n), np.uint16), empty((m, k), np.uint16)
