@@ -122,7 +122,7 @@ __device__ __forceinline__ void store_elem(void *base, int64_t i, float v) {
 // XCD (ids congruent mod 8) receive one contiguous range of logical tiles.
 // The mapping is a permutation of [0, nb); it never changes which tile a
 // workgroup computes arithmetically, only where it runs.
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
+__host__ __device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nb) {
     const int64_t full = nb - nb % 8;
     if (bid >= full) return bid;
     return (bid % 8) * (full / 8) + bid / 8;

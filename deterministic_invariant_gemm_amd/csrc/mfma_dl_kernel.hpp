@@ -341,8 +341,8 @@ constexpr int dl_threads(int nw, bool spread, int wtm, int wtn) {
 // a slot run on that slot's XCD (s1 a multiple of 8).  A half past the last
 // column, or of a slot past the grid, has nothing to do.
 template <int MODE, int BM, int BNB, int NTH>
-__device__ __forceinline__ TileInfo decode_half_tile(const MfmaArgs &p, int t, int64_t u,
-                                                     int64_t s1) {
+__host__ __device__ __forceinline__ TileInfo decode_half_tile(const MfmaArgs &p, int t, int64_t u,
+                                                              int64_t s1) {
     static_assert(MODE == MODE_SEGMENTS, "column halves of the segment grid");
     constexpr int BNH = BNB / 2;
     const int64_t xcd = u % 8, v = u / 8, h = v & 1;
@@ -352,6 +352,16 @@ __device__ __forceinline__ TileInfo decode_half_tile(const MfmaArgs &p, int t, i
         if (ti.col0 >= p.cols) ti.skip = true;
     }
     return ti;
+}
+
+// First workgroup of the column halves in a split launch of `nslots` segment
+// slots over `cus` workgroups per round, for `work` working slots (expert row
+// tiles x column tiles): F = work rounded down to whole rounds when the work
+// left over is more than none and at most half a round, else nslots (every
+// slot whole).
+__host__ __device__ constexpr int64_t split_first_half(int64_t work, int64_t nslots, int64_t cus) {
+    return work / cus > 0 && work % cus > 0 && 2 * (work % cus) <= cus ? work / cus * cus
+                                                                        : nslots;
 }
 
 // LDS ring bytes of a BM x BN tile with ns stages (0: dl_stages) of sr-byte

@@ -55,11 +55,10 @@ __global__ __launch_bounds__(kThSplit) void mfma_dl_grouped_split_kernel(MfmaArg
     __shared__ __align__(16) float lds_bias[TBig::BN];
     const int64_t b = blockIdx.x;
     int64_t first_half = nslots;  // first workgroup of the half tiles
-    if (b >= kGroupedSplitCUs) {
-        const int64_t work = (int64_t)expert_row_tiles<TBig::BM>(p, threadIdx.x & 63) * p.tiles_j;
-        const int64_t full = work / kGroupedSplitCUs * kGroupedSplitCUs, tail = work - full;
-        if (full > 0 && tail > 0 && 2 * tail <= kGroupedSplitCUs) first_half = full;
-    }
+    if (b >= kGroupedSplitCUs)
+        first_half = split_first_half(
+            (int64_t)expert_row_tiles<TBig::BM>(p, threadIdx.x & 63) * p.tiles_j, nslots,
+            kGroupedSplitCUs);
     if (b < first_half) {
         if (b >= nslots) return;
         dl_body<DT, true, true, TBig::BM, TBig::BN, TBig::WGM, TBig::WGN, EPI_ROUND,

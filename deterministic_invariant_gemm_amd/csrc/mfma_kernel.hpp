@@ -311,7 +311,7 @@ struct TileInfo {
 // padding tile of MODE_SEGMENTS zero-fills columns col0 + fill_off ..
 // col0 + fill_off + fill_w - 1 (fill_w < 0: the whole tile width).
 template <int MODE, int BM, int BN, int NTH = NT>
-__device__ __forceinline__ TileInfo decode_tile_at(const MfmaArgs &p, int t, int64_t blk,
+__host__ __device__ __forceinline__ TileInfo decode_tile_at(const MfmaArgs &p, int t, int64_t blk,
                                                    int64_t nblk, int64_t fill_off = 0,
                                                    int64_t fill_w = -1) {
     TileInfo ti{};
